@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the weight-only-quantized MoE expert layer on one MI355X.
+
+One step = one full layer forward (top-k gating, stable sort + permute, grouped GEMM 1 with
+in-register dequantization and activation, grouped GEMM 2 with the gate weight, unpermute +
+combine) over one batch of T synthetic tokens whose inputs already sit in HBM.
+
+Default workload: the encoder MoE FFN of the MT model in "Who Says Elephants Can't Run"
+(hidden 1024, FFN 4096, ReLU, 32 experts, top-1 Switch gating, softmax over all experts),
+INT4 per-channel weights, T = 3840 tokens (96 sentences x 40 tokens), Zipf(1.1) skewed routing.
+
+Prints one JSON line.  `roofline` describes the dominant kernel (the grouped GEMM launch with
+the larger average duration), timed with HIP events on the stream the kernels run on, over
+the timed region.  `cpu_baseline` times the CPU oracle on a bounded sample of the workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + weight GB/s (or MFMA util) vs MI355X roofline, W4A16"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("quantized_expert_layer_amd/csrc/gemm.hip",
+                  "quantized_expert_layer_amd/csrc/common.hpp")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="mt_encoder")
+    ap.add_argument("--T", type=int, default=0, help="tokens per step (default: config's first)")
+    ap.add_argument("--wtype", default="int4")
+    ap.add_argument("--active", type=int, default=0, help="restrict routing to experts [0, A)")
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 stream, 2 tile")
+    ap.add_argument("--rotate-gb", type=float, default=1.0,
+                    help="cycle weight copies totalling at least this many GB (cold weights)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one device copy of this size before timing (counter calibration)")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, budget_s):
+    """Time the CPU oracle on a bounded sample of the workload's tokens."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    T = inp.T
+    n = min(T, 256)
+    while True:
+        toks = np.arange(n)
+        t0 = time.perf_counter()
+        oracle.moe_layer_tokens(inp, toks)
+        dt = time.perf_counter() - t0
+        if n >= T or dt * 2 > budget_s:
+            break
+        n = min(T, n * 4 if dt * 4 < budget_s else n * 2)
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {T} tokens of the same layer, fp64 NumPy oracle "
+                      f"(dequantization of the experts those tokens use included), {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this layer build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_expert_layer_amd as q
+    import synth
+
+    cfg = synth.get_config(args.config)
+    T = args.T or cfg.T_list[0]
+    inp = synth.make_inputs(cfg, T, wtype=args.wtype, active=args.active)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layer = q.DeviceLayer.from_inputs(inp, device=dev, gemm_path=args.path)
+    ws = layer.workspace(T)
+    x = torch.from_numpy(inp.x).to(dev)
+    logits = torch.from_numpy(inp.logits).to(dev)
+
+    # weight rotation: enough copies that each step reads weights the caches do not hold
+    wbytes = layer.w1.numel() + layer.w2.numel()
+    n_copies = max(1, int(np.ceil(args.rotate_gb * 1e9 / wbytes)))
+    copies = [(layer.w1, layer.w2)] + [(layer.w1.clone(), layer.w2.clone())
+                                       for _ in range(n_copies - 1)]
+    plans = [layer.plan(ws, x, logits, weights=c) for c in copies]
+    names = plans[0].names
+    i_g1, i_g2 = names.index("gemm1"), names.index("gemm2")
+
+    if args.calib_copy_mb:
+        src = torch.empty(args.calib_copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        plans[i % n_copies].run()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    n_ev = len(names) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(K)]
+    stream = torch.cuda.current_stream()
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e = evs[i]
+        plans[i % n_copies].run(marker=lambda j, e=e: e[j].record(stream))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    stage_us = {}
+    for j, nm in enumerate(names):
+        stage_us[nm] = float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]) * 1e3)
+
+    # algorithmic work of the two grouped GEMM launches
+    off = ws.bufs["off"].cpu().numpy()
+    counts = np.diff(off)
+    active = int((counts > 0).sum())
+    R = T * cfg.k
+    per_expert_w1 = layer.w1.numel() // cfg.E + 2 * inp.scales1[0].size
+    per_expert_w2 = layer.w2.numel() // cfg.E + 2 * inp.scales2[0].size
+    g1 = {"flops": 2.0 * R * cfg.d * layer.n1, "bytes": active * per_expert_w1}
+    g2 = {"flops": 2.0 * R * cfg.inter * cfg.d, "bytes": active * per_expert_w2}
+    dom_name, dom = max((("gemm1", g1), ("gemm2", g2)), key=lambda kv: stage_us[kv[0]])
+    dom_us = stage_us[dom_name]
+    t_hbm = dom["bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = dom["flops"] / (MFMA_F16_PEAK_TFLOPS * 1e12)
+    if t_mfma >= t_hbm:
+        achieved = dom["flops"] / (dom_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_F16_PEAK_TFLOPS}
+    else:
+        achieved = dom["bytes"] / (dom_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    roof["kernel"] = dom_name
+    roof["avg_us"] = dom_us
+    traffic = None
+    src_hash = kernel_source_hash()
+    workload = f"{cfg.name}_{args.wtype}_T{T}" + (f"_A{args.active}" if args.active else "")
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            rec = json.load(open(TRAFFIC_FILE)).get(workload, {})
+            if rec.get("kernel_source_hash") == src_hash and rec.get("kernel") == dom_name:
+                traffic = rec.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    roof["traffic"] = traffic
+
+    layer_s = ms_per_step * 1e-3
+    weight_bytes = g1["bytes"] + g2["bytes"]
+    flops = g1["flops"] + g2["flops"]
+    result = {
+        "metric": METRIC,
+        "value": T / layer_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": workload, "d": cfg.d, "ffn": cfg.inter, "act": cfg.act,
+                   "experts": cfg.E, "top_k": cfg.k, "tokens": T, "weights": args.wtype,
+                   "group": cfg.group or "per-channel", "gate": cfg.gate_mode,
+                   "active_experts": active, "max_rows_per_expert": int(counts.max()),
+                   "weight_copies_rotated": n_copies, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "layer": {"weight_GBps": weight_bytes / layer_s / 1e9,
+                  "weight_frac_hbm": weight_bytes / layer_s / 1e9 / HBM_PEAK_GBS,
+                  "mfma_TFLOPs": flops / layer_s / 1e12,
+                  "mfma_frac": flops / layer_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                  "stage_us": stage_us, "kernel_source_hash": src_hash},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,211 @@
+/*
+ * moe_wq.h -- C ABI of the weight-only-quantized MoE expert layer for AMD MI355X (gfx950).
+ *
+ * The layer, for T tokens of hidden size d, E routed experts and k experts per token:
+ *   1. moe_route_topk        top-k gating over fp32 router logits
+ *   2. moe_permute           stable sort of the T*k routed rows by expert + row gather
+ *   3. moe_grouped_gemm_wq   grouped GEMM over all active experts, int4/int8 codes
+ *                            dequantized in registers, fused activation / gate weight
+ *   4. moe_unpermute_combine restore token order, scale by gate weight, sum the k rows
+ *   and moe_dequant          the standalone per-expert dequantization (Algorithm 1)
+ *
+ * Sources (page, section):
+ *   [W] "Who Says Elephants Can't Run: Bringing Large Scale MoE Models into Cloud Scale
+ *       Production" review, section 3: symmetric per-channel expert quantization with
+ *       scales of shape (E,1,N); Algorithm 1 (dequantization); optimized int-to-float
+ *       conversion (exponent of 1024; 8-bit and 4-bit variants); workflow (sort keyed on
+ *       expert index with the row index attached, permute, grouped GEMM, unpermute with
+ *       expert_scale); section 4: fused GEMM + dequantization.
+ *   [S] "Specter" summary: Background / MoE (top-k routing), Background / GPTQ INT4
+ *       (symmetric, group size 128), Method steps, step 5 (tokens grouped by expert into
+ *       one GEMM per expert, then scattered back).
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers owned by the caller unless marked [host].  fp16 values
+ *     travel as uint16_t bit patterns.  Tensors are dense row-major.
+ *   - Calls never allocate device memory and never synchronize: work is enqueued on
+ *     `stream` (a hipStream_t passed as void*; NULL = the default stream).
+ *   - Arguments are validated on the host before anything is enqueued.  On any error
+ *     nothing is enqueued and outputs are untouched.
+ *   - T == 0 (or R == 0) returns MOE_OK and enqueues nothing.
+ *   - Pointers must be 16-byte aligned.
+ *   - The library keeps no mutable global state; calls are thread-safe.  Results are
+ *     deterministic: two identical calls give identical bits.
+ */
+#ifndef MOE_WQ_H
+#define MOE_WQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define MOE_OK               0
+#define MOE_ERR_INVALID     -1   /* bad argument: null pointer, bad size, misaligned, ... */
+#define MOE_ERR_UNSUPPORTED -2   /* valid but outside what this library implements */
+#define MOE_ERR_WORKSPACE   -3   /* workspace missing or too small */
+#define MOE_ERR_NO_DEVICE   -4   /* no usable gfx950 device */
+#define MOE_ERR_HIP         -5   /* a HIP runtime call failed */
+
+/* ---- enumerations ---- */
+enum moe_gate  { MOE_GATE_SOFTMAX_TOPK = 0,   /* softmax over the k chosen logits        */
+                 MOE_GATE_SOFTMAX_ALL  = 1 }; /* softmax over all E, then keep the top k */
+enum moe_wtype { MOE_W_INT4 = 0, MOE_W_INT8 = 1, MOE_W_FP16 = 2 };
+enum moe_act   { MOE_ACT_NONE = 0, MOE_ACT_RELU = 1, MOE_ACT_SWIGLU = 2 };
+enum moe_path  { MOE_PATH_AUTO = 0,           /* chosen from R, E, K, N                  */
+                 MOE_PATH_STREAM = 1,         /* weight-streaming path, 16-row tiles     */
+                 MOE_PATH_TILE = 2 };         /* LDS-staged MFMA tile path, 128-row tiles */
+
+/* Optional per-call GEMM settings.  Pass NULL for the defaults (all fields 0). */
+typedef struct moe_gemm_opts {
+    int32_t path;      /* enum moe_path                                              */
+    int32_t split_k;   /* 0 = automatic; >= 1 forces the K split of the stream path  */
+    int32_t reserved[6];
+} moe_gemm_opts;
+
+/* Limits. */
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK      8
+#define MOE_MAX_SPLIT_K  16
+
+/*
+ * moe_route_topk -- top-k gating.   [S] Background / MoE: the router scores every expert
+ * and only the k best-scoring experts run for a token.
+ *
+ *   logits    fp32 [T, E]   router logits (finite values; NaN gives an unspecified order)
+ *   topk_ids  int32 [T, k]  out: chosen experts, ordered by logit descending, ties broken
+ *                           by the smaller expert index (+0 and -0 compare equal)
+ *   topk_w    fp32 [T, k]   out: gate weights.  MOE_GATE_SOFTMAX_TOPK: softmax over the k
+ *                           chosen logits (renormalised).  MOE_GATE_SOFTMAX_ALL: softmax
+ *                           over all E logits, then the k chosen entries (no renorm).
+ *   Selection is made on the fp32 logits themselves, so indices are exact.
+ *   Requires 1 <= E <= 256, 1 <= k <= min(E, 8), T >= 0.
+ */
+int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t gate_mode,
+                       int32_t* topk_ids, float* topk_w, void* stream);
+
+/*
+ * moe_permute -- stable counting sort of routed rows by expert, then row gather.
+ *   [W] section 3 workflow: the row index is attached to the gating output, the tuples are
+ *   sorted with the expert index as key, and the activation matrix is permuted.
+ *
+ *   topk_ids        int32 [T, k]  expert of flat slot f = t*k + j (values in [0, E))
+ *   topk_w          fp32  [T, k]  gate weights, or NULL (then w_perm must be NULL)
+ *   x               fp16  [T, d]  token activations
+ *   perm            int32 [T*k]   out: perm[p] = flat slot at sorted position p; slots of one
+ *                                 expert keep ascending f (stable)
+ *   inv_perm        int32 [T*k]   out: inv_perm[f] = sorted position of slot f
+ *   expert_offsets  int32 [E+1]   out: rows of expert e are positions offsets[e]..offsets[e+1]-1
+ *   x_perm          fp16  [T*k, d] out: x_perm[p] = x[perm[p] / k] (bit copy)
+ *   w_perm          fp32  [T*k]   out (optional): w_perm[p] = topk_w.flat[perm[p]]
+ *   ws, ws_bytes    workspace of at least moe_permute_workspace_size(T, k, E) bytes
+ *                   (currently 0: NULL allowed)
+ *   Requires 1 <= E <= 256, 1 <= k <= 8, d % 8 == 0.  Ids outside [0, E) are a caller
+ *   error: their rows are dropped from the output (no fault), offsets[E] then < T*k.
+ */
+int32_t moe_permute(const int32_t* topk_ids, const float* topk_w, const uint16_t* x,
+                    int32_t T, int32_t k, int32_t E, int32_t d,
+                    int32_t* perm, int32_t* inv_perm, int32_t* expert_offsets,
+                    uint16_t* x_perm, float* w_perm,
+                    void* ws, size_t ws_bytes, void* stream);
+size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E);
+
+/*
+ * moe_grouped_gemm_wq -- grouped GEMM over all experts with in-register dequantization.
+ *   [W] section 3 Fig. 1 / workflow (one sub-matrix per expert, all experts in one grouped
+ *   GEMM), section 4 (dequantization fused into the GEMM), section 3 optimized I2F; the
+ *   dequantized weight is W_dq[e,m,n] = code * S[e, g(m), n] (Algorithm 1).
+ *
+ *   a               fp16 [R, K]  rows sorted by expert (x_perm, or the first GEMM's output)
+ *   expert_offsets  int32 [E+1]  rows of expert e are a[offsets[e] .. offsets[e+1]-1];
+ *                                offsets[0] == 0, non-decreasing, offsets[E] <= R.
+ *                                Experts with no rows read no weights.
+ *   w_packed        weights packed by moe_pack_wq for (wtype, E, K, N)
+ *   scales          fp16 [E, G, N], G = 1 (group_size 0: one scale per output channel,
+ *                   shape (E,1,N)) or K/128 (group_size 128: groups along K).  NULL for
+ *                   MOE_W_FP16.
+ *   act             MOE_ACT_NONE / RELU: out = act(a W_dq) [R, N].
+ *                   MOE_ACT_SWIGLU: W columns are [gate | up] (N = 2I); out [R, I] =
+ *                   silu(a W_gate) * (a W_up), silu(z) = z / (1 + exp(-z)).
+ *   row_scale       fp32 [R] or NULL: each output row is multiplied by row_scale[p]
+ *                   (the gate weight, w_perm) after the activation.
+ *   out             fp16 [R, N or N/2]; rows at or beyond offsets[E] are not written.
+ *   opts            [host] NULL or settings (path, split).
+ *   ws, ws_bytes    workspace of at least moe_gemm_workspace_size(...) bytes.
+ *   Accumulation is fp32, the result is rounded once to fp16 (nearest even).
+ *   Requires K % 128 == 0, N % 16 == 0 (N % 32 for SWIGLU), E <= 256, group_size in
+ *   {0, 128} (0 only for FP16 weights).
+ */
+int32_t moe_grouped_gemm_wq(const uint16_t* a, const int32_t* expert_offsets,
+                            int32_t R, int32_t E, int32_t K, int32_t N,
+                            const void* w_packed, const uint16_t* scales,
+                            int32_t wtype, int32_t group_size, int32_t act,
+                            const float* row_scale, uint16_t* out,
+                            const moe_gemm_opts* opts, void* ws, size_t ws_bytes,
+                            void* stream);
+size_t moe_gemm_workspace_size(int32_t R, int32_t E, int32_t K, int32_t N, int32_t wtype,
+                               int32_t act, const moe_gemm_opts* opts);
+
+/*
+ * moe_unpermute_combine -- [W] section 3 workflow: rows are restored to the original order
+ * and scaled by the gate weight (expert_scale); the k rows of a token are summed.
+ *
+ *   out[t] = fp16( sum_{j=0..k-1} w[t,j] * y_perm[inv_perm[t*k+j]]  + addend[t] )
+ *   evaluated in fp32 in ascending j, then the addend, then one rounding to fp16.
+ *   y_perm    fp16 [R, d] (R >= T*k rows; only rows inv_perm points at are read)
+ *   inv_perm  int32 [T*k] (from moe_permute)
+ *   topk_w    fp32 [T, k] or NULL (rows already scaled, e.g. by row_scale in the GEMM)
+ *   addend    fp16 [T, d] or NULL (added with weight 1, e.g. shared experts)
+ *   out       fp16 [T, d]
+ *   Requires 1 <= k <= 8, d % 8 == 0.
+ */
+int32_t moe_unpermute_combine(const uint16_t* y_perm, const int32_t* inv_perm,
+                              const float* topk_w, const uint16_t* addend,
+                              int32_t T, int32_t k, int32_t d, uint16_t* out, void* stream);
+
+/*
+ * moe_dequant -- Algorithm 1 of [W] section 3:
+ *   for e, m, n:  W_dq[e, m, n] = IntToFloat(W[e, m, n]) * S[e, g(m), n]   (fp16)
+ * with IntToFloat done by the exponent-of-1024 construction and one fp16 multiply (round
+ * to nearest even), so the result is the correctly rounded fp16 product.
+ *   w_packed  packed by moe_pack_wq; scales fp16 [E, G, N] as for the GEMM
+ *   w_out     fp16 [E, K, N], logical (unpacked) layout
+ *   Requires wtype INT4 or INT8, K % 128 == 0, N % 16 == 0.
+ */
+int32_t moe_dequant(const void* w_packed, const uint16_t* scales, int32_t wtype,
+                    int32_t group_size, int32_t E, int32_t K, int32_t N, uint16_t* w_out,
+                    void* stream);
+
+/* ---- host-only helpers (no device needed) ---- */
+
+/* Bytes of the packed weights of (wtype, E, K, N): E*K*N/2 (INT4), E*K*N (INT8),
+ * 2*E*K*N (FP16); 0 if the shape is unsupported. */
+size_t moe_packed_bytes(int32_t wtype, int32_t E, int32_t K, int32_t N);
+
+/*
+ * moe_pack_wq -- pack weights into the library's layout (host memory to host memory).
+ *   codes   [host] int8 [E, K, N] codes (INT4: values in [-8, 7]; INT8: [-128, 127]), or
+ *           uint16 fp16 bit patterns [E, K, N] for MOE_W_FP16.
+ *   packed  [host] moe_packed_bytes(wtype, E, K, N) bytes.
+ *   Layout: 16-column blocks, each contiguous along K in 1 KiB units; inside a 32-bit word
+ *   8 int4 codes of 8 consecutive K rows of one column, stored offset by +8 in the nibble
+ *   order [e0,e2,e4,e6,e1,e3,e5,e7] of [W] section 3 (4-bit variant); int8 codes are stored
+ *   offset by +128, 4 consecutive K rows per word in natural byte order (8-bit variant).
+ *   Returns MOE_ERR_INVALID for a code outside its range (packed is then undefined).
+ */
+int32_t moe_pack_wq(const void* codes, int32_t wtype, int32_t E, int32_t K, int32_t N,
+                    void* packed);
+
+/* Text of a status code (static storage). */
+const char* moe_status_str(int32_t status);
+
+/* Library version, e.g. 100 for 0.1.0. */
+int32_t moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_WQ_H */

@@ -1,0 +1,294 @@
+"""Python binding of libmoe_wq.so, the MI355X (gfx950) weight-only-quantized MoE expert layer.
+
+Argument marshalling only: every step of the layer runs in the library's HIP kernels.
+PyTorch supplies device memory (tensors) and the stream; nothing here computes.  The
+functions carry the names of the C entry points declared in include/moe_wq.h.
+
+The library is loaded on first use and a missing or unloadable library raises
+`MoELibraryError`: there is no fallback implementation.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "MOE_OK", "MOE_ERR_INVALID", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
+    "MOE_ERR_NO_DEVICE", "MOE_ERR_HIP",
+    "GATE_TOPK", "GATE_ALL", "W_INT4", "W_INT8", "W_FP16", "ACT_NONE", "ACT_RELU",
+    "ACT_SWIGLU", "PATH_AUTO", "PATH_STREAM", "PATH_TILE",
+    "MoEError", "MoELibraryError", "lib", "lib_path", "status_str", "version",
+    "moe_route_topk", "moe_permute", "moe_grouped_gemm_wq", "moe_unpermute_combine",
+    "moe_dequant", "moe_pack_wq", "moe_packed_bytes", "moe_gemm_workspace_size",
+    "moe_permute_workspace_size", "GemmOpts", "EXPORTED_SYMBOLS",
+]
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE = 0, -1, -2, -3
+MOE_ERR_NO_DEVICE, MOE_ERR_HIP = -4, -5
+GATE_TOPK, GATE_ALL = 0, 1
+W_INT4, W_INT8, W_FP16 = 0, 1, 2
+ACT_NONE, ACT_RELU, ACT_SWIGLU = 0, 1, 2
+PATH_AUTO, PATH_STREAM, PATH_TILE = 0, 1, 2
+
+WTYPES = {"int4": W_INT4, "int8": W_INT8, "fp16": W_FP16}
+ACTS = {"none": ACT_NONE, "relu": ACT_RELU, "swiglu": ACT_SWIGLU}
+GATES = {"topk": GATE_TOPK, "all": GATE_ALL}
+
+lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_wq.so")
+
+# Every symbol include/moe_wq.h declares.
+EXPORTED_SYMBOLS = (
+    "moe_route_topk", "moe_permute", "moe_permute_workspace_size", "moe_grouped_gemm_wq",
+    "moe_gemm_workspace_size", "moe_unpermute_combine", "moe_dequant", "moe_packed_bytes",
+    "moe_pack_wq", "moe_status_str", "moe_version",
+)
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {status_str(status)} ({status})")
+
+
+class MoELibraryError(ImportError):
+    pass
+
+
+class GemmOpts(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+
+def lib():
+    """The loaded library (loaded once; raises MoELibraryError when unavailable)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise MoELibraryError(f"{lib_path} is missing: build it with "
+                              "`python -m quantized_expert_layer_amd.build`")
+    try:
+        L = ctypes.CDLL(lib_path)
+    except OSError as e:
+        raise MoELibraryError(f"cannot load {lib_path}: {e}") from e
+    sig = {
+        "moe_route_topk": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
+        "moe_permute": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+        "moe_permute_workspace_size": (_SZ, [_I, _I, _I]),
+        "moe_grouped_gemm_wq": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _P, _P, _P,
+                                     _P, _SZ, _P]),
+        "moe_gemm_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _P]),
+        "moe_unpermute_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
+        "moe_dequant": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
+        "moe_packed_bytes": (_SZ, [_I, _I, _I, _I]),
+        "moe_pack_wq": (_I, [_P, _I, _I, _I, _I, _P]),
+        "moe_status_str": (ctypes.c_char_p, [_I]),
+        "moe_version": (_I, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(int(status)).decode()
+
+
+def version() -> int:
+    return lib().moe_version()
+
+
+def _check(fn, status):
+    if status != MOE_OK:
+        raise MoEError(fn, status)
+
+
+# ---------------------------------------------------------------- tensor marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t, dtype, name, numel=None):
+    torch = _torch()
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
+
+
+def _opts(path=PATH_AUTO, split_k=0):
+    if path == PATH_AUTO and split_k == 0:
+        return None
+    o = GemmOpts()
+    o.path, o.split_k = int(path), int(split_k)
+    return o
+
+
+# ---------------------------------------------------------------- the five calls
+def moe_route_topk(logits, k, gate_mode, topk_ids=None, topk_w=None, stream=None):
+    torch = _torch()
+    T, E = logits.shape
+    gm = GATES.get(gate_mode, gate_mode)
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _need(logits, torch.float32, "logits")
+    _need(topk_ids, torch.int32, "topk_ids", T * k)
+    _need(topk_w, torch.float32, "topk_w", T * k)
+    _check("moe_route_topk", lib().moe_route_topk(_ptr(logits), T, E, k, gm, _ptr(topk_ids),
+                                                  _ptr(topk_w), _stream(stream)))
+    return topk_ids, topk_w
+
+
+def moe_permute(topk_ids, topk_w, x, E, want_w_perm=True, out=None, stream=None):
+    """Returns (perm, inv_perm, expert_offsets, x_perm, w_perm or None)."""
+    torch = _torch()
+    T, k = topk_ids.shape
+    d = x.shape[1]
+    R = T * k
+    dev = x.device
+    if out is None:
+        out = (torch.empty(R, dtype=torch.int32, device=dev),
+               torch.empty(R, dtype=torch.int32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty((R, d), dtype=torch.float16, device=dev),
+               torch.empty(R, dtype=torch.float32, device=dev)
+               if (want_w_perm and topk_w is not None) else None)
+    perm, inv_perm, offsets, x_perm, w_perm = out
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(topk_w, torch.float32, "topk_w")
+    _need(x, torch.float16, "x")
+    _need(perm, torch.int32, "perm", R)
+    _need(inv_perm, torch.int32, "inv_perm", R)
+    _need(offsets, torch.int32, "expert_offsets", E + 1)
+    _need(x_perm, torch.float16, "x_perm", R * d)
+    _need(w_perm, torch.float32, "w_perm", R)
+    _check("moe_permute", lib().moe_permute(
+        _ptr(topk_ids), _ptr(topk_w), _ptr(x), T, k, E, d, _ptr(perm), _ptr(inv_perm),
+        _ptr(offsets), _ptr(x_perm), _ptr(w_perm), None, 0, _stream(stream)))
+    return perm, inv_perm, offsets, x_perm, w_perm
+
+
+def moe_gemm_workspace_size(R, E, K, N, wtype, act, path=PATH_AUTO, split_k=0):
+    o = _opts(path, split_k)
+    return lib().moe_gemm_workspace_size(R, E, K, N, WTYPES.get(wtype, wtype),
+                                         ACTS.get(act, act), ctypes.byref(o) if o else None)
+
+
+def moe_permute_workspace_size(T, k, E):
+    return lib().moe_permute_workspace_size(T, k, E)
+
+
+def moe_grouped_gemm_wq(a, expert_offsets, E, K, N, w_packed, scales, wtype, group_size, act,
+                        row_scale=None, out=None, path=PATH_AUTO, split_k=0, ws=None,
+                        stream=None):
+    torch = _torch()
+    R = a.shape[0]
+    wt = WTYPES.get(wtype, wtype)
+    ac = ACTS.get(act, act)
+    n_out = N // 2 if ac == ACT_SWIGLU else N
+    if out is None:
+        out = torch.empty((R, n_out), dtype=torch.float16, device=a.device)
+    o = _opts(path, split_k)
+    need_ws = lib().moe_gemm_workspace_size(R, E, K, N, wt, ac, ctypes.byref(o) if o else None)
+    if need_ws and ws is None:
+        ws = torch.empty(need_ws, dtype=torch.uint8, device=a.device)
+    _need(a, torch.float16, "a", R * K)
+    _need(expert_offsets, torch.int32, "expert_offsets", E + 1)
+    _need(w_packed, torch.uint8, "w_packed")
+    _need(scales, torch.float16, "scales")
+    _need(row_scale, torch.float32, "row_scale", R)
+    _need(out, torch.float16, "out", R * n_out)
+    _need(ws, torch.uint8, "ws")
+    _check("moe_grouped_gemm_wq", lib().moe_grouped_gemm_wq(
+        _ptr(a), _ptr(expert_offsets), R, E, K, N, _ptr(w_packed), _ptr(scales), wt,
+        int(group_size), ac, _ptr(row_scale), _ptr(out), ctypes.byref(o) if o else None,
+        _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return out
+
+
+def moe_unpermute_combine(y_perm, inv_perm, topk_w, addend, T, k, out=None, stream=None):
+    torch = _torch()
+    d = y_perm.shape[1]
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.float16, device=y_perm.device)
+    _need(y_perm, torch.float16, "y_perm")
+    _need(inv_perm, torch.int32, "inv_perm", T * k)
+    _need(topk_w, torch.float32, "topk_w", T * k)
+    _need(addend, torch.float16, "addend", T * d)
+    _need(out, torch.float16, "out", T * d)
+    _check("moe_unpermute_combine", lib().moe_unpermute_combine(
+        _ptr(y_perm), _ptr(inv_perm), _ptr(topk_w), _ptr(addend), T, k, d, _ptr(out),
+        _stream(stream)))
+    return out
+
+
+def moe_dequant(w_packed, scales, wtype, group_size, E, K, N, out=None, stream=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty((E, K, N), dtype=torch.float16, device=w_packed.device)
+    _need(w_packed, torch.uint8, "w_packed")
+    _need(scales, torch.float16, "scales")
+    _need(out, torch.float16, "w_out", E * K * N)
+    _check("moe_dequant", lib().moe_dequant(_ptr(w_packed), _ptr(scales), WTYPES.get(wtype, wtype),
+                                            int(group_size), E, K, N, _ptr(out), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------- host helpers
+def moe_packed_bytes(wtype, E, K, N):
+    return lib().moe_packed_bytes(WTYPES.get(wtype, wtype), E, K, N)
+
+
+def moe_pack_wq(codes: np.ndarray, wtype) -> np.ndarray:
+    """Pack host codes [E, K, N] (int8 codes, or float16 weights for "fp16") -> uint8 array."""
+    wt = WTYPES.get(wtype, wtype)
+    codes = np.ascontiguousarray(codes)
+    if wt == W_FP16:
+        if codes.dtype != np.float16:
+            raise TypeError("fp16 weights must be float16")
+    elif codes.dtype != np.int8:
+        raise TypeError("integer codes must be int8")
+    E, K, N = codes.shape
+    nbytes = lib().moe_packed_bytes(wt, E, K, N)
+    if nbytes == 0:
+        raise MoEError("moe_pack_wq", MOE_ERR_UNSUPPORTED)
+    out = np.empty(nbytes, dtype=np.uint8)
+    _check("moe_pack_wq", lib().moe_pack_wq(codes.ctypes.data_as(_P), wt, E, K, N,
+                                            out.ctypes.data_as(_P)))
+    return out
+
+
+from .layer import DeviceLayer, Workspace  # noqa: E402,F401

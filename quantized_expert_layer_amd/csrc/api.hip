@@ -1,0 +1,216 @@
+// C ABI of the MoE expert layer: argument validation, device check, dispatch.
+// Validation runs before any HIP call, so argument errors are reported (and nothing is
+// enqueued) even on a machine without a GPU.
+#include <atomic>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int32_t kVersion = 100;
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// gfx950 check, cached per device id (immutable once written).
+std::atomic<int> g_dev_state[64];   // 0 unknown, 1 usable, 2 unusable
+
+int32_t check_device() {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return MOE_ERR_NO_DEVICE;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_NO_DEVICE;
+    if (dev < 0 || dev >= 64) return MOE_ERR_NO_DEVICE;
+    int st = g_dev_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_NO_DEVICE;
+        const char* a = prop.gcnArchName;
+        st = (a[0] == 'g' && a[1] == 'f' && a[2] == 'x' && a[3] == '9' && a[4] == '5' &&
+              a[5] == '0') ? 1 : 2;
+        g_dev_state[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? MOE_OK : MOE_ERR_NO_DEVICE;
+}
+
+inline int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+struct GemmPlan {
+    int path;
+    int split;
+    size_t ws;
+};
+
+GemmPlan plan_gemm(int32_t R, int32_t E, int32_t K, int32_t N, int32_t wtype, int32_t act,
+                   const moe_gemm_opts* opts) {
+    GemmPlan pl;
+    const int forced_path = opts ? opts->path : MOE_PATH_AUTO;
+    const int forced_split = opts ? opts->split_k : 0;
+    pl.path = moe::gemm_choose_path(R, E, K, N, wtype, act, forced_path);
+    pl.split = 1;
+    if (pl.path == MOE_PATH_STREAM) pl.split = moe::gemm_choose_split(R, E, K, N, wtype, act, forced_split);
+    pl.ws = pl.split > 1 ? (size_t)pl.split * (size_t)R * (size_t)N * sizeof(float) : 0;
+    return pl;
+}
+
+int32_t validate_gemm(const uint16_t* a, const int32_t* offsets, int32_t R, int32_t E, int32_t K,
+                      int32_t N, const void* w, const uint16_t* scales, int32_t wtype,
+                      int32_t group, int32_t act, uint16_t* out, const moe_gemm_opts* opts) {
+    if (R < 0 || E < 1 || E > MOE_MAX_EXPERTS || K <= 0 || N <= 0) return MOE_ERR_INVALID;
+    if (wtype < MOE_W_INT4 || wtype > MOE_W_FP16) return MOE_ERR_INVALID;
+    if (act < MOE_ACT_NONE || act > MOE_ACT_SWIGLU) return MOE_ERR_INVALID;
+    if (group != 0 && group != 128) return MOE_ERR_UNSUPPORTED;
+    if (wtype == MOE_W_FP16 && group != 0) return MOE_ERR_UNSUPPORTED;
+    if (K % 128 != 0 || N % 16 != 0) return MOE_ERR_UNSUPPORTED;
+    if (act == MOE_ACT_SWIGLU && N % 32 != 0) return MOE_ERR_UNSUPPORTED;
+    if (opts) {
+        if (opts->path < MOE_PATH_AUTO || opts->path > MOE_PATH_TILE) return MOE_ERR_INVALID;
+        if (opts->split_k < 0 || opts->split_k > MOE_MAX_SPLIT_K) return MOE_ERR_INVALID;
+    }
+    if ((int64_t)R * K >= (int64_t)1 << 40) return MOE_ERR_UNSUPPORTED;
+    if (R == 0) return MOE_OK;
+    if (!a || !offsets || !w || !out) return MOE_ERR_INVALID;
+    if (wtype != MOE_W_FP16 && !scales) return MOE_ERR_INVALID;
+    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(out, 4) || !aligned(offsets, 4))
+        return MOE_ERR_INVALID;
+    if (scales && !aligned(scales, 2)) return MOE_ERR_INVALID;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_version(void) { return kVersion; }
+
+const char* moe_status_str(int32_t s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID: return "MOE_ERR_INVALID: invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape or option not supported";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+        case MOE_ERR_NO_DEVICE: return "MOE_ERR_NO_DEVICE: no usable gfx950 device";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t gate_mode,
+                       int32_t* topk_ids, float* topk_w, void* stream) {
+    if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E)
+        return MOE_ERR_INVALID;
+    if (gate_mode != MOE_GATE_SOFTMAX_TOPK && gate_mode != MOE_GATE_SOFTMAX_ALL)
+        return MOE_ERR_INVALID;
+    if ((int64_t)T * E >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID;
+    if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID;
+    if (int32_t st = check_device()) return st;
+    return hip_status(moe::launch_route_topk(logits, T, E, k, gate_mode == MOE_GATE_SOFTMAX_ALL,
+                                             topk_ids, topk_w, (hipStream_t)stream));
+}
+
+size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E) {
+    (void)T; (void)k; (void)E;
+    return 0;
+}
+
+int32_t moe_permute(const int32_t* topk_ids, const float* topk_w, const uint16_t* x, int32_t T,
+                    int32_t k, int32_t E, int32_t d, int32_t* perm, int32_t* inv_perm,
+                    int32_t* expert_offsets, uint16_t* x_perm, float* w_perm, void* ws,
+                    size_t ws_bytes, void* stream) {
+    (void)ws; (void)ws_bytes;
+    if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS || d <= 0)
+        return MOE_ERR_INVALID;
+    if (d % 8 != 0) return MOE_ERR_UNSUPPORTED;
+    const int64_t R = (int64_t)T * k;
+    if (R >= (int64_t)1 << 31 || R * (d / 8) >= (int64_t)1 << 32) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!topk_ids || !x || !perm || !inv_perm || !expert_offsets || !x_perm) return MOE_ERR_INVALID;
+    if (w_perm && !topk_w) return MOE_ERR_INVALID;
+    if (!aligned(x, 16) || !aligned(x_perm, 16) || !aligned(topk_ids, 4) || !aligned(perm, 4) ||
+        !aligned(inv_perm, 4) || !aligned(expert_offsets, 4))
+        return MOE_ERR_INVALID;
+    if ((topk_w && !aligned(topk_w, 4)) || (w_perm && !aligned(w_perm, 4))) return MOE_ERR_INVALID;
+    if (int32_t st = check_device()) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = moe::launch_sort(topk_ids, topk_w, (int)R, E, perm, inv_perm, expert_offsets,
+                                    w_perm, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(moe::launch_gather(x, perm, (int)R, k, d, x_perm, s));
+}
+
+size_t moe_gemm_workspace_size(int32_t R, int32_t E, int32_t K, int32_t N, int32_t wtype,
+                               int32_t act, const moe_gemm_opts* opts) {
+    if (R <= 0 || E < 1 || K <= 0 || N <= 0) return 0;
+    return plan_gemm(R, E, K, N, wtype, act, opts).ws;
+}
+
+int32_t moe_grouped_gemm_wq(const uint16_t* a, const int32_t* expert_offsets, int32_t R,
+                            int32_t E, int32_t K, int32_t N, const void* w_packed,
+                            const uint16_t* scales, int32_t wtype, int32_t group_size,
+                            int32_t act, const float* row_scale, uint16_t* out,
+                            const moe_gemm_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+    if (int32_t st = validate_gemm(a, expert_offsets, R, E, K, N, w_packed, scales, wtype,
+                                   group_size, act, out, opts))
+        return st;
+    if (R == 0) return MOE_OK;
+    if (row_scale && !aligned(row_scale, 4)) return MOE_ERR_INVALID;
+    const GemmPlan pl = plan_gemm(R, E, K, N, wtype, act, opts);
+    if (pl.ws > 0 && (!ws || ws_bytes < pl.ws || !aligned(ws, 16))) return MOE_ERR_WORKSPACE;
+    if (int32_t st = check_device()) return st;
+
+    moe::GemmParams p;
+    p.a = a;
+    p.offsets = expert_offsets;
+    p.w = w_packed;
+    p.scales = scales;
+    p.row_scale = row_scale;
+    p.out = out;
+    p.partial = (float*)ws;
+    p.R = R;
+    p.E = E;
+    p.K = K;
+    p.N = N;
+    p.wtype = wtype;
+    p.group = group_size;
+    p.act = act;
+    p.split = pl.split;
+    hipStream_t s = (hipStream_t)stream;
+    return hip_status(pl.path == MOE_PATH_TILE ? moe::launch_gemm_tile(p, s)
+                                               : moe::launch_gemm_stream(p, s));
+}
+
+int32_t moe_unpermute_combine(const uint16_t* y_perm, const int32_t* inv_perm, const float* topk_w,
+                              const uint16_t* addend, int32_t T, int32_t k, int32_t d,
+                              uint16_t* out, void* stream) {
+    if (T < 0 || k < 1 || k > MOE_MAX_TOPK || d <= 0) return MOE_ERR_INVALID;
+    if (d % 8 != 0) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)T * k >= (int64_t)1 << 31 || (int64_t)T * (d / 8) >= (int64_t)1 << 32)
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!y_perm || !inv_perm || !out) return MOE_ERR_INVALID;
+    if (!aligned(y_perm, 16) || !aligned(out, 16) || !aligned(inv_perm, 4)) return MOE_ERR_INVALID;
+    if ((addend && !aligned(addend, 16)) || (topk_w && !aligned(topk_w, 4))) return MOE_ERR_INVALID;
+    if (int32_t st = check_device()) return st;
+    return hip_status(moe::launch_combine(y_perm, inv_perm, topk_w, addend, T, k, d, out,
+                                          (hipStream_t)stream));
+}
+
+int32_t moe_dequant(const void* w_packed, const uint16_t* scales, int32_t wtype, int32_t group_size,
+                    int32_t E, int32_t K, int32_t N, uint16_t* w_out, void* stream) {
+    if (E < 1 || E > MOE_MAX_EXPERTS || K <= 0 || N <= 0) return MOE_ERR_INVALID;
+    if (wtype != MOE_W_INT4 && wtype != MOE_W_INT8) return MOE_ERR_INVALID;
+    if (group_size != 0 && group_size != 128) return MOE_ERR_UNSUPPORTED;
+    if (K % 128 != 0 || N % 16 != 0) return MOE_ERR_UNSUPPORTED;
+    if (!w_packed || !scales || !w_out) return MOE_ERR_INVALID;
+    if (!aligned(w_packed, 16) || !aligned(scales, 2) || !aligned(w_out, 2)) return MOE_ERR_INVALID;
+    if (int32_t st = check_device()) return st;
+    return hip_status(moe::launch_dequant(w_packed, scales, wtype, group_size, E, K, N, w_out,
+                                          (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+// Shared device/host definitions of the MoE expert-layer kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_wq.h"
+
+namespace moe {
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------------------------
+// Packed weight layout (shared by every kernel that reads weights).
+//
+// A weight matrix of expert e is K x N (K = reduction).  It is cut into 16-column blocks
+// (cb = n / 16).  Each column block is stored contiguously along K as a run of 1 KiB
+// "super-blocks"; a super-block holds the operand of one MFMA 16x16x32 B fragment per
+// 32-row K-step for all 64 lanes:  lane l owns column cb*16 + (l & 15) and, within each
+// K-step, rows 8*(l >> 4) .. 8*(l >> 4) + 7.  Lane l's 16 bytes of a super-block are at
+// byte offset 16*l, so one 16-byte load per lane fetches a whole super-block.
+//   INT4: 4 K-steps (128 rows) per super-block; word j of lane l = K-step j; the 8 codes
+//         (offset +8) sit in nibble order [e0,e2,e4,e6,e1,e3,e5,e7].
+//   INT8: 2 K-steps (64 rows); words 2j, 2j+1 = K-step j, rows 0..3 and 4..7; bytes in
+//         natural order, offset +128 (offset-binary).
+//   FP16: 1 K-step (32 rows); the 8 halves of the lane in row order.
+// Address of super-block (e, cb, kb): ((e * (N/16) + cb) * (K / KSB) + kb) * 1024 bytes.
+// ------------------------------------------------------------------------------------
+template <int WT> struct WTraits;
+template <> struct WTraits<MOE_W_INT4> { static constexpr int KSB = 128; };
+template <> struct WTraits<MOE_W_INT8> { static constexpr int KSB = 64; };
+template <> struct WTraits<MOE_W_FP16> { static constexpr int KSB = 32; };
+
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+
+// Exponent-of-1024 int-to-float construction ("Who Says Elephants Can't Run", section 3,
+// optimized I2F).  0x6400 is fp16 1024 with an all-zero mantissa; OR-ing an integer Y < 1024
+// into the mantissa gives the fp16 value 1024 + Y, and one packed fp16 subtraction removes
+// the offset.  INT4 nibbles four bits up the half-word land as 16*u: (1024 + 16u)/16 - 72 =
+// u - 8 with a single packed fma, exact in fp16.
+__device__ __forceinline__ void i2f_int4(uint32_t w, f16x2 out[4]) {
+    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, magic = 0x64006400u;
+    const uint32_t w8 = w >> 8;
+    const f16x2 sub_lo = {(f16)1032.0f, (f16)1032.0f};
+    const f16x2 mul_hi = {(f16)0.0625f, (f16)0.0625f};
+    const f16x2 sub_hi = {(f16)-72.0f, (f16)-72.0f};
+    out[0] = as_f16x2((w & lo) | magic) - sub_lo;            // [e0, e1]
+    out[1] = as_f16x2((w & hi) | magic) * mul_hi + sub_hi;   // [e2, e3]
+    out[2] = as_f16x2((w8 & lo) | magic) - sub_lo;           // [e4, e5]
+    out[3] = as_f16x2((w8 & hi) | magic) * mul_hi + sub_hi;  // [e6, e7]
+}
+
+// 8-bit variant: byte u = q + 128 goes into the mantissa of 1024, then 1152 = 1024 + 128
+// is subtracted.  v_perm_b32 builds [0x64|b0, 0x64|b1] in one instruction.
+__device__ __forceinline__ void i2f_int8(uint32_t w, f16x2 out[2]) {
+    const f16x2 sub = {(f16)1152.0f, (f16)1152.0f};
+    out[0] = as_f16x2(__builtin_amdgcn_perm(0x64646464u, w, 0x05010400u)) - sub;  // [e0,e1]
+    out[1] = as_f16x2(__builtin_amdgcn_perm(0x64646464u, w, 0x05030402u)) - sub;  // [e2,e3]
+}
+
+__device__ __forceinline__ f16x8 pack8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
+    f16x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+    return __builtin_bit_cast(uint16_t, (f16)v);   // round to nearest even
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+    return (float)__builtin_bit_cast(f16, b);
+}
+
+// Non-temporal 16-byte load of packed weights (streamed once; keep caches for activations).
+__device__ __forceinline__ u32x4 load_weights16(const u32x4* p) {
+    return __builtin_nontemporal_load(p);
+}
+
+// ------------------------------------------------------------------------------------
+// Tile lookup: m-tile `mt` of the grouped GEMM -> (expert, first row, rows).
+// Experts are visited in order; expert e contributes ceil(c_e / BM) m-tiles where c_e is
+// its row count taken from the offsets, clamped into [0, R] so that any offsets array
+// yields in-bounds rows.  Executed by a whole wave; returns false when mt is past the end.
+// ------------------------------------------------------------------------------------
+template <int BM>
+__device__ __forceinline__ bool find_m_tile(const int32_t* __restrict__ offsets, int E, int R,
+                                            int mt, int& e_out, int& row0, int& rows) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int base = 0;
+    for (int e0 = 0; e0 < E; e0 += kWave) {
+        const int e = e0 + lane;
+        int lo = 0, hi = 0;
+        if (e < E) {
+            lo = min(max(offsets[e], 0), R);
+            hi = min(max(offsets[e + 1], 0), R);
+        }
+        const int cnt = max(hi - lo, 0);
+        const int tiles = (cnt + BM - 1) / BM;
+        // inclusive prefix sum of tiles across the wave
+        int incl = tiles;
+#pragma unroll
+        for (int s = 1; s < kWave; s <<= 1) {
+            const int v = __shfl_up(incl, s, kWave);
+            if (lane >= s) incl += v;
+        }
+        const int excl = incl - tiles;
+        const unsigned long long hit = __ballot(tiles > 0 && mt >= base + excl && mt < base + incl);
+        if (hit) {
+            const int src = __builtin_ctzll(hit);
+            const int my_row0 = lo + (mt - base - excl) * BM;
+            const int my_rows = min(BM, hi - my_row0);
+            e_out = __shfl(e, src, kWave);
+            row0 = __shfl(my_row0, src, kWave);
+            rows = __shfl(my_rows, src, kWave);
+            return true;
+        }
+        base += __shfl(incl, kWave - 1, kWave);
+    }
+    return false;
+}
+
+}  // namespace moe

@@ -1,0 +1,489 @@
+// Grouped GEMM over all experts with weights dequantized in registers.
+//
+// "Who Says Elephants Can't Run", section 3 (Fig. 1, workflow): every expert's GEMM runs in
+// one grouped launch, one sub-matrix per expert; section 4: the dequantization is fused
+// into the GEMM; section 3 optimized I2F: codes become fp16 through the exponent-of-1024
+// construction.  The dequantized weight is Algorithm 1's W_dq = code * S.
+//
+// Two paths share the packed layout and the MFMA 16x16x32 fp16 fragment shapes:
+//   stream : 16-row m-tiles, one wave per 16 output columns, A fragments straight from
+//            global memory, weights streamed once with a deep register prefetch.  Meant for
+//            the few rows per expert of decode / verify (the Specter page's fine-grained
+//            expert kernels); optional split along K with a fixed-order reduction.
+//   tile   : 128-row m-tiles, 4 waves x 64 weight columns, A staged through LDS (double
+//            buffered), weights double buffered in registers.  Meant for large M.
+// Experts with no rows launch no work that reads weights.
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+// ------------------------------------------------------------------------------------
+// Weight fragment expansion: K-step j of a lane's 16-byte super-block slice -> B operand.
+// Group scales (group 128) are folded in by one fp16 multiply, giving exactly Algorithm 1's
+// fp16 weight; per-channel scales are applied to the fp32 result instead.
+// ------------------------------------------------------------------------------------
+template <int WT, bool SCALE>
+__device__ __forceinline__ f16x8 weight_frag(const u32x4& raw, int j, f16x2 s2) {
+    f16x2 q[4];
+    if constexpr (WT == MOE_W_INT4) {
+        i2f_int4(raw[j], q);
+    } else if constexpr (WT == MOE_W_INT8) {
+        i2f_int8(raw[2 * j], q);
+        i2f_int8(raw[2 * j + 1], q + 2);
+    } else {
+        return __builtin_bit_cast(f16x8, raw);
+    }
+    if constexpr (SCALE) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) q[h] = q[h] * s2;
+    }
+    return pack8(q[0], q[1], q[2], q[3]);
+}
+
+// ------------------------------------------------------------------------------------
+// Stream path.
+//   grid  = m-tiles(upper bound) x ceil(NBo / 4) x S blocks of 4 waves.
+//   wave  = one 16-column output block; for SwiGLU it streams the gate block and the up
+//           block (columns I + ...) of the same 16 outputs.
+// ------------------------------------------------------------------------------------
+template <int WT, int ACT, bool GROUPED, bool SPLIT, int PF>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p, int nbo, int ncbg) {
+    constexpr int KSB = WTraits<WT>::KSB;
+    constexpr int KSTEPS = KSB / 32;
+    constexpr int NCB = (ACT == MOE_ACT_SWIGLU) ? 2 : 1;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int S = p.split;
+
+    int b = blockIdx.x;
+    const int s = b % S;
+    b /= S;
+    const int cbg = b % ncbg;
+    const int mt = b / ncbg;
+    const int cbo = cbg * 4 + wave;
+    if (cbo >= nbo) return;
+    int e, row0, rows;
+    if (!find_m_tile<16>(p.offsets, p.E, p.R, mt, e, row0, rows)) return;
+
+    const int K = p.K, N = p.N;
+    const int nSB = K / KSB;
+    const int chunk = (nSB + S - 1) / S;
+    const int kb0 = s * chunk;
+    const int kb1 = min(nSB, kb0 + chunk);
+
+    const int ncbw = N / 16;
+    int ncol[NCB];
+    const u32x4* wp[NCB];
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+        const int cbw = cbo + c * nbo;          // SwiGLU: up block sits I/16 blocks later
+        ncol[c] = cbw * 16 + (lane & 15);
+        wp[c] = (const u32x4*)p.w + ((size_t)(e * ncbw + cbw) * nSB) * kWave + lane;
+    }
+    const int G = GROUPED ? K / 128 : 1;         // groups of 128 rows along K
+    const uint16_t* sp = p.scales + (size_t)e * G * N;
+
+    // A fragment source: row (lane & 15) of the tile, 8 halves at k = 8 * (lane >> 4).
+    const int arow = lane & 15;
+    const bool arow_ok = arow < rows;
+    const f16x8* ap = (const f16x8*)(p.a + (size_t)(row0 + (arow_ok ? arow : 0)) * K) + (lane >> 4);
+
+    f32x4 acc[NCB];
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 braw[PF][NCB];
+    f16x8 araw[PF][KSTEPS];
+    uint16_t sraw[PF][NCB] = {};
+
+    auto issue = [&](int slot, int kb) {
+        const int kl = min(kb, kb1 - 1);        // clamped: tail loads repeat the last block
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) {
+            braw[slot][c] = load_weights16(wp[c] + (size_t)kl * kWave);
+            if constexpr (GROUPED) sraw[slot][c] = sp[(size_t)((kl * KSB) >> 7) * N + ncol[c]];
+        }
+#pragma unroll
+        for (int j = 0; j < KSTEPS; ++j) araw[slot][j] = ap[(kl * KSB + j * 32) / 8];
+    };
+
+    if (kb0 < kb1) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) issue(u, kb0 + u);
+        for (int kb = kb0; kb < kb1; kb += PF) {
+#pragma unroll
+            for (int u = 0; u < PF; ++u) {
+                const int kc = kb + u;
+                u32x4 bcur[NCB];
+                uint16_t scur[NCB];
+#pragma unroll
+                for (int c = 0; c < NCB; ++c) { bcur[c] = braw[u][c]; scur[c] = sraw[u][c]; }
+                f16x8 acur[KSTEPS];
+#pragma unroll
+                for (int j = 0; j < KSTEPS; ++j) acur[j] = araw[u][j];
+                issue(u, kc + PF);
+                if (kc < kb1) {
+#pragma unroll
+                    for (int c = 0; c < NCB; ++c) {
+                        const f16 sv = __builtin_bit_cast(f16, scur[c]);
+                        const f16x2 s2 = {sv, sv};
+#pragma unroll
+                        for (int j = 0; j < KSTEPS; ++j)
+                            acc[c] = mfma16x16x32(acur[j], weight_frag<WT, GROUPED>(bcur[c], j, s2), acc[c]);
+                    }
+                }
+            }
+        }
+    }
+
+    // per-channel scales on the fp32 sums
+    if constexpr (!GROUPED && WT != MOE_W_FP16) {
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) {
+            const float sc = f16_bits_to_f32(sp[ncol[c]]);
+            acc[c] *= sc;
+        }
+    }
+
+    const int rbase = 4 * (lane >> 4);
+    if constexpr (SPLIT) {
+        // fp32 partial sums of this K slice: partial[s][row][n]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rbase + i;
+            if (r < rows) {
+                float* dst = p.partial + ((size_t)s * p.R + row0 + r) * N;
+#pragma unroll
+                for (int c = 0; c < NCB; ++c) dst[ncol[c]] = acc[c][i];
+            }
+        }
+    } else {
+        const int n_out = (ACT == MOE_ACT_SWIGLU) ? N / 2 : N;
+        const int col = cbo * 16 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rbase + i;
+            if (r < rows) {
+                float v;
+                if constexpr (ACT == MOE_ACT_SWIGLU) v = silu(acc[0][i]) * acc[1][i];
+                else if constexpr (ACT == MOE_ACT_RELU) v = fmaxf(acc[0][i], 0.0f);
+                else v = acc[0][i];
+                if (p.row_scale) v *= p.row_scale[row0 + r];
+                p.out[(size_t)(row0 + r) * n_out + col] = f32_to_f16_bits(v);
+            }
+        }
+    }
+}
+
+// Fixed-order reduction of the split-K partial sums, then activation and row scale.
+template <int ACT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
+    const int N = p.N;
+    const int n_out = (ACT == MOE_ACT_SWIGLU) ? N / 2 : N;
+    const int rows = min(max(p.offsets[p.E], 0), p.R);
+    const size_t total = (size_t)rows * n_out;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (size_t)gridDim.x * blockDim.x) {
+        const int r = (int)(i / n_out);
+        const int c = (int)(i - (size_t)r * n_out);
+        float g = 0.f, u = 0.f;
+        for (int s = 0; s < p.split; ++s) {
+            const float* src = p.partial + ((size_t)s * p.R + r) * N;
+            g += src[c];
+            if constexpr (ACT == MOE_ACT_SWIGLU) u += src[n_out + c];
+        }
+        float v;
+        if constexpr (ACT == MOE_ACT_SWIGLU) v = silu(g) * u;
+        else if constexpr (ACT == MOE_ACT_RELU) v = fmaxf(g, 0.0f);
+        else v = g;
+        if (p.row_scale) v *= p.row_scale[r];
+        p.out[i] = f32_to_f16_bits(v);
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Tile path.
+//   block tile  = 128 rows x 256 weight columns (4 waves x 4 column blocks of 16)
+//                 SwiGLU: 4 waves x (2 gate + 2 up blocks) = 128 output columns
+//   K stage     = 128 rows of K; A stage = 128 x 128 fp16 in LDS (row pitch 136 halves so
+//                 that the 16 lanes of a ds_read_b128 group hit distinct banks)
+// ------------------------------------------------------------------------------------
+constexpr int kTileBM = 128;
+constexpr int kTileMS = 8;           // 16-row subtiles per wave
+constexpr int kTileNS = 4;           // 16-column weight blocks per wave
+// K per stage: one 128-group for the integer codes, 64 rows for fp16 weights (whose
+// register double buffer is 4x larger per row).
+template <int WT> constexpr int tile_kc() { return WT == MOE_W_FP16 ? 64 : 128; }
+constexpr int kTileLdsMax = kTileBM * (128 + 8);   // halves per LDS buffer
+
+template <int WT, int ACT, bool GROUPED>
+__global__ __launch_bounds__(256, 1) void gemm_tile_kernel(GemmParams p, int ncbg, int mt_ub,
+                                                           int grid_real) {
+    constexpr int KSB = WTraits<WT>::KSB;
+    constexpr int kTileKC = tile_kc<WT>();
+    constexpr int kTileLdsPitch = kTileKC + 8;       // halves; 16 lanes of a b128 read hit
+                                                     // distinct banks
+    constexpr int SBPS = kTileKC / KSB;              // super-blocks per stage per column block
+    constexpr int CPR = kTileKC / 8;                 // 16-byte chunks per A row per stage
+    constexpr int ACH = kTileBM * CPR / 256;         // A chunks per thread per stage
+    constexpr bool SWI = (ACT == MOE_ACT_SWIGLU);
+    __shared__ __attribute__((aligned(16))) f16 lds[2][kTileLdsMax];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+
+    // XCD-aware order: hardware block b runs on XCD b % 8; give each XCD a contiguous
+    // range of logical tiles so that the m-tiles sharing a weight block share an L2.
+    const int G8 = gridDim.x / 8;
+    const int L = (blockIdx.x % 8) * G8 + blockIdx.x / 8;
+    if (L >= grid_real) return;
+    const int mt = L % mt_ub;
+    const int cbg = L / mt_ub;
+    int e, row0, rows;
+    if (!find_m_tile<kTileBM>(p.offsets, p.E, p.R, mt, e, row0, rows)) return;
+
+    const int K = p.K, N = p.N;
+    const int nSB = K / KSB;
+    const int ncbw = N / 16;
+    const int nbo = SWI ? ncbw / 2 : ncbw;           // output column blocks
+
+    // this wave's weight column blocks
+    int cbw[kTileNS];
+    bool cb_ok[kTileNS];
+#pragma unroll
+    for (int c = 0; c < kTileNS; ++c) {
+        int ob;
+        if constexpr (SWI) ob = cbg * 8 + wave * 2 + (c & 1);
+        else ob = cbg * 16 + wave * 4 + c;
+        cb_ok[c] = ob < nbo;
+        const int obc = cb_ok[c] ? ob : 0;
+        cbw[c] = SWI ? obc + (c >> 1) * nbo : obc;
+    }
+    const u32x4* wp[kTileNS];
+    int ncol[kTileNS];
+#pragma unroll
+    for (int c = 0; c < kTileNS; ++c) {
+        wp[c] = (const u32x4*)p.w + ((size_t)(e * ncbw + cbw[c]) * nSB) * kWave + lane;
+        ncol[c] = cbw[c] * 16 + (lane & 15);
+    }
+    const int G = GROUPED ? K / 128 : 1;         // groups of 128 rows along K
+    const uint16_t* sp = p.scales + (size_t)e * G * N;
+
+    // A staging: 128 rows x KC halves in 16-byte chunks, ACH per thread
+    const int nstage = K / kTileKC;
+    u32x4 areg[ACH];
+    auto load_a = [&](int st) {
+#pragma unroll
+        for (int i = 0; i < ACH; ++i) {
+            const int cidx = threadIdx.x + 256 * i;
+            const int r = cidx / CPR, c8 = cidx % CPR;
+            const int rr = row0 + min(r, rows - 1);
+            areg[i] = *(const u32x4*)(p.a + (size_t)rr * K + st * kTileKC + c8 * 8);
+        }
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < ACH; ++i) {
+            const int cidx = threadIdx.x + 256 * i;
+            const int r = cidx / CPR, c8 = cidx % CPR;
+            *(u32x4*)(&lds[buf][r * kTileLdsPitch + c8 * 8]) = areg[i];
+        }
+    };
+
+    u32x4 breg[2][kTileNS][SBPS];
+    uint16_t sreg[2][kTileNS] = {};
+    auto load_b = [&](int slot, int st) {
+#pragma unroll
+        for (int c = 0; c < kTileNS; ++c) {
+#pragma unroll
+            for (int q = 0; q < SBPS; ++q)
+                breg[slot][c][q] = load_weights16(wp[c] + (size_t)(st * SBPS + q) * kWave);
+            if constexpr (GROUPED) sreg[slot][c] = sp[(size_t)((st * kTileKC) >> 7) * N + ncol[c]];
+        }
+    };
+
+    f32x4 acc[kTileMS][kTileNS];
+#pragma unroll
+    for (int m = 0; m < kTileMS; ++m)
+#pragma unroll
+        for (int c = 0; c < kTileNS; ++c) acc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    load_a(0);
+    load_b(0, 0);
+    store_a(0);
+    __syncthreads();
+
+    // One stage: compute from LDS buffer / register slot CUR while stage st+1 is fetched.
+    // CUR is a compile-time constant so that the register double buffer stays in VGPRs.
+    auto stage = [&](auto cur_tag, int st) {
+        constexpr int cur = decltype(cur_tag)::value;
+        const bool more = st + 1 < nstage;
+        if (more) {
+            load_a(st + 1);
+            load_b(cur ^ 1, st + 1);
+        }
+        const f16* abuf = lds[cur];
+#pragma unroll
+        for (int ks = 0; ks < kTileKC / 32; ++ks) {
+            f16x8 bq[kTileNS];
+#pragma unroll
+            for (int c = 0; c < kTileNS; ++c) {
+                const f16 sv = __builtin_bit_cast(f16, sreg[cur][c]);
+                const f16x2 s2 = {sv, sv};
+                constexpr int KSPS = KSB / 32;       // K-steps per super-block
+                bq[c] = weight_frag<WT, GROUPED>(breg[cur][c][ks / KSPS], ks % KSPS, s2);
+            }
+#pragma unroll
+            for (int m = 0; m < kTileMS; ++m) {
+                const f16x8 af = *(const f16x8*)(abuf + (m * 16 + (lane & 15)) * kTileLdsPitch +
+                                                 ks * 32 + 8 * (lane >> 4));
+#pragma unroll
+                for (int c = 0; c < kTileNS; ++c) acc[m][c] = mfma16x16x32(af, bq[c], acc[m][c]);
+            }
+        }
+        if (more) {
+            store_a(cur ^ 1);
+            __syncthreads();
+        }
+    };
+    for (int st = 0; st < nstage; st += 2) {
+        stage(std::integral_constant<int, 0>{}, st);
+        if (st + 1 < nstage) stage(std::integral_constant<int, 1>{}, st + 1);
+    }
+
+    // epilogue
+    if constexpr (!GROUPED && WT != MOE_W_FP16) {
+#pragma unroll
+        for (int c = 0; c < kTileNS; ++c) {
+            const float sc = f16_bits_to_f32(sp[ncol[c]]);
+#pragma unroll
+            for (int m = 0; m < kTileMS; ++m) acc[m][c] *= sc;
+        }
+    }
+    const int n_out = SWI ? N / 2 : N;
+    const int rbase = 4 * (lane >> 4);
+#pragma unroll
+    for (int m = 0; m < kTileMS; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = m * 16 + rbase + i;
+            if (r >= rows) continue;
+            const float rs = p.row_scale ? p.row_scale[row0 + r] : 1.0f;
+            uint16_t* orow = p.out + (size_t)(row0 + r) * n_out;
+            if constexpr (SWI) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    if (!cb_ok[c]) continue;
+                    const float v = silu(acc[m][c][i]) * acc[m][c + 2][i] * rs;
+                    orow[cbw[c] * 16 + (lane & 15)] = f32_to_f16_bits(v);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < kTileNS; ++c) {
+                    if (!cb_ok[c]) continue;
+                    float v = acc[m][c][i];
+                    if constexpr (ACT == MOE_ACT_RELU) v = fmaxf(v, 0.0f);
+                    orow[ncol[c]] = f32_to_f16_bits(v * rs);
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Host side: path choice, split choice, launch.
+// ------------------------------------------------------------------------------------
+static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
+
+int gemm_choose_path(int R, int E, int K, int N, int wtype, int act, int forced) {
+    (void)K; (void)N; (void)wtype; (void)act;
+    if (forced == MOE_PATH_STREAM || forced == MOE_PATH_TILE) return forced;
+    // average rows per (possibly) active expert
+    const int active = R < E ? R : E;
+    const double rows_per_expert = active > 0 ? (double)R / active : 0.0;
+    return rows_per_expert >= 48.0 ? MOE_PATH_TILE : MOE_PATH_STREAM;
+}
+
+int gemm_choose_split(int R, int E, int K, int N, int wtype, int act, int forced) {
+    if (forced >= 1) return forced > MOE_MAX_SPLIT_K ? MOE_MAX_SPLIT_K : forced;
+    const int KSB = (wtype == MOE_W_INT4) ? 128 : (wtype == MOE_W_INT8 ? 64 : 32);
+    const int nSB = K / KSB;
+    const int active = R < E ? R : E;
+    const int nbo = (act == MOE_ACT_SWIGLU) ? N / 32 : N / 16;
+    const long waves = (long)active * cdiv(R, active > 0 ? active * 16 : 16) * nbo;
+    // aim for >= 4096 streaming waves (16 per CU); keep >= 8 super-blocks per slice
+    int s = 1;
+    while (s < MOE_MAX_SPLIT_K && waves * s < 4096 && nSB / (2 * s) >= 8) s *= 2;
+    return s;
+}
+
+template <int WT, int ACT, bool GROUPED>
+static hipError_t stream_dispatch(const GemmParams& p, hipStream_t stream) {
+    const int nbo = (ACT == MOE_ACT_SWIGLU) ? p.N / 32 : p.N / 16;
+    const int ncbg = cdiv(nbo, 4);
+    const int active = p.R < p.E ? p.R : p.E;
+    const int mt_ub = cdiv(p.R, 16) + active;
+    const long blocks = (long)mt_ub * ncbg * p.split;
+    if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+    constexpr int PF = (WT == MOE_W_FP16) ? 4 : 4;
+    if (p.split > 1) {
+        gemm_stream_kernel<WT, ACT, GROUPED, true, PF><<<(unsigned)blocks, 256, 0, stream>>>(p, nbo, ncbg);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        const int n_out = (ACT == MOE_ACT_SWIGLU) ? p.N / 2 : p.N;
+        const long want = ((long)p.R * n_out + 255) / 256;
+        splitk_reduce_kernel<ACT><<<(unsigned)(want < 16384 ? want : 16384), 256, 0, stream>>>(p);
+    } else {
+        gemm_stream_kernel<WT, ACT, GROUPED, false, PF><<<(unsigned)blocks, 256, 0, stream>>>(p, nbo, ncbg);
+    }
+    return hipGetLastError();
+}
+
+template <int WT, int ACT, bool GROUPED>
+static hipError_t tile_dispatch(const GemmParams& p, hipStream_t stream) {
+    const int ncbw = p.N / 16;
+    const int ncbg = (ACT == MOE_ACT_SWIGLU) ? cdiv(ncbw / 2, 8) : cdiv(ncbw, 16);
+    const int active = p.R < p.E ? p.R : p.E;
+    const int mt_ub = cdiv(p.R, kTileBM) + active;
+    const long real = (long)mt_ub * ncbg;
+    const long grid = (real + 7) / 8 * 8;
+    if (grid > 0x7fffffffL) return hipErrorInvalidValue;
+    gemm_tile_kernel<WT, ACT, GROUPED><<<(unsigned)grid, 256, 0, stream>>>(p, ncbg, mt_ub, (int)real);
+    return hipGetLastError();
+}
+
+#define MOE_DISPATCH(FN, p, stream)                                                        \
+    do {                                                                                   \
+        const bool grouped = (p).group != 0;                                               \
+        switch ((p).wtype * 100 + (p).act * 10 + (grouped ? 1 : 0)) {                      \
+            case 0 * 100 + 0 * 10 + 0: return FN<MOE_W_INT4, MOE_ACT_NONE, false>(p, stream);   \
+            case 0 * 100 + 0 * 10 + 1: return FN<MOE_W_INT4, MOE_ACT_NONE, true>(p, stream);    \
+            case 0 * 100 + 1 * 10 + 0: return FN<MOE_W_INT4, MOE_ACT_RELU, false>(p, stream);   \
+            case 0 * 100 + 1 * 10 + 1: return FN<MOE_W_INT4, MOE_ACT_RELU, true>(p, stream);    \
+            case 0 * 100 + 2 * 10 + 0: return FN<MOE_W_INT4, MOE_ACT_SWIGLU, false>(p, stream); \
+            case 0 * 100 + 2 * 10 + 1: return FN<MOE_W_INT4, MOE_ACT_SWIGLU, true>(p, stream);  \
+            case 1 * 100 + 0 * 10 + 0: return FN<MOE_W_INT8, MOE_ACT_NONE, false>(p, stream);   \
+            case 1 * 100 + 0 * 10 + 1: return FN<MOE_W_INT8, MOE_ACT_NONE, true>(p, stream);    \
+            case 1 * 100 + 1 * 10 + 0: return FN<MOE_W_INT8, MOE_ACT_RELU, false>(p, stream);   \
+            case 1 * 100 + 1 * 10 + 1: return FN<MOE_W_INT8, MOE_ACT_RELU, true>(p, stream);    \
+            case 1 * 100 + 2 * 10 + 0: return FN<MOE_W_INT8, MOE_ACT_SWIGLU, false>(p, stream); \
+            case 1 * 100 + 2 * 10 + 1: return FN<MOE_W_INT8, MOE_ACT_SWIGLU, true>(p, stream);  \
+            case 2 * 100 + 0 * 10 + 0: return FN<MOE_W_FP16, MOE_ACT_NONE, false>(p, stream);   \
+            case 2 * 100 + 1 * 10 + 0: return FN<MOE_W_FP16, MOE_ACT_RELU, false>(p, stream);   \
+            case 2 * 100 + 2 * 10 + 0: return FN<MOE_W_FP16, MOE_ACT_SWIGLU, false>(p, stream); \
+            default: return hipErrorInvalidValue;                                          \
+        }                                                                                  \
+    } while (0)
+
+hipError_t launch_gemm_stream(const GemmParams& p, hipStream_t stream) {
+    MOE_DISPATCH(stream_dispatch, p, stream);
+}
+
+hipError_t launch_gemm_tile(const GemmParams& p, hipStream_t stream) {
+    MOE_DISPATCH(tile_dispatch, p, stream);
+}
+
+}  // namespace moe

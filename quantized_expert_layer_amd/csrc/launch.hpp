@@ -1,0 +1,46 @@
+// Internal launchers (one per kernel family).  Arguments are validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int gate_all,
+                             int32_t* ids, float* wts, hipStream_t stream);
+
+hipError_t launch_sort(const int32_t* ids, const float* wts, int R, int E,
+                       int32_t* perm, int32_t* inv_perm, int32_t* offsets, float* w_perm,
+                       hipStream_t stream);
+
+hipError_t launch_gather(const uint16_t* x, const int32_t* perm, int R, int k, int d,
+                         uint16_t* x_perm, hipStream_t stream);
+
+hipError_t launch_combine(const uint16_t* y, const int32_t* inv_perm, const float* w,
+                          const uint16_t* addend, int T, int k, int d, uint16_t* out,
+                          hipStream_t stream);
+
+hipError_t launch_dequant(const void* w, const uint16_t* scales, int wtype, int group,
+                          int E, int K, int N, uint16_t* out, hipStream_t stream);
+
+struct GemmParams {
+    const uint16_t* a;
+    const int32_t* offsets;
+    const void* w;
+    const uint16_t* scales;
+    const float* row_scale;
+    uint16_t* out;
+    float* partial;      // split-K partial sums [S][R][N] (stream path, S > 1)
+    int R, E, K, N;
+    int wtype, group, act;
+    int split;           // S
+};
+
+// Path/split decisions (host-only, deterministic in the arguments).
+int gemm_choose_path(int R, int E, int K, int N, int wtype, int act, int forced);
+int gemm_choose_split(int R, int E, int K, int N, int wtype, int act, int forced);
+
+hipError_t launch_gemm_stream(const GemmParams& p, hipStream_t stream);
+hipError_t launch_gemm_tile(const GemmParams& p, hipStream_t stream);
+
+}  // namespace moe

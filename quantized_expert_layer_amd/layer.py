@@ -1,0 +1,203 @@
+"""A whole MoE expert layer on the device: the C entry points called in order.
+
+DeviceLayer owns the packed expert weights in device memory; forward() enqueues
+  moe_route_topk -> moe_permute -> moe_grouped_gemm_wq (gate/up or W1, activation)
+  -> moe_grouped_gemm_wq (down or W2, gate weight as row scale)
+  [-> shared fp16 experts through the same GEMM entry, E = 1]
+  -> moe_unpermute_combine
+on one stream, with no host synchronisation.  Nothing here computes: torch only allocates.
+"""
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+import ctypes
+
+from . import (ACTS, GATES, WTYPES, MoEError, _ptr, _stream, lib, moe_gemm_workspace_size,
+               moe_grouped_gemm_wq, moe_pack_wq, moe_permute, moe_route_topk,
+               moe_unpermute_combine)
+
+
+def _dev(a, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+@dataclass
+class Workspace:
+    """Per-(T) device buffers reused across forward() calls."""
+    T: int
+    bufs: Dict[str, object] = field(default_factory=dict)
+
+
+class DeviceLayer:
+    def __init__(self, *, E: int, k: int, d: int, inter: int, act: str, wtype: str, group: int,
+                 gate_mode: str, codes1: np.ndarray, scales1: np.ndarray, codes2: np.ndarray,
+                 scales2: np.ndarray, shared: Optional[List[Tuple[np.ndarray, np.ndarray]]] = None,
+                 device: str = "cuda", gemm_path: int = 0):
+        import torch
+        self.E, self.k, self.d, self.inter = E, k, d, inter
+        self.act, self.wtype, self.group, self.gate_mode = act, wtype, group, gate_mode
+        self.n1 = 2 * inter if act == "swiglu" else inter
+        self.device = torch.device(device)
+        self.gemm_path = gemm_path
+        self.w1 = _dev(moe_pack_wq(codes1, wtype), self.device)
+        self.w2 = _dev(moe_pack_wq(codes2, wtype), self.device)
+        self.s1 = _dev(scales1.astype(np.float16), self.device)
+        self.s2 = _dev(scales2.astype(np.float16), self.device)
+        self.weight_bytes_per_expert = (self.w1.numel() + self.w2.numel()) // E + \
+            2 * (scales1[0].size + scales2[0].size)
+        self.shared = None
+        if shared:
+            # n always-on SwiGLU experts summed = one expert whose intermediate columns are
+            # concatenated: W1 = [gate_1 .. gate_n | up_1 .. up_n], W2 = [W2_1; ..; W2_n].
+            gates = [w1[:, : w1.shape[1] // 2] for w1, _ in shared]
+            ups = [w1[:, w1.shape[1] // 2:] for w1, _ in shared]
+            sw1 = np.concatenate(gates + ups, axis=1)[None]
+            sw2 = np.concatenate([w2 for _, w2 in shared], axis=0)[None]
+            self.shared_inter = sw2.shape[1]
+            self.shared = (_dev(moe_pack_wq(sw1.astype(np.float16), "fp16"), self.device),
+                           _dev(moe_pack_wq(sw2.astype(np.float16), "fp16"), self.device))
+
+    @classmethod
+    def from_inputs(cls, inp, device="cuda", gemm_path=0):
+        c = inp.cfg
+        return cls(E=c.E, k=c.k, d=c.d, inter=c.inter, act=c.act, wtype=inp.wtype,
+                   group=c.group, gate_mode=c.gate_mode, codes1=inp.codes1,
+                   scales1=inp.scales1, codes2=inp.codes2, scales2=inp.scales2,
+                   shared=inp.shared or None, device=device, gemm_path=gemm_path)
+
+    def workspace(self, T: int) -> Workspace:
+        import torch
+        dev, R, d = self.device, T * self.k, self.d
+        n_h = self.inter
+        b = {
+            "ids": torch.empty((T, self.k), dtype=torch.int32, device=dev),
+            "w": torch.empty((T, self.k), dtype=torch.float32, device=dev),
+            "perm": torch.empty(R, dtype=torch.int32, device=dev),
+            "inv": torch.empty(R, dtype=torch.int32, device=dev),
+            "off": torch.empty(self.E + 1, dtype=torch.int32, device=dev),
+            "xp": torch.empty((R, d), dtype=torch.float16, device=dev),
+            "wp": torch.empty(R, dtype=torch.float32, device=dev),
+            "h": torch.empty((R, n_h), dtype=torch.float16, device=dev),
+            "y": torch.empty((R, d), dtype=torch.float16, device=dev),
+            "out": torch.empty((T, d), dtype=torch.float16, device=dev),
+        }
+        ws1 = moe_gemm_workspace_size(R, self.E, d, self.n1, self.wtype, self.act, self.gemm_path)
+        ws2 = moe_gemm_workspace_size(R, self.E, self.inter, d, self.wtype, "none", self.gemm_path)
+        wsz = max(ws1, ws2)
+        if self.shared is not None:
+            b["sh_off"] = torch.tensor([0, T], dtype=torch.int32, device=dev)
+            b["sh_h"] = torch.empty((T, self.shared_inter), dtype=torch.float16, device=dev)
+            b["sh_y"] = torch.empty((T, d), dtype=torch.float16, device=dev)
+            wsz = max(wsz, moe_gemm_workspace_size(T, 1, d, 2 * self.shared_inter, "fp16",
+                                                   "swiglu", self.gemm_path),
+                      moe_gemm_workspace_size(T, 1, self.shared_inter, d, "fp16", "none",
+                                              self.gemm_path))
+        b["ws"] = torch.empty(max(wsz, 16), dtype=torch.uint8, device=dev)
+        return Workspace(T=T, bufs=b)
+
+    def forward(self, x, logits, ws: Optional[Workspace] = None, gate_in_gemm: bool = True,
+                stream=None):
+        """Layer output fp16 [T, d] for x fp16 [T, d] and router logits fp32 [T, E]."""
+        T = x.shape[0]
+        if ws is None or ws.T != T:
+            ws = self.workspace(T)
+        b = ws.bufs
+        path = self.gemm_path
+        moe_route_topk(logits, self.k, self.gate_mode, b["ids"], b["w"], stream=stream)
+        moe_permute(b["ids"], b["w"], x, self.E,
+                    out=(b["perm"], b["inv"], b["off"], b["xp"], b["wp"]), stream=stream)
+        moe_grouped_gemm_wq(b["xp"], b["off"], self.E, self.d, self.n1, self.w1, self.s1,
+                            self.wtype, self.group, self.act, out=b["h"], path=path,
+                            ws=b["ws"], stream=stream)
+        moe_grouped_gemm_wq(b["h"], b["off"], self.E, self.inter, self.d, self.w2, self.s2,
+                            self.wtype, self.group, "none",
+                            row_scale=b["wp"] if gate_in_gemm else None, out=b["y"],
+                            path=path, ws=b["ws"], stream=stream)
+        addend = None
+        if self.shared is not None:
+            moe_grouped_gemm_wq(x, b["sh_off"], 1, self.d, 2 * self.shared_inter,
+                                self.shared[0], None, "fp16", 0, "swiglu", out=b["sh_h"],
+                                path=path, ws=b["ws"], stream=stream)
+            moe_grouped_gemm_wq(b["sh_h"], b["sh_off"], 1, self.shared_inter, self.d,
+                                self.shared[1], None, "fp16", 0, "none", out=b["sh_y"],
+                                path=path, ws=b["ws"], stream=stream)
+            addend = b["sh_y"]
+        moe_unpermute_combine(b["y"], b["inv"], None if gate_in_gemm else b["w"], addend, T,
+                              self.k, out=b["out"], stream=stream)
+        return b["out"]
+
+    # ------------------------------------------------------------------ cached launch plan
+    def plan(self, ws: Workspace, x, logits, weights=None, gate_in_gemm: bool = True,
+             stream=None) -> "LayerPlan":
+        """Pre-marshal every C call of one forward() for fixed buffers, so that a step is
+        just the C calls (no per-call Python argument checks).  `weights` = (w1, w2) device
+        tensors in the packed layout (defaults to this layer's own)."""
+        w1, w2 = weights if weights is not None else (self.w1, self.w2)
+        b, L, T = ws.bufs, lib(), ws.T
+        st = _stream(stream)
+        path = self.gemm_path
+        opts = None
+        if path:
+            from . import GemmOpts
+            opts = GemmOpts()
+            opts.path = path
+        ob = ctypes.byref(opts) if opts is not None else None
+        wsp, wsn = _ptr(b["ws"]), b["ws"].numel()
+        wt, ac = WTYPES[self.wtype], ACTS[self.act]
+        calls = [
+            ("route", L.moe_route_topk, (_ptr(logits), T, self.E, self.k, GATES[self.gate_mode],
+                                         _ptr(b["ids"]), _ptr(b["w"]), st)),
+            ("permute", L.moe_permute, (_ptr(b["ids"]), _ptr(b["w"]), _ptr(x), T, self.k, self.E,
+                                        self.d, _ptr(b["perm"]), _ptr(b["inv"]), _ptr(b["off"]),
+                                        _ptr(b["xp"]), _ptr(b["wp"]), None, 0, st)),
+            ("gemm1", L.moe_grouped_gemm_wq, (_ptr(b["xp"]), _ptr(b["off"]), T * self.k, self.E,
+                                              self.d, self.n1, _ptr(w1), _ptr(self.s1), wt,
+                                              self.group, ac, None, _ptr(b["h"]), ob, wsp, wsn,
+                                              st)),
+            ("gemm2", L.moe_grouped_gemm_wq, (_ptr(b["h"]), _ptr(b["off"]), T * self.k, self.E,
+                                              self.inter, self.d, _ptr(w2), _ptr(self.s2), wt,
+                                              self.group, 0,
+                                              _ptr(b["wp"]) if gate_in_gemm else None,
+                                              _ptr(b["y"]), ob, wsp, wsn, st)),
+        ]
+        addend = None
+        if self.shared is not None:
+            calls += [
+                ("shared1", L.moe_grouped_gemm_wq, (_ptr(x), _ptr(b["sh_off"]), T, 1, self.d,
+                                                    2 * self.shared_inter, _ptr(self.shared[0]),
+                                                    None, 2, 0, 2, None, _ptr(b["sh_h"]), ob,
+                                                    wsp, wsn, st)),
+                ("shared2", L.moe_grouped_gemm_wq, (_ptr(b["sh_h"]), _ptr(b["sh_off"]), T, 1,
+                                                    self.shared_inter, self.d,
+                                                    _ptr(self.shared[1]), None, 2, 0, 0, None,
+                                                    _ptr(b["sh_y"]), ob, wsp, wsn, st)),
+            ]
+            addend = b["sh_y"]
+        calls.append(("combine", L.moe_unpermute_combine,
+                      (_ptr(b["y"]), _ptr(b["inv"]), None if gate_in_gemm else _ptr(b["w"]),
+                       _ptr(addend), T, self.k, self.d, _ptr(b["out"]), st)))
+        return LayerPlan(calls, b["out"], keep=(opts, x, logits, w1, w2))
+
+
+class LayerPlan:
+    """The C calls of one layer forward with their arguments fixed."""
+
+    def __init__(self, calls, out, keep):
+        self.calls = calls
+        self.out = out
+        self._keep = keep                     # keeps referenced tensors / opts alive
+        self.names = [c[0] for c in calls]
+
+    def run(self, marker=None):
+        for i, (name, fn, args) in enumerate(self.calls):
+            if marker is not None:
+                marker(i)
+            st = fn(*args)
+            if st != 0:
+                raise MoEError(fn.__name__, st)
+        if marker is not None:
+            marker(len(self.calls))
+        return self.out

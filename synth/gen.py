@@ -21,6 +21,8 @@ tensor.  Value distributions follow the layer shapes being modelled:
 A "coverage" variant replaces the weight draw by codes uniform over the full code
 range and scales uniform in [2^-8, 2^-4], so that every code value occurs.
 """
+import concurrent.futures
+import os
 from dataclasses import dataclass, field
 from typing import List, Optional, Tuple
 
@@ -85,7 +87,8 @@ def _expert_mats(rngs, E, K, N, qmax, group, coverage):
     G = 1 if group == 0 else K // group
     codes = np.empty((E, K, N), dtype=np.int8)
     scales = np.empty((E, G, N), dtype=np.float16)
-    for e in range(E):
+
+    def one(e):
         rng = rngs[e]
         if coverage:
             codes[e] = rng.integers(-qmax - 1, qmax + 1, size=(K, N), dtype=np.int8)
@@ -93,6 +96,15 @@ def _expert_mats(rngs, E, K, N, qmax, group, coverage):
         else:
             w = rng.standard_normal((K, N), dtype=np.float32) * np.float32(0.02)
             codes[e], scales[e] = _rtn_codes(w, qmax, group)
+
+    # Each expert has its own stream, so the result does not depend on the thread count.
+    workers = max(1, min(E, 16, os.cpu_count() or 1))
+    if workers == 1 or E * K * N < (1 << 22):
+        for e in range(E):
+            one(e)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, range(E)))
     return codes, scales
 
 

@@ -1,0 +1,208 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every symbol include/moe_wq.h declares, reject invalid
+arguments with the documented status codes before touching a device, and pack weights into
+the documented layout (checked with a test-local unpacker written from that description).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import quantized_expert_layer_amd as q
+from tests.conftest import ROOT, gpu_available
+
+HEADER = os.path.join(ROOT, "include", "moe_wq.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^[\w\s\*]*?\b(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared()
+    assert set(declared) == set(q.EXPORTED_SYMBOLS), declared
+    L = q.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", q.lib_path], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", nm))
+    assert set(declared) <= exported
+
+
+def test_version_and_status_strings():
+    assert q.version() >= 100
+    for s in (0, -1, -2, -3, -4, -5):
+        assert q.status_str(s).startswith("MOE_")
+    assert q.status_str(123) == "unknown status"
+
+
+def test_packed_bytes():
+    assert q.moe_packed_bytes("int4", 3, 256, 32) == 3 * 256 * 32 // 2
+    assert q.moe_packed_bytes("int8", 3, 256, 32) == 3 * 256 * 32
+    assert q.moe_packed_bytes("fp16", 3, 256, 32) == 3 * 256 * 32 * 2
+    assert q.moe_packed_bytes("int4", 3, 100, 32) == 0        # K % 128
+    assert q.moe_packed_bytes("int4", 3, 128, 24) == 0        # N % 16
+
+
+# ---------------------------------------------------------------- packer vs documented layout
+def _unpack(packed, wtype, E, K, N):
+    """Inverse of the documented layout, written independently of the C packer."""
+    ncb = N // 16
+    if wtype == "int4":
+        ksb = 128
+        words = packed.view(np.uint32).reshape(E, ncb, K // ksb, 64, 4)
+        out = np.empty((E, K, N), np.int64)
+        order = [0, 2, 4, 6, 1, 3, 5, 7]
+        for l in range(64):
+            n = np.arange(ncb)[:, None] * 16 + (l & 15)                      # [ncb, 1]
+            for j in range(4):
+                w = words[:, :, :, l, j].astype(np.int64)                      # [E, ncb, nSB]
+                for p in range(8):
+                    k = np.arange(K // ksb)[None, :] * ksb + j * 32 + 8 * (l >> 4) + order[p]
+                    out[:, k, n] = ((w >> (4 * p)) & 0xF) - 8
+        return out
+    if wtype == "int8":
+        ksb = 64
+        words = packed.view(np.uint32).reshape(E, ncb, K // ksb, 64, 4)
+        out = np.empty((E, K, N), np.int64)
+        for l in range(64):
+            n = np.arange(ncb)[:, None] * 16 + (l & 15)
+            for wi in range(4):
+                w = words[:, :, :, l, wi].astype(np.int64)
+                for b in range(4):
+                    k = (np.arange(K // ksb)[None, :] * ksb + (wi >> 1) * 32 + 8 * (l >> 4)
+                         + 4 * (wi & 1) + b)
+                    out[:, k, n] = ((w >> (8 * b)) & 0xFF) - 128
+        return out
+    ksb = 32
+    halves = packed.view(np.uint16).reshape(E, ncb, K // ksb, 64, 8)
+    out = np.empty((E, K, N), np.uint16)
+    for l in range(64):
+        n = np.arange(ncb)[:, None] * 16 + (l & 15)
+        for i in range(8):
+            k = np.arange(K // ksb)[None, :] * ksb + 8 * (l >> 4) + i
+            out[:, k, n] = halves[:, :, :, l, i]
+    return out
+
+
+@pytest.mark.parametrize("wtype,E,K,N", [("int4", 2, 256, 48), ("int8", 3, 128, 32),
+                                         ("int4", 1, 384, 16)])
+def test_pack_roundtrip_integer_codes(wtype, E, K, N):
+    rng = np.random.default_rng(1)
+    lo, hi = (-8, 8) if wtype == "int4" else (-128, 128)
+    codes = rng.integers(lo, hi, size=(E, K, N)).astype(np.int8)
+    packed = q.moe_pack_wq(codes, wtype)
+    assert packed.size == q.moe_packed_bytes(wtype, E, K, N)
+    assert np.array_equal(_unpack(packed, wtype, E, K, N), codes)
+
+
+def test_pack_roundtrip_fp16():
+    rng = np.random.default_rng(2)
+    w = rng.standard_normal((2, 128, 32)).astype(np.float16)
+    packed = q.moe_pack_wq(w, "fp16")
+    assert np.array_equal(_unpack(packed, "fp16", 2, 128, 32), w.view(np.uint16))
+
+
+def test_pack_int4_nibble_order_matches_page():
+    # K-step 0 of lane 0 holds rows 0..7 of column 0; nibble p holds row order[p] (+8).
+    codes = np.zeros((1, 128, 16), np.int8)
+    codes[0, :8, 0] = np.arange(8) - 4                       # rows 0..7 -> -4..3
+    word = q.moe_pack_wq(codes, "int4").view(np.uint32)[0]
+    nibbles = [(int(word) >> (4 * p)) & 0xF for p in range(8)]
+    assert nibbles == [r - 4 + 8 for r in (0, 2, 4, 6, 1, 3, 5, 7)]
+
+
+def test_pack_rejects_out_of_range_int4():
+    codes = np.zeros((1, 128, 16), np.int8)
+    codes[0, 5, 3] = 8
+    with pytest.raises(q.MoEError) as ei:
+        q.moe_pack_wq(codes, "int4")
+    assert ei.value.status == q.MOE_ERR_INVALID
+
+
+# ---------------------------------------------------------------- validation before launch
+FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced on these paths
+MIS = ctypes.c_void_p(0x10002)        # misaligned
+
+
+def test_route_topk_validation():
+    L = q.lib()
+    assert L.moe_route_topk(FAKE, 4, 8, 9, 0, FAKE, FAKE, None) == q.MOE_ERR_INVALID   # k > E
+    assert L.moe_route_topk(FAKE, 4, 8, 0, 0, FAKE, FAKE, None) == q.MOE_ERR_INVALID   # k = 0
+    assert L.moe_route_topk(FAKE, 4, 300, 2, 0, FAKE, FAKE, None) == q.MOE_ERR_INVALID  # E > 256
+    assert L.moe_route_topk(FAKE, 4, 8, 2, 7, FAKE, FAKE, None) == q.MOE_ERR_INVALID   # gate mode
+    assert L.moe_route_topk(None, 4, 8, 2, 0, FAKE, FAKE, None) == q.MOE_ERR_INVALID
+    assert L.moe_route_topk(None, 0, 8, 2, 0, None, None, None) == q.MOE_OK            # T = 0
+    assert L.moe_route_topk(FAKE, -1, 8, 2, 0, FAKE, FAKE, None) == q.MOE_ERR_INVALID
+
+
+def test_permute_validation():
+    L = q.lib()
+    args = lambda **kw: [kw.get(n, v) for n, v in (
+        ("ids", FAKE), ("w", FAKE), ("x", FAKE), ("T", 4), ("k", 2), ("E", 8), ("d", 64),
+        ("perm", FAKE), ("inv", FAKE), ("off", FAKE), ("xp", FAKE), ("wp", FAKE),
+        ("ws", None), ("wsb", 0), ("s", None))]
+    assert L.moe_permute(*args(d=60)) == q.MOE_ERR_UNSUPPORTED
+    assert L.moe_permute(*args(k=9)) == q.MOE_ERR_INVALID
+    assert L.moe_permute(*args(x=MIS)) == q.MOE_ERR_INVALID
+    assert L.moe_permute(*args(w=None)) == q.MOE_ERR_INVALID          # w_perm needs topk_w
+    assert L.moe_permute(*args(perm=None)) == q.MOE_ERR_INVALID
+    assert L.moe_permute(*args(T=0, ids=None, x=None)) == q.MOE_OK
+
+
+def _gemm_args(**kw):
+    d = dict(a=FAKE, off=FAKE, R=64, E=8, K=256, N=64, w=FAKE, s=FAKE, wt=0, g=128, act=1,
+             rs=None, out=FAKE, opts=None, ws=None, wsb=0, stream=None)
+    d.update(kw)
+    return [d[n] for n in ("a", "off", "R", "E", "K", "N", "w", "s", "wt", "g", "act", "rs",
+                           "out", "opts", "ws", "wsb", "stream")]
+
+
+def test_gemm_validation():
+    L = q.lib()
+    g = L.moe_grouped_gemm_wq
+    assert g(*_gemm_args(K=200)) == q.MOE_ERR_UNSUPPORTED
+    assert g(*_gemm_args(N=40)) == q.MOE_ERR_UNSUPPORTED
+    assert g(*_gemm_args(N=48, act=2)) == q.MOE_ERR_UNSUPPORTED        # SwiGLU needs N % 32
+    assert g(*_gemm_args(g=64)) == q.MOE_ERR_UNSUPPORTED
+    assert g(*_gemm_args(wt=2, g=128)) == q.MOE_ERR_UNSUPPORTED        # fp16 has no groups
+    assert g(*_gemm_args(wt=5)) == q.MOE_ERR_INVALID
+    assert g(*_gemm_args(act=3)) == q.MOE_ERR_INVALID
+    assert g(*_gemm_args(E=0)) == q.MOE_ERR_INVALID
+    assert g(*_gemm_args(E=257)) == q.MOE_ERR_INVALID
+    assert g(*_gemm_args(s=None)) == q.MOE_ERR_INVALID                 # int codes need scales
+    assert g(*_gemm_args(a=MIS)) == q.MOE_ERR_INVALID
+    assert g(*_gemm_args(R=0, a=None, out=None)) == q.MOE_OK
+    o = q.GemmOpts()
+    o.path = 9
+    assert g(*_gemm_args(opts=ctypes.byref(o))) == q.MOE_ERR_INVALID
+    o.path, o.split_k = q.PATH_STREAM, 4                               # needs a workspace
+    need = L.moe_gemm_workspace_size(64, 8, 256, 64, 0, 1, ctypes.byref(o))
+    assert need == 4 * 64 * 64 * 4
+    assert g(*_gemm_args(opts=ctypes.byref(o))) == q.MOE_ERR_WORKSPACE
+    assert g(*_gemm_args(opts=ctypes.byref(o), ws=FAKE, wsb=need - 1)) == q.MOE_ERR_WORKSPACE
+
+
+def test_combine_and_dequant_validation():
+    L = q.lib()
+    assert L.moe_unpermute_combine(FAKE, FAKE, None, None, 4, 9, 64, FAKE, None) == q.MOE_ERR_INVALID
+    assert L.moe_unpermute_combine(FAKE, FAKE, None, None, 4, 2, 12, FAKE, None) == q.MOE_ERR_UNSUPPORTED
+    assert L.moe_unpermute_combine(FAKE, FAKE, None, MIS, 4, 2, 64, FAKE, None) == q.MOE_ERR_INVALID
+    assert L.moe_dequant(FAKE, FAKE, 2, 0, 2, 128, 16, FAKE, None) == q.MOE_ERR_INVALID  # fp16
+    assert L.moe_dequant(FAKE, FAKE, 0, 0, 2, 100, 16, FAKE, None) == q.MOE_ERR_UNSUPPORTED
+    assert L.moe_dequant(None, FAKE, 0, 0, 2, 128, 16, FAKE, None) == q.MOE_ERR_INVALID
+
+
+@pytest.mark.skipif(gpu_available(), reason="valid calls would launch on a real GPU")
+def test_valid_calls_report_no_device_without_gpu():
+    L = q.lib()
+    assert L.moe_route_topk(FAKE, 4, 8, 2, 0, FAKE, FAKE, None) == q.MOE_ERR_NO_DEVICE
+    assert L.moe_grouped_gemm_wq(*_gemm_args()) == q.MOE_ERR_NO_DEVICE
+    assert L.moe_dequant(FAKE, FAKE, 0, 0, 2, 128, 16, FAKE, None) == q.MOE_ERR_NO_DEVICE

@@ -1,0 +1,169 @@
+"""GPU parity: Algorithm 1 dequantization (bit-exact) and the grouped GEMM (tolerance; exact
+special cases) on both GEMM paths, every weight type and activation."""
+import numpy as np
+import pytest
+
+import oracle
+import quantized_expert_layer_amd as q
+import synth
+from tests.gpu_util import assert_layer_close, case, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------- dequant (Algorithm 1)
+@pytest.mark.parametrize("wtype,group,coverage", [("int4", 0, True), ("int4", 128, True),
+                                                  ("int8", 0, True), ("int8", 128, True),
+                                                  ("int4", 0, False), ("int8", 0, False)])
+def test_dequant_bit_exact(wtype, group, coverage):
+    case(f"dequant {wtype} g={group} coverage={coverage}")
+    cfg = synth.LayerConfig("dq", 11, d=384, inter=256, E=3, k=1, act="relu", wtypes=(wtype,),
+                            group=group, gate_mode="topk", zipf_bias=False, T_list=(1,))
+    inp = synth.make_inputs(cfg, 1, wtype=wtype, coverage=coverage)
+    for codes, scales in ((inp.codes1, inp.scales1), (inp.codes2, inp.scales2)):
+        E, K, N = codes.shape
+        out = q.moe_dequant(dev(q.moe_pack_wq(codes, wtype)), dev(scales), wtype, group, E, K, N)
+        ref = oracle.dequant_algorithm1(codes, scales, group)
+        assert np.array_equal(host(out).view(np.uint16), ref.view(np.uint16))
+
+
+@pytest.mark.parametrize("wtype", ["int4", "int8"])
+def test_dequant_unit_scale_reproduces_every_code(wtype):
+    # s = 1: W_dq == code for every code value at every position in the word
+    case(f"dequant unit scale {wtype}")
+    lo, hi = (-8, 8) if wtype == "int4" else (-128, 128)
+    K, N = 256, 32
+    codes = ((np.arange(K * N).reshape(1, K, N) % (hi - lo)) + lo).astype(np.int8)
+    scales = np.ones((1, 1, N), np.float16)
+    out = q.moe_dequant(dev(q.moe_pack_wq(codes, wtype)), dev(scales), wtype, 0, 1, K, N)
+    assert np.array_equal(host(out).astype(np.float64), codes.astype(np.float64))
+
+
+def test_dequant_hand_worked_products(golden_dir):
+    # the golden products (ties to even, subnormal scales) through the GPU's fp16 multiply
+    rows = []
+    for line in open(f"{golden_dir}/algorithm1_products.txt"):
+        line = line.split("#", 1)[0].split()
+        if line:
+            rows.append((int(line[0], 16), int(line[1]), int(line[2], 16)))
+    N = 16
+    codes = np.zeros((1, 128, N), np.int8)
+    scales = np.ones((1, 1, N), np.float16)
+    for n, (sb, c, _) in enumerate(rows):
+        codes[0, 0, n] = c
+        scales[0, 0, n] = np.array([sb], np.uint16).view(np.float16)[0]
+    case("dequant golden products")
+    out = host(q.moe_dequant(dev(q.moe_pack_wq(codes, "int8")), dev(scales), "int8", 0, 1, 128, N))
+    got = out.view(np.uint16)[0, 0]
+    for n, (_, _, eb) in enumerate(rows):
+        assert got[n] == eb, (n, hex(got[n]), hex(eb))
+
+
+# ---------------------------------------------------------------- grouped GEMM
+def _gemm_case(E, K, N, wtype, group, T, k, seed, skew=True):
+    rng = np.random.default_rng(seed)
+    cfg = synth.LayerConfig("g", 12, d=K, inter=N, E=E, k=1, act="relu", wtypes=(wtype,),
+                            group=group, gate_mode="topk", zipf_bias=False, T_list=(1,))
+    inp = synth.make_inputs(cfg, 1, wtype=wtype)
+    codes, scales = inp.codes1, inp.scales1
+    ids = synth.gen.random_ids(T, k, E, seed=seed, skew=skew)
+    _, _, off = oracle.stable_expert_sort(ids, E)
+    R = T * k
+    a = rng.standard_normal((R, K)).astype(np.float16)
+    return codes, scales, off, a
+
+
+GEMM_CASES = [
+    # E, K, N, wtype, group, T, k
+    (8, 128, 256, "int4", 0, 16, 2),
+    (32, 1024, 512, "int4", 0, 300, 1),
+    (32, 1024, 512, "int8", 0, 300, 1),
+    (60, 256, 352, "int4", 128, 17, 4),
+    (60, 256, 352, "int4", 128, 200, 4),
+    (16, 512, 160, "int8", 128, 70, 2),
+    (5, 384, 96, "int4", 128, 1, 2),
+    (3, 256, 48, "int4", 0, 333, 1),
+]
+
+
+@pytest.mark.parametrize("path", [q.PATH_STREAM, q.PATH_TILE])
+@pytest.mark.parametrize("act", ["none", "relu", "swiglu"])
+@pytest.mark.parametrize("E,K,N,wtype,group,T,k", GEMM_CASES)
+def test_grouped_gemm_matches_oracle(E, K, N, wtype, group, T, k, act, path):
+    if act == "swiglu" and N % 32:
+        pytest.skip("SwiGLU needs an even number of 16-column blocks")
+    codes, scales, off, a = _gemm_case(E, K, N, wtype, group, T, k, seed=E * K + N)
+    R = a.shape[0]
+    rs = np.random.default_rng(3).random(R, dtype=np.float32)
+    case(f"gemm E={E} K={K} N={N} {wtype} g={group} T={T} k={k} act={act} path={path}")
+    out = q.moe_grouped_gemm_wq(dev(a), dev(off), E, K, N, dev(q.moe_pack_wq(codes, wtype)),
+                                dev(scales), wtype, group, act, row_scale=dev(rs), path=path)
+    wdq = oracle.dequant_algorithm1(codes, scales, group)
+    ref = oracle.grouped_gemm(a, off, wdq, act, row_scale=rs)
+    assert_layer_close(host(out), ref, "grouped gemm")
+
+
+@pytest.mark.parametrize("split", [2, 3, 4, 16])
+def test_stream_split_k_matches_oracle_and_unsplit(split):
+    E, K, N = 4, 2048, 256
+    codes, scales, off, a = _gemm_case(E, K, N, "int4", 128, 3, 2, seed=split)
+    w = dev(q.moe_pack_wq(codes, "int4"))
+    wdq = oracle.dequant_algorithm1(codes, scales, 128)
+    for act in ("relu", "swiglu"):
+        case(f"split-k S={split} act={act}")
+        o1 = host(q.moe_grouped_gemm_wq(dev(a), dev(off), E, K, N, w, dev(scales), "int4", 128,
+                                        act, path=q.PATH_STREAM, split_k=1))
+        oS = host(q.moe_grouped_gemm_wq(dev(a), dev(off), E, K, N, w, dev(scales), "int4", 128,
+                                        act, path=q.PATH_STREAM, split_k=split))
+        ref = oracle.grouped_gemm(a, off, wdq, act)
+        assert_layer_close(oS, ref, "split")
+        assert_layer_close(o1, ref, "unsplit")
+
+
+@pytest.mark.parametrize("path", [q.PATH_STREAM, q.PATH_TILE])
+@pytest.mark.parametrize("wtype,group", [("int4", 0), ("int4", 128), ("int8", 0), ("int8", 128)])
+def test_one_hot_rows_reproduce_dequantized_weight_rows(wtype, group, path):
+    # a one-hot row i of expert e gives exactly W_dq[e, i, :] (pins packing, nibble order,
+    # scale indexing and the fragment layout inside the fused kernel)
+    E, K, N = 3, 256, 64
+    inp = synth.make_inputs(synth.LayerConfig("oh", 13, d=K, inter=N, E=E, k=1, act="relu",
+                                              wtypes=(wtype,), group=group, gate_mode="topk",
+                                              zipf_bias=False, T_list=(1,)),
+                            1, wtype=wtype, coverage=True)
+    codes, scales = inp.codes1, inp.scales1
+    rows = [np.arange(0, K, 3), np.arange(1, K, 5), np.arange(2, K, 2)]   # ragged row counts
+    a = np.concatenate([np.eye(K, dtype=np.float16)[r] for r in rows])
+    off = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    case(f"one-hot {wtype} g={group} path={path}")
+    out = host(q.moe_grouped_gemm_wq(dev(a), dev(off), E, K, N, dev(q.moe_pack_wq(codes, wtype)),
+                                     dev(scales), wtype, group, "none", path=path))
+    wdq = oracle.dequant_algorithm1(codes, scales, group)
+    ref = np.concatenate([wdq[e][r] for e, r in enumerate(rows)])
+    assert np.array_equal(out.view(np.uint16), ref.view(np.uint16))
+
+
+@pytest.mark.parametrize("path", [q.PATH_STREAM, q.PATH_TILE])
+def test_fp16_weights_and_zero_row_experts(path):
+    E, K, N, T = 6, 256, 128, 40
+    rng = np.random.default_rng(8)
+    w = (rng.standard_normal((E, K, N)) * 0.05).astype(np.float16)
+    off = np.array([0, 0, 17, 17, 17, 40, 40], np.int32)      # experts 0, 2, 3, 5 have no rows
+    a = rng.standard_normal((T, K)).astype(np.float16)
+    for act in ("none", "swiglu"):
+        case(f"fp16 weights act={act} path={path}")
+        out = q.moe_grouped_gemm_wq(dev(a), dev(off), E, K, N, dev(q.moe_pack_wq(w, "fp16")), None,
+                                    "fp16", 0, act, path=path)
+        ref = oracle.grouped_gemm(a, off, w.astype(np.float64), act)
+        assert_layer_close(host(out), ref, "fp16 gemm")
+
+
+def test_gemm_rows_beyond_offsets_are_untouched():
+    E, K, N = 2, 128, 32
+    codes, scales, _, a = _gemm_case(E, K, N, "int4", 0, 20, 1, seed=4)
+    off = np.array([0, 5, 12], np.int32)                       # rows 12..19 belong to no expert
+    import torch
+    out = torch.full((20, N), 7.0, dtype=torch.float16, device="cuda")
+    case("gemm rows beyond offsets")
+    q.moe_grouped_gemm_wq(dev(a), dev(off), E, K, N, dev(q.moe_pack_wq(codes, "int4")),
+                          dev(scales), "int4", 0, "relu", out=out)
+    assert (host(out)[12:] == 7.0).all()

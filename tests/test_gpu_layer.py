@@ -1,0 +1,84 @@
+"""GPU parity of the whole layer (route -> permute -> GEMM1 -> GEMM2 -> combine) against the
+fp64 oracle on every layer shape, plus determinism and token-order equivariance."""
+import numpy as np
+import pytest
+
+import oracle
+import quantized_expert_layer_amd as q
+import synth
+from tests.gpu_util import assert_layer_close, case, dev, host
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def _layer(name, T, wtype=None, active=0, path=0):
+    key = (name, T, wtype, active)
+    if key not in _CACHE:
+        _CACHE.clear()
+        inp = synth.make_inputs(synth.get_config(name), T, wtype=wtype, active=active)
+        _CACHE[key] = (inp, {})
+    inp, layers = _CACHE[key]
+    if path not in layers:
+        layers[path] = q.DeviceLayer.from_inputs(inp, gemm_path=path)
+    return inp, layers[path]
+
+
+# (config, T, weight type, active experts, tokens the oracle checks: None = all)
+LAYER_CASES = [
+    ("tiny", 16, None, 0, None),
+    ("mt_encoder", 3840, "int4", 0, None),
+    ("mt_encoder", 3840, "int8", 0, None),
+    ("mt_encoder", 3840, "int4", 1, 512),
+    ("mt_encoder", 3840, "int8", 8, 512),
+    ("qwen15_moe", 17, None, 0, None),
+    ("qwen15_moe", 544, None, 0, None),
+    ("dsv2_lite", 9, None, 0, None),
+    ("dsv2_lite", 288, None, 0, None),
+    ("phi35_moe", 1, None, 0, None),
+    ("phi35_moe", 17, None, 0, None),
+    ("phi35_moe", 8192, None, 0, 24),
+]
+
+
+def _tokens(T, n):
+    if n is None or n >= T:
+        return np.arange(T)
+    rng = np.random.default_rng(T)
+    return np.unique(np.concatenate([[0, T - 1], rng.choice(T, n - 2, replace=False)]))
+
+
+@pytest.mark.parametrize("name,T,wtype,active,n_check", LAYER_CASES)
+def test_layer_matches_oracle(name, T, wtype, active, n_check):
+    inp, layer = _layer(name, T, wtype, active)
+    case(f"layer {name} T={T} wtype={inp.wtype} active={active}")
+    out = host(layer.forward(dev(inp.x), dev(inp.logits)))
+    toks = _tokens(T, n_check)
+    ref = oracle.moe_layer_tokens(inp, toks)
+    rel, mx = assert_layer_close(out[toks], ref, f"{name} T={T}")
+    print(f"[gpu-case] {name} T={T}: rel-L2 {rel:.2e} max/rms {mx:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 16), ("qwen15_moe", 544), ("dsv2_lite", 9)])
+def test_layer_paths_and_gate_placement_agree(name, T):
+    for path in (q.PATH_STREAM, q.PATH_TILE):
+        inp, layer = _layer(name, T, path=path)
+        ref = oracle.moe_layer(inp)
+        for gate_in_gemm in (True, False):
+            case(f"layer {name} T={T} path={path} gate_in_gemm={gate_in_gemm}")
+            out = host(layer.forward(dev(inp.x), dev(inp.logits), gate_in_gemm=gate_in_gemm))
+            assert_layer_close(out, ref, f"path {path} gate_in_gemm {gate_in_gemm}")
+
+
+@pytest.mark.parametrize("name,T", [("qwen15_moe", 544), ("mt_encoder", 3840), ("phi35_moe", 17)])
+def test_layer_is_deterministic_and_token_order_equivariant(name, T):
+    inp, layer = _layer(name, T)
+    case(f"determinism {name} T={T}")
+    x, L = dev(inp.x), dev(inp.logits)
+    a = host(layer.forward(x, L)).copy()
+    b = host(layer.forward(x, L)).copy()
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    p = np.random.default_rng(1).permutation(T)
+    c = host(layer.forward(dev(inp.x[p]), dev(inp.logits[p])))
+    assert np.array_equal(c.view(np.uint16), a[p].view(np.uint16))
