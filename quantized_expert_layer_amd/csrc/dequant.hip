@@ -43,9 +43,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(const u32x4* __restrict__ 
         }
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-            const f16x2 v = q[h] * s2;
-            o[(size_t)(k0 + 2 * h) * N] = __builtin_bit_cast(uint16_t, v[0]);
-            o[(size_t)(k0 + 2 * h + 1) * N] = __builtin_bit_cast(uint16_t, v[1]);
+            // bit-cast the whole pair: a bit-cast of a single vector element is not used
+            // because hipcc mistranslates it (the high element reads as the low one)
+            const uint32_t v = __builtin_bit_cast(uint32_t, q[h] * s2);
+            o[(size_t)(k0 + 2 * h) * N] = (uint16_t)(v & 0xFFFFu);
+            o[(size_t)(k0 + 2 * h + 1) * N] = (uint16_t)(v >> 16);
         }
     }
 }

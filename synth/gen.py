@@ -160,6 +160,15 @@ def make_inputs(cfg: LayerConfig, T: int, wtype: Optional[str] = None, active: i
                        codes2=codes2, scales2=scales2, shared=shared)
 
 
+def make_expert_weights(E: int, K: int, N: int, wtype: str, group: int, seed: int,
+                        coverage: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """Codes int8 [E, K, N] and fp16 scales [E, G, N] of one weight matrix per expert (for
+    single-GEMM tests), drawn like a layer's weights."""
+    ss = np.random.SeedSequence([seed, E, K, N, WTYPE_ID[wtype], group, int(coverage), SEED_TAG])
+    rngs = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(E)]
+    return _expert_mats(rngs, E, K, N, QMAX[wtype], group, coverage)
+
+
 def random_ids(T: int, k: int, E: int, seed: int = 0, skew: bool = False) -> np.ndarray:
     """Routing ids [T, k] with k distinct experts per token (for sort/permute tests)."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, T, k, E, SEED_TAG])))

@@ -62,14 +62,10 @@ def test_dequant_hand_worked_products(golden_dir):
 # ---------------------------------------------------------------- grouped GEMM
 def _gemm_case(E, K, N, wtype, group, T, k, seed, skew=True):
     rng = np.random.default_rng(seed)
-    cfg = synth.LayerConfig("g", 12, d=K, inter=N, E=E, k=1, act="relu", wtypes=(wtype,),
-                            group=group, gate_mode="topk", zipf_bias=False, T_list=(1,))
-    inp = synth.make_inputs(cfg, 1, wtype=wtype)
-    codes, scales = inp.codes1, inp.scales1
+    codes, scales = synth.gen.make_expert_weights(E, K, N, wtype, group, seed)
     ids = synth.gen.random_ids(T, k, E, seed=seed, skew=skew)
     _, _, off = oracle.stable_expert_sort(ids, E)
-    R = T * k
-    a = rng.standard_normal((R, K)).astype(np.float16)
+    a = rng.standard_normal((T * k, K)).astype(np.float16)
     return codes, scales, off, a
 
 
@@ -126,11 +122,7 @@ def test_one_hot_rows_reproduce_dequantized_weight_rows(wtype, group, path):
     # a one-hot row i of expert e gives exactly W_dq[e, i, :] (pins packing, nibble order,
     # scale indexing and the fragment layout inside the fused kernel)
     E, K, N = 3, 256, 64
-    inp = synth.make_inputs(synth.LayerConfig("oh", 13, d=K, inter=N, E=E, k=1, act="relu",
-                                              wtypes=(wtype,), group=group, gate_mode="topk",
-                                              zipf_bias=False, T_list=(1,)),
-                            1, wtype=wtype, coverage=True)
-    codes, scales = inp.codes1, inp.scales1
+    codes, scales = synth.gen.make_expert_weights(E, K, N, wtype, group, seed=77, coverage=True)
     rows = [np.arange(0, K, 3), np.arange(1, K, 5), np.arange(2, K, 2)]   # ragged row counts
     a = np.concatenate([np.eye(K, dtype=np.float16)[r] for r in rows])
     off = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
