@@ -75,6 +75,13 @@ def lib():
     if not os.path.exists(lib_path):
         raise MoELibraryError(f"{lib_path} is missing: build it with "
                               "`python -m quantized_expert_layer_amd.build`")
+    # torch ships its own HIP runtime under the same soname.  Load it first so that the
+    # library binds to that copy: two HIP runtimes in one process do not share devices,
+    # and the library would then find no usable device for torch's tensors.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     try:
         L = ctypes.CDLL(lib_path)
     except OSError as e:

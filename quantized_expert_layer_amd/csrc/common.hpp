@@ -122,9 +122,11 @@ __device__ __forceinline__ bool find_m_tile(const int32_t* __restrict__ offsets,
             const int src = __builtin_ctzll(hit);
             const int my_row0 = lo + (mt - base - excl) * BM;
             const int my_rows = min(BM, hi - my_row0);
-            e_out = __shfl(e, src, kWave);
-            row0 = __shfl(my_row0, src, kWave);
-            rows = __shfl(my_rows, src, kWave);
+            // readfirstlane: the results are wave-uniform, keep them in scalar registers so
+            // that branches on them are scalar branches rather than exec-mask regions
+            e_out = __builtin_amdgcn_readfirstlane(__shfl(e, src, kWave));
+            row0 = __builtin_amdgcn_readfirstlane(__shfl(my_row0, src, kWave));
+            rows = __builtin_amdgcn_readfirstlane(__shfl(my_rows, src, kWave));
             return true;
         }
         base += __shfl(incl, kWave - 1, kWave);

@@ -97,46 +97,49 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p, int nbo,
 
     u32x4 braw[PF][NCB];
     f16x8 araw[PF][KSTEPS];
-    uint16_t sraw[PF][NCB] = {};
+    uint32_t sraw[PF][NCB] = {};           // fp16 scale bits, zero-extended
 
     auto issue = [&](int slot, int kb) {
         const int kl = min(kb, kb1 - 1);        // clamped: tail loads repeat the last block
 #pragma unroll
         for (int c = 0; c < NCB; ++c) {
             braw[slot][c] = load_weights16(wp[c] + (size_t)kl * kWave);
-            if constexpr (GROUPED) sraw[slot][c] = sp[(size_t)((kl * KSB) >> 7) * N + ncol[c]];
+            if constexpr (GROUPED) sraw[slot][c] = (uint32_t)sp[(size_t)((kl * KSB) >> 7) * N + ncol[c]];
         }
 #pragma unroll
         for (int j = 0; j < KSTEPS; ++j) araw[slot][j] = ap[(kl * KSB + j * 32) / 8];
     };
 
+    auto compute = [&](const u32x4 (&bq)[NCB], const uint32_t (&sq)[NCB],
+                       const f16x8 (&aq)[KSTEPS]) {
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) {
+            const f16 sv = __builtin_bit_cast(f16, (uint16_t)sq[c]);
+            const f16x2 s2 = {sv, sv};
+#pragma unroll
+            for (int j = 0; j < KSTEPS; ++j)
+                acc[c] = mfma16x16x32(aq[j], weight_frag<WT, GROUPED>(bq[c], j, s2), acc[c]);
+        }
+    };
+
     if (kb0 < kb1) {
+        // ring of PF register slots: slot u holds super-block kc + u of the current group
 #pragma unroll
         for (int u = 0; u < PF; ++u) issue(u, kb0 + u);
-        for (int kb = kb0; kb < kb1; kb += PF) {
+        int kc = kb0;
+        // steady state, branch-free: compute from slot u in place, then refill slot u with the
+        // block PF ahead (no register copies of in-flight loads, so no early waits)
+        for (; kc + PF <= kb1; kc += PF) {
 #pragma unroll
             for (int u = 0; u < PF; ++u) {
-                const int kc = kb + u;
-                u32x4 bcur[NCB];
-                uint16_t scur[NCB];
-#pragma unroll
-                for (int c = 0; c < NCB; ++c) { bcur[c] = braw[u][c]; scur[c] = sraw[u][c]; }
-                f16x8 acur[KSTEPS];
-#pragma unroll
-                for (int j = 0; j < KSTEPS; ++j) acur[j] = araw[u][j];
-                issue(u, kc + PF);
-                if (kc < kb1) {
-#pragma unroll
-                    for (int c = 0; c < NCB; ++c) {
-                        const f16 sv = __builtin_bit_cast(f16, scur[c]);
-                        const f16x2 s2 = {sv, sv};
-#pragma unroll
-                        for (int j = 0; j < KSTEPS; ++j)
-                            acc[c] = mfma16x16x32(acur[j], weight_frag<WT, GROUPED>(bcur[c], j, s2), acc[c]);
-                    }
-                }
+                compute(braw[u], sraw[u], araw[u]);
+                issue(u, kc + u + PF);
             }
         }
+        // tail: fewer than PF blocks left, already in their slots
+#pragma unroll
+        for (int u = 0; u < PF; ++u)
+            if (kc + u < kb1) compute(braw[u], sraw[u], araw[u]);
     }
 
     // per-channel scales on the fp32 sums
@@ -206,190 +209,201 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
 
 // ------------------------------------------------------------------------------------
 // Tile path.
-//   block tile  = 128 rows x 256 weight columns (4 waves x 4 column blocks of 16)
-//                 SwiGLU: 4 waves x (2 gate + 2 up blocks) = 128 output columns
-//   K stage     = 128 rows of K; A stage = 128 x 128 fp16 in LDS (row pitch 136 halves so
-//                 that the 16 lanes of a ds_read_b128 group hit distinct banks)
+//   block tile  = 16*MS rows x (4 waves x NS column blocks of 16); a wave owns its NS weight
+//                 column blocks for all the tile's rows, so each weight byte of the tile is
+//                 loaded and expanded by one wave only.  SwiGLU: NS/2 gate blocks + the
+//                 matching NS/2 up blocks.
+//   K stage     = 128 rows of K (64 for fp16 weights).  The A stage (rows x KC fp16) is
+//                 loaded to registers one stage ahead and written to LDS (double buffered).
+//                 LDS rows are not padded: 16-byte chunk c of row r sits at chunk position
+//                 c ^ (r & 15), so the 16 lanes of an A-fragment read (16 rows, one chunk)
+//                 and of a row write hit distinct 4-bank groups.
+//   partial     = a tile with fewer valid rows runs the body specialised for its number of
+//                 16-row subtiles (1..MS), so it neither loads nor multiplies absent rows.
+//   occupancy   = 2+ blocks per CU, so each SIMD interleaves at least two waves.
 // ------------------------------------------------------------------------------------
-constexpr int kTileBM = 128;
-constexpr int kTileMS = 8;           // 16-row subtiles per wave
-constexpr int kTileNS = 4;           // 16-column weight blocks per wave
-// K per stage: one 128-group for the integer codes, 64 rows for fp16 weights (whose
-// register double buffer is 4x larger per row).
 template <int WT> constexpr int tile_kc() { return WT == MOE_W_FP16 ? 64 : 128; }
-constexpr int kTileLdsMax = kTileBM * (128 + 8);   // halves per LDS buffer
 
-template <int WT, int ACT, bool GROUPED>
-__global__ __launch_bounds__(256, 1) void gemm_tile_kernel(GemmParams p, int ncbg, int mt_ub,
-                                                           int grid_real) {
+template <int WT, int ACT, bool GROUPED, int MA, int NS, int BM>
+__device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__ lds, int e,
+                                          int row0, int rows, int cbg) {
     constexpr int KSB = WTraits<WT>::KSB;
-    constexpr int kTileKC = tile_kc<WT>();
-    constexpr int kTileLdsPitch = kTileKC + 8;       // halves; 16 lanes of a b128 read hit
-                                                     // distinct banks
-    constexpr int SBPS = kTileKC / KSB;              // super-blocks per stage per column block
-    constexpr int CPR = kTileKC / 8;                 // 16-byte chunks per A row per stage
-    constexpr int ACH = kTileBM * CPR / 256;         // A chunks per thread per stage
+    constexpr int KC = tile_kc<WT>();
+    constexpr int KSTEPS = KC / 32;                  // MFMA K-steps per stage
+    constexpr int KSPS = KSB / 32;                   // K-steps per super-block
+    constexpr int SBPS = KC / KSB;                   // super-blocks per stage per column block
+    constexpr int CPR = KC / 8;                      // 16-byte chunks per LDS row
+    constexpr int ATOT = MA * 16 * CPR;              // A chunks per stage
+    constexpr int ACH = (ATOT + 255) / 256;          // A chunks per thread per stage
+    constexpr int LDS_BUF = BM * KC;                 // halves per buffer
     constexpr bool SWI = (ACT == MOE_ACT_SWIGLU);
-    __shared__ __attribute__((aligned(16))) f16 lds[2][kTileLdsMax];
+    constexpr int NO = SWI ? NS / 2 : NS;            // output column blocks per wave
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    const int K = p.K, N = p.N;
+    const int nSB = K / KSB;
+    const int ncbw = N / 16;
+    const int nbo = SWI ? ncbw / 2 : ncbw;
 
-    // XCD-aware order: hardware block b runs on XCD b % 8; give each XCD a contiguous
-    // range of logical tiles so that the m-tiles sharing a weight block share an L2.
+    int ob[NO];
+    bool ob_ok[NO];
+#pragma unroll
+    for (int c = 0; c < NO; ++c) {
+        const int o = (cbg * 4 + wave) * NO + c;
+        ob_ok[c] = o < nbo;
+        ob[c] = ob_ok[c] ? o : 0;
+    }
+    const u32x4* wp[NS];
+    int ncol[NS];
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+        const int cbw = SWI ? ob[c % NO] + (c / NO) * nbo : ob[c];
+        wp[c] = (const u32x4*)p.w + ((size_t)(e * ncbw + cbw) * nSB) * kWave + lane;
+        ncol[c] = cbw * 16 + (lane & 15);
+    }
+    const int G = GROUPED ? K / 128 : 1;
+    const uint16_t* sp = p.scales + (size_t)e * G * N;
+
+    // A staging addresses: chunk q = threadIdx.x + 256 i -> row q / CPR, chunk q % CPR
+    const u32x4* asrc[ACH];
+    int adst[ACH];
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+        const int q = min((int)threadIdx.x + 256 * i, ATOT - 1);
+        const int r = q / CPR, c = q % CPR;
+        asrc[i] = (const u32x4*)(p.a + (size_t)(row0 + min(r, rows - 1)) * K) + c;
+        adst[i] = r * KC + ((c ^ (r & (CPR - 1))) * 8);
+    }
+    u32x4 areg[ACH];
+    auto load_a = [&](int st) {
+#pragma unroll
+        for (int i = 0; i < ACH; ++i)
+            if (ATOT % 256 == 0 || (int)threadIdx.x + 256 * i < ATOT) areg[i] = asrc[i][st * CPR];
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < ACH; ++i)
+            if (ATOT % 256 == 0 || (int)threadIdx.x + 256 * i < ATOT)
+                *(u32x4*)(lds + buf * LDS_BUF + adst[i]) = areg[i];
+    };
+
+    u32x4 bcur[NS][SBPS], bnext[NS][SBPS];
+    uint16_t scur[NS] = {}, snext[NS] = {};
+    auto load_b = [&](u32x4 (&b)[NS][SBPS], uint16_t (&sc)[NS], int st) {
+#pragma unroll
+        for (int c = 0; c < NS; ++c) {
+#pragma unroll
+            for (int q = 0; q < SBPS; ++q) b[c][q] = wp[c][(size_t)(st * SBPS + q) * kWave];
+            if constexpr (GROUPED) sc[c] = sp[(size_t)((st * KC) >> 7) * N + ncol[c]];
+        }
+    };
+
+    f32x4 acc[MA][NS];
+#pragma unroll
+    for (int m = 0; m < MA; ++m)
+#pragma unroll
+        for (int c = 0; c < NS; ++c) acc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nstage = K / KC;
+    load_a(0);
+    load_b(bcur, scur, 0);
+    store_a(0);
+    __syncthreads();
+
+    // The loop body is branch-free: the last stage prefetches (and stores to the idle LDS
+    // buffer) a copy of itself, so the compiler can count outstanding loads exactly and keep
+    // the next stage's loads in flight across the whole compute of this one.
+    const int lrow = lane & 15;
+    for (int st = 0; st < nstage; ++st) {
+        const int nxt = min(st + 1, nstage - 1);
+        load_a(nxt);
+        load_b(bnext, snext, nxt);
+        // keep the prefetch at the top: the scheduler would otherwise sink the loads next to
+        // their first use at the end of the stage and expose their full latency
+        __builtin_amdgcn_sched_barrier(0);
+        const f16* abuf = lds + (st & 1) * LDS_BUF;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            f16x8 bq[NS];
+#pragma unroll
+            for (int c = 0; c < NS; ++c) {
+                const f16 sv = __builtin_bit_cast(f16, scur[c]);
+                const f16x2 s2 = {sv, sv};
+                bq[c] = weight_frag<WT, GROUPED>(bcur[c][ks / KSPS], ks % KSPS, s2);
+            }
+            const int pos = (ks * 4 + (lane >> 4)) ^ (lrow & (CPR - 1));
+            f16x8 af[MA];
+#pragma unroll
+            for (int m = 0; m < MA; ++m) af[m] = *(const f16x8*)(abuf + (m * 16 + lrow) * KC + pos * 8);
+#pragma unroll
+            for (int m = 0; m < MA; ++m)
+#pragma unroll
+                for (int c = 0; c < NS; ++c) acc[m][c] = mfma16x16x32(af[m], bq[c], acc[m][c]);
+        }
+        store_a((st + 1) & 1);
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < NS; ++c) {
+#pragma unroll
+            for (int q = 0; q < SBPS; ++q) bcur[c][q] = bnext[c][q];
+            scur[c] = snext[c];
+        }
+    }
+
+    // epilogue
+    if constexpr (!GROUPED && WT != MOE_W_FP16) {
+#pragma unroll
+        for (int c = 0; c < NS; ++c) {
+            const float sc = f16_bits_to_f32(sp[ncol[c]]);
+#pragma unroll
+            for (int m = 0; m < MA; ++m) acc[m][c] *= sc;
+        }
+    }
+    const int n_out = SWI ? N / 2 : N;
+    const int rbase = 4 * (lane >> 4);
+#pragma unroll
+    for (int m = 0; m < MA; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = m * 16 + rbase + i;
+            if (r >= rows) continue;
+            const float rs = p.row_scale ? p.row_scale[row0 + r] : 1.0f;
+            uint16_t* orow = p.out + (size_t)(row0 + r) * n_out + (lane & 15);
+#pragma unroll
+            for (int c = 0; c < NO; ++c) {
+                if (!ob_ok[c]) continue;
+                float v;
+                if constexpr (SWI) v = silu(acc[m][c][i]) * acc[m][c + NO][i];
+                else if constexpr (ACT == MOE_ACT_RELU) v = fmaxf(acc[m][c][i], 0.0f);
+                else v = acc[m][c][i];
+                orow[ob[c] * 16] = f32_to_f16_bits(v * rs);
+            }
+        }
+    }
+}
+
+template <int WT, int ACT, bool GROUPED, int MS, int NS>
+__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmParams p, int ncbg, int mt_ub,
+                                                           int grid_real) {
+    constexpr int BM = 16 * MS;
+    __shared__ __attribute__((aligned(16))) f16 lds[2 * BM * tile_kc<WT>()];
+
+    // XCD-aware order: hardware block b runs on XCD b % 8; each XCD gets a contiguous range
+    // of logical tiles, so the m-tiles that share a weight block share an L2.
     const int G8 = gridDim.x / 8;
     const int L = (blockIdx.x % 8) * G8 + blockIdx.x / 8;
     if (L >= grid_real) return;
     const int mt = L % mt_ub;
     const int cbg = L / mt_ub;
     int e, row0, rows;
-    if (!find_m_tile<kTileBM>(p.offsets, p.E, p.R, mt, e, row0, rows)) return;
-
-    const int K = p.K, N = p.N;
-    const int nSB = K / KSB;
-    const int ncbw = N / 16;
-    const int nbo = SWI ? ncbw / 2 : ncbw;           // output column blocks
-
-    // this wave's weight column blocks
-    int cbw[kTileNS];
-    bool cb_ok[kTileNS];
-#pragma unroll
-    for (int c = 0; c < kTileNS; ++c) {
-        int ob;
-        if constexpr (SWI) ob = cbg * 8 + wave * 2 + (c & 1);
-        else ob = cbg * 16 + wave * 4 + c;
-        cb_ok[c] = ob < nbo;
-        const int obc = cb_ok[c] ? ob : 0;
-        cbw[c] = SWI ? obc + (c >> 1) * nbo : obc;
-    }
-    const u32x4* wp[kTileNS];
-    int ncol[kTileNS];
-#pragma unroll
-    for (int c = 0; c < kTileNS; ++c) {
-        wp[c] = (const u32x4*)p.w + ((size_t)(e * ncbw + cbw[c]) * nSB) * kWave + lane;
-        ncol[c] = cbw[c] * 16 + (lane & 15);
-    }
-    const int G = GROUPED ? K / 128 : 1;         // groups of 128 rows along K
-    const uint16_t* sp = p.scales + (size_t)e * G * N;
-
-    // A staging: 128 rows x KC halves in 16-byte chunks, ACH per thread
-    const int nstage = K / kTileKC;
-    u32x4 areg[ACH];
-    auto load_a = [&](int st) {
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            const int cidx = threadIdx.x + 256 * i;
-            const int r = cidx / CPR, c8 = cidx % CPR;
-            const int rr = row0 + min(r, rows - 1);
-            areg[i] = *(const u32x4*)(p.a + (size_t)rr * K + st * kTileKC + c8 * 8);
-        }
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            const int cidx = threadIdx.x + 256 * i;
-            const int r = cidx / CPR, c8 = cidx % CPR;
-            *(u32x4*)(&lds[buf][r * kTileLdsPitch + c8 * 8]) = areg[i];
-        }
-    };
-
-    u32x4 breg[2][kTileNS][SBPS];
-    uint16_t sreg[2][kTileNS] = {};
-    auto load_b = [&](int slot, int st) {
-#pragma unroll
-        for (int c = 0; c < kTileNS; ++c) {
-#pragma unroll
-            for (int q = 0; q < SBPS; ++q)
-                breg[slot][c][q] = load_weights16(wp[c] + (size_t)(st * SBPS + q) * kWave);
-            if constexpr (GROUPED) sreg[slot][c] = sp[(size_t)((st * kTileKC) >> 7) * N + ncol[c]];
-        }
-    };
-
-    f32x4 acc[kTileMS][kTileNS];
-#pragma unroll
-    for (int m = 0; m < kTileMS; ++m)
-#pragma unroll
-        for (int c = 0; c < kTileNS; ++c) acc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    load_a(0);
-    load_b(0, 0);
-    store_a(0);
-    __syncthreads();
-
-    // One stage: compute from LDS buffer / register slot CUR while stage st+1 is fetched.
-    // CUR is a compile-time constant so that the register double buffer stays in VGPRs.
-    auto stage = [&](auto cur_tag, int st) {
-        constexpr int cur = decltype(cur_tag)::value;
-        const bool more = st + 1 < nstage;
-        if (more) {
-            load_a(st + 1);
-            load_b(cur ^ 1, st + 1);
-        }
-        const f16* abuf = lds[cur];
-#pragma unroll
-        for (int ks = 0; ks < kTileKC / 32; ++ks) {
-            f16x8 bq[kTileNS];
-#pragma unroll
-            for (int c = 0; c < kTileNS; ++c) {
-                const f16 sv = __builtin_bit_cast(f16, sreg[cur][c]);
-                const f16x2 s2 = {sv, sv};
-                constexpr int KSPS = KSB / 32;       // K-steps per super-block
-                bq[c] = weight_frag<WT, GROUPED>(breg[cur][c][ks / KSPS], ks % KSPS, s2);
-            }
-#pragma unroll
-            for (int m = 0; m < kTileMS; ++m) {
-                const f16x8 af = *(const f16x8*)(abuf + (m * 16 + (lane & 15)) * kTileLdsPitch +
-                                                 ks * 32 + 8 * (lane >> 4));
-#pragma unroll
-                for (int c = 0; c < kTileNS; ++c) acc[m][c] = mfma16x16x32(af, bq[c], acc[m][c]);
-            }
-        }
-        if (more) {
-            store_a(cur ^ 1);
-            __syncthreads();
-        }
-    };
-    for (int st = 0; st < nstage; st += 2) {
-        stage(std::integral_constant<int, 0>{}, st);
-        if (st + 1 < nstage) stage(std::integral_constant<int, 1>{}, st + 1);
-    }
-
-    // epilogue
-    if constexpr (!GROUPED && WT != MOE_W_FP16) {
-#pragma unroll
-        for (int c = 0; c < kTileNS; ++c) {
-            const float sc = f16_bits_to_f32(sp[ncol[c]]);
-#pragma unroll
-            for (int m = 0; m < kTileMS; ++m) acc[m][c] *= sc;
-        }
-    }
-    const int n_out = SWI ? N / 2 : N;
-    const int rbase = 4 * (lane >> 4);
-#pragma unroll
-    for (int m = 0; m < kTileMS; ++m) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = m * 16 + rbase + i;
-            if (r >= rows) continue;
-            const float rs = p.row_scale ? p.row_scale[row0 + r] : 1.0f;
-            uint16_t* orow = p.out + (size_t)(row0 + r) * n_out;
-            if constexpr (SWI) {
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    if (!cb_ok[c]) continue;
-                    const float v = silu(acc[m][c][i]) * acc[m][c + 2][i] * rs;
-                    orow[cbw[c] * 16 + (lane & 15)] = f32_to_f16_bits(v);
-                }
-            } else {
-#pragma unroll
-                for (int c = 0; c < kTileNS; ++c) {
-                    if (!cb_ok[c]) continue;
-                    float v = acc[m][c][i];
-                    if constexpr (ACT == MOE_ACT_RELU) v = fmaxf(v, 0.0f);
-                    orow[ncol[c]] = f32_to_f16_bits(v * rs);
-                }
-            }
-        }
+    if (!find_m_tile<BM>(p.offsets, p.E, p.R, mt, e, row0, rows)) return;
+    static_assert(MS == 4, "bodies below are instantiated for up to 4 subtiles");
+    switch ((rows + 15) / 16) {
+        case 1: tile_body<WT, ACT, GROUPED, 1, NS, BM>(p, lds, e, row0, rows, cbg); break;
+        case 2: tile_body<WT, ACT, GROUPED, 2, NS, BM>(p, lds, e, row0, rows, cbg); break;
+        case 3: tile_body<WT, ACT, GROUPED, 3, NS, BM>(p, lds, e, row0, rows, cbg); break;
+        default: tile_body<WT, ACT, GROUPED, 4, NS, BM>(p, lds, e, row0, rows, cbg); break;
     }
 }
 
@@ -404,7 +418,7 @@ int gemm_choose_path(int R, int E, int K, int N, int wtype, int act, int forced)
     // average rows per (possibly) active expert
     const int active = R < E ? R : E;
     const double rows_per_expert = active > 0 ? (double)R / active : 0.0;
-    return rows_per_expert >= 48.0 ? MOE_PATH_TILE : MOE_PATH_STREAM;
+    return rows_per_expert >= 16.0 ? MOE_PATH_TILE : MOE_PATH_STREAM;
 }
 
 int gemm_choose_split(int R, int E, int K, int N, int wtype, int act, int forced) {
@@ -444,14 +458,24 @@ static hipError_t stream_dispatch(const GemmParams& p, hipStream_t stream) {
 
 template <int WT, int ACT, bool GROUPED>
 static hipError_t tile_dispatch(const GemmParams& p, hipStream_t stream) {
+    constexpr int MS = 4, BM = 16 * MS;
     const int ncbw = p.N / 16;
-    const int ncbg = (ACT == MOE_ACT_SWIGLU) ? cdiv(ncbw / 2, 8) : cdiv(ncbw, 16);
+    const int nbo = (ACT == MOE_ACT_SWIGLU) ? ncbw / 2 : ncbw;
     const int active = p.R < p.E ? p.R : p.E;
-    const int mt_ub = cdiv(p.R, kTileBM) + active;
+    const int mt_ub = cdiv(p.R, BM) + active;
+    // 4 column blocks per wave when that still gives >= 4 blocks per CU, else 2
+    const int out_per_wave4 = (ACT == MOE_ACT_SWIGLU) ? 2 : 4;
+    const long blocks4 = (long)cdiv(nbo, 4 * out_per_wave4) * (cdiv(p.R, BM) + active / 2);
+    const bool wide = blocks4 >= 4L * 256;
+    const int out_per_wave = wide ? out_per_wave4 : out_per_wave4 / 2;
+    const int ncbg = cdiv(nbo, 4 * out_per_wave);
     const long real = (long)mt_ub * ncbg;
     const long grid = (real + 7) / 8 * 8;
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
-    gemm_tile_kernel<WT, ACT, GROUPED><<<(unsigned)grid, 256, 0, stream>>>(p, ncbg, mt_ub, (int)real);
+    if (wide)
+        gemm_tile_kernel<WT, ACT, GROUPED, MS, 4><<<(unsigned)grid, 256, 0, stream>>>(p, ncbg, mt_ub, (int)real);
+    else
+        gemm_tile_kernel<WT, ACT, GROUPED, MS, 2><<<(unsigned)grid, 256, 0, stream>>>(p, ncbg, mt_ub, (int)real);
     return hipGetLastError();
 }
 
