@@ -53,6 +53,8 @@ def parse():
                     help="cycle weight copies totalling at least this many GB (cold weights)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the same steps replayed from captured HIP graphs")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one device copy of this size before timing (counter calibration)")
     return ap.parse_args()
@@ -179,6 +181,41 @@ def main():
             traffic = None
     roof["traffic"] = traffic
 
+    graph_info = None
+    if args.graph:
+        # one graph per weight copy, captured on a side stream; replays are checked against
+        # the eager output of the same weights before they are timed
+        gs = torch.cuda.Stream()
+        gplans = [layer.plan(ws, x, logits, weights=c, stream=gs) for c in copies]
+        graphs = []
+        ref_out = None
+        for gp in gplans:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=gs):
+                gp.run()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        plans[0].run()
+        torch.cuda.synchronize()
+        ref_out = ws.bufs["out"].clone()
+        for _ in range(3):
+            graphs[0].replay()
+            torch.cuda.synchronize()
+            if not torch.equal(ws.bufs["out"], ref_out):
+                raise RuntimeError("graph replay differs from the eager layer output")
+            plans[1 % n_copies].run()
+            torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % n_copies].replay()
+        torch.cuda.synchronize()
+        tg0 = time.perf_counter()
+        for i in range(K):
+            graphs[i % n_copies].replay()
+        torch.cuda.synchronize()
+        tg1 = time.perf_counter()
+        g_ms = (tg1 - tg0) * 1e3 / K
+        graph_info = {"ms_per_step": g_ms, "tokens_per_s": T / (g_ms * 1e-3)}
+
     layer_s = ms_per_step * 1e-3
     weight_bytes = g1["bytes"] + g2["bytes"]
     flops = g1["flops"] + g2["flops"]
@@ -207,6 +244,8 @@ def main():
                   "mfma_frac": flops / layer_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
                   "stage_us": stage_us, "kernel_source_hash": src_hash},
     }
+    if graph_info is not None:
+        result["graph_replay"] = graph_info
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)
     print(json.dumps(result), flush=True)

@@ -74,9 +74,9 @@ int32_t validate_gemm(const uint16_t* a, const int32_t* offsets, int32_t R, int3
     if (R == 0) return MOE_OK;
     if (!a || !offsets || !w || !out) return MOE_ERR_INVALID;
     if (wtype != MOE_W_FP16 && !scales) return MOE_ERR_INVALID;
-    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(out, 4) || !aligned(offsets, 4))
+    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(out, 16) || !aligned(offsets, 4))
         return MOE_ERR_INVALID;
-    if (scales && !aligned(scales, 2)) return MOE_ERR_INVALID;
+    if (scales && !aligned(scales, 16)) return MOE_ERR_INVALID;
     return MOE_OK;
 }
 

@@ -44,16 +44,37 @@ __device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cas
 // into the mantissa gives the fp16 value 1024 + Y, and one packed fp16 subtraction removes
 // the offset.  INT4 nibbles four bits up the half-word land as 16*u: (1024 + 16u)/16 - 72 =
 // u - 8 with a single packed fma, exact in fp16.
-__device__ __forceinline__ void i2f_int4(uint32_t w, f16x2 out[4]) {
-    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, magic = 0x64006400u;
+// (w & mask) | magic in one v_and_or_b32.  Written out because the compiler otherwise splits
+// it into v_and + v_or (both constants would need the single scalar operand slot of VOP3).
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "v"(mask), "s"(magic));
+    return r;
+}
+
+struct I2F4Consts {
+    uint32_t lo, hi;                 // nibble masks, kept in VGPRs
+    __device__ __forceinline__ I2F4Consts() {
+        asm("v_mov_b32 %0, 0x000F000F" : "=v"(lo));
+        asm("v_mov_b32 %0, 0x00F000F0" : "=v"(hi));
+    }
+};
+
+__device__ __forceinline__ void i2f_int4(uint32_t w, f16x2 out[4], const I2F4Consts& k) {
+    const uint32_t magic = 0x64006400u;
     const uint32_t w8 = w >> 8;
     const f16x2 sub_lo = {(f16)1032.0f, (f16)1032.0f};
     const f16x2 mul_hi = {(f16)0.0625f, (f16)0.0625f};
     const f16x2 sub_hi = {(f16)-72.0f, (f16)-72.0f};
-    out[0] = as_f16x2((w & lo) | magic) - sub_lo;            // [e0, e1]
-    out[1] = as_f16x2((w & hi) | magic) * mul_hi + sub_hi;   // [e2, e3]
-    out[2] = as_f16x2((w8 & lo) | magic) - sub_lo;           // [e4, e5]
-    out[3] = as_f16x2((w8 & hi) | magic) * mul_hi + sub_hi;  // [e6, e7]
+    out[0] = as_f16x2(and_or(w, k.lo, magic)) - sub_lo;             // [e0, e1]
+    out[1] = as_f16x2(and_or(w, k.hi, magic)) * mul_hi + sub_hi;    // [e2, e3]
+    out[2] = as_f16x2(and_or(w8, k.lo, magic)) - sub_lo;            // [e4, e5]
+    out[3] = as_f16x2(and_or(w8, k.hi, magic)) * mul_hi + sub_hi;   // [e6, e7]
+}
+
+__device__ __forceinline__ void i2f_int4(uint32_t w, f16x2 out[4]) {
+    const I2F4Consts k;
+    i2f_int4(w, out, k);
 }
 
 // 8-bit variant: byte u = q + 128 goes into the mantissa of 1024, then 1152 = 1024 + 128

@@ -26,10 +26,11 @@ namespace moe {
 // fp16 weight; per-channel scales are applied to the fp32 result instead.
 // ------------------------------------------------------------------------------------
 template <int WT, bool SCALE>
-__device__ __forceinline__ f16x8 weight_frag(const u32x4& raw, int j, f16x2 s2) {
+__device__ __forceinline__ f16x8 weight_frag(const u32x4& raw, int j, f16x2 s2,
+                                             const I2F4Consts& k4) {
     f16x2 q[4];
     if constexpr (WT == MOE_W_INT4) {
-        i2f_int4(raw[j], q);
+        i2f_int4(raw[j], q, k4);
     } else if constexpr (WT == MOE_W_INT8) {
         i2f_int8(raw[2 * j], q);
         i2f_int8(raw[2 * j + 1], q + 2);
@@ -43,28 +44,47 @@ __device__ __forceinline__ f16x8 weight_frag(const u32x4& raw, int j, f16x2 s2) 
     return pack8(q[0], q[1], q[2], q[3]);
 }
 
+
+// Output fragment layout.  The MFMA is issued with the weight fragment as its first operand
+// and the activation fragment as its second, i.e. it computes Y^T = W^T X^T; lane l then holds
+// row (l & 15) of its 16-row subtile and the 4 consecutive columns 4*(l >> 4) .. +3 of its
+// 16-column block, so results leave in 8-byte stores.
+__device__ __forceinline__ void store4_f16(uint16_t* dst, float a, float b, float c, float d) {
+    f16x2 lo = {(f16)a, (f16)b}, hi = {(f16)c, (f16)d};
+    uint2 v;
+    v.x = __builtin_bit_cast(uint32_t, lo);
+    v.y = __builtin_bit_cast(uint32_t, hi);
+    *(uint2*)dst = v;
+}
+
+__device__ __forceinline__ f32x4 load4_scale(const uint16_t* src) {
+    const uint2 v = *(const uint2*)src;
+    const f16x2 lo = __builtin_bit_cast(f16x2, v.x), hi = __builtin_bit_cast(f16x2, v.y);
+    return f32x4{(float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]};
+}
+
 // ------------------------------------------------------------------------------------
 // Stream path.
-//   grid  = m-tiles(upper bound) x ceil(NBo / 4) x S blocks of 4 waves.
+//   grid  = m-tiles(upper bound) x NBo x S one-wave blocks (small blocks balance the few
+//           hundred to few thousand streams of a decode step evenly over the CUs).
 //   wave  = one 16-column output block; for SwiGLU it streams the gate block and the up
 //           block (columns I + ...) of the same 16 outputs.
 // ------------------------------------------------------------------------------------
 template <int WT, int ACT, bool GROUPED, bool SPLIT, int PF>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p, int nbo, int ncbg) {
+__global__ __launch_bounds__(64) void gemm_stream_kernel(GemmParams p, int nbo) {
     constexpr int KSB = WTraits<WT>::KSB;
     constexpr int KSTEPS = KSB / 32;
     constexpr int NCB = (ACT == MOE_ACT_SWIGLU) ? 2 : 1;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
     const int S = p.split;
 
+    // one wave per block: (m-tile, output column block, K slice), m-tile slowest so that the
+    // blocks of existing tiles come first and the surplus of the upper-bound grid exits last
     int b = blockIdx.x;
     const int s = b % S;
     b /= S;
-    const int cbg = b % ncbg;
-    const int mt = b / ncbg;
-    const int cbo = cbg * 4 + wave;
-    if (cbo >= nbo) return;
+    const int cbo = b % nbo;
+    const int mt = b / nbo;
     int e, row0, rows;
     if (!find_m_tile<16>(p.offsets, p.E, p.R, mt, e, row0, rows)) return;
 
@@ -110,6 +130,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p, int nbo,
         for (int j = 0; j < KSTEPS; ++j) araw[slot][j] = ap[(kl * KSB + j * 32) / 8];
     };
 
+    const I2F4Consts k4;
     auto compute = [&](const u32x4 (&bq)[NCB], const uint32_t (&sq)[NCB],
                        const f16x8 (&aq)[KSTEPS]) {
 #pragma unroll
@@ -118,7 +139,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p, int nbo,
             const f16x2 s2 = {sv, sv};
 #pragma unroll
             for (int j = 0; j < KSTEPS; ++j)
-                acc[c] = mfma16x16x32(aq[j], weight_frag<WT, GROUPED>(bq[c], j, s2), acc[c]);
+                acc[c] = mfma16x16x32(weight_frag<WT, GROUPED>(bq[c], j, s2, k4), aq[j], acc[c]);
         }
     };
 
@@ -142,41 +163,32 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmParams p, int nbo,
             if (kc + u < kb1) compute(braw[u], sraw[u], araw[u]);
     }
 
-    // per-channel scales on the fp32 sums
+    // per-channel scales on the fp32 sums (4 consecutive output columns per lane)
+    const int q4 = 4 * (lane >> 4);
     if constexpr (!GROUPED && WT != MOE_W_FP16) {
 #pragma unroll
-        for (int c = 0; c < NCB; ++c) {
-            const float sc = f16_bits_to_f32(sp[ncol[c]]);
-            acc[c] *= sc;
-        }
+        for (int c = 0; c < NCB; ++c) acc[c] *= load4_scale(sp + (cbo + c * nbo) * 16 + q4);
     }
 
-    const int rbase = 4 * (lane >> 4);
-    if constexpr (SPLIT) {
-        // fp32 partial sums of this K slice: partial[s][row][n]
+    const int r = lane & 15;                 // row of this lane within the tile
+    if (r < rows) {
+        if constexpr (SPLIT) {
+            // fp32 partial sums of this K slice: partial[s][row][n], 16 bytes per lane
+            float* dst = p.partial + ((size_t)s * p.R + row0 + r) * N;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rbase + i;
-            if (r < rows) {
-                float* dst = p.partial + ((size_t)s * p.R + row0 + r) * N;
+            for (int c = 0; c < NCB; ++c) *(f32x4*)(dst + (cbo + c * nbo) * 16 + q4) = acc[c];
+        } else {
+            const int n_out = (ACT == MOE_ACT_SWIGLU) ? N / 2 : N;
+            const float rs = p.row_scale ? p.row_scale[row0 + r] : 1.0f;
+            float v[4];
 #pragma unroll
-                for (int c = 0; c < NCB; ++c) dst[ncol[c]] = acc[c][i];
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (ACT == MOE_ACT_SWIGLU) v[i] = silu(acc[0][i]) * acc[1][i];
+                else if constexpr (ACT == MOE_ACT_RELU) v[i] = fmaxf(acc[0][i], 0.0f);
+                else v[i] = acc[0][i];
+                v[i] *= rs;
             }
-        }
-    } else {
-        const int n_out = (ACT == MOE_ACT_SWIGLU) ? N / 2 : N;
-        const int col = cbo * 16 + (lane & 15);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rbase + i;
-            if (r < rows) {
-                float v;
-                if constexpr (ACT == MOE_ACT_SWIGLU) v = silu(acc[0][i]) * acc[1][i];
-                else if constexpr (ACT == MOE_ACT_RELU) v = fmaxf(acc[0][i], 0.0f);
-                else v = acc[0][i];
-                if (p.row_scale) v *= p.row_scale[row0 + r];
-                p.out[(size_t)(row0 + r) * n_out + col] = f32_to_f16_bits(v);
-            }
+            store4_f16(p.out + (size_t)(row0 + r) * n_out + cbo * 16 + q4, v[0], v[1], v[2], v[3]);
         }
     }
 }
@@ -299,6 +311,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         }
     };
 
+    const I2F4Consts k4;
     f32x4 acc[MA][NS];
 #pragma unroll
     for (int m = 0; m < MA; ++m)
@@ -323,23 +336,33 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         // their first use at the end of the stage and expose their full latency
         __builtin_amdgcn_sched_barrier(0);
         const f16* abuf = lds + (st & 1) * LDS_BUF;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            f16x8 bq[NS];
+        // the weight fragments of K-step ks+1 are expanded while the MFMAs of ks issue
+        auto expand = [&](f16x8 (&bq)[NS], int ks) {
 #pragma unroll
             for (int c = 0; c < NS; ++c) {
                 const f16 sv = __builtin_bit_cast(f16, scur[c]);
                 const f16x2 s2 = {sv, sv};
-                bq[c] = weight_frag<WT, GROUPED>(bcur[c][ks / KSPS], ks % KSPS, s2);
+                bq[c] = weight_frag<WT, GROUPED>(bcur[c][ks / KSPS], ks % KSPS, s2, k4);
             }
+        };
+        f16x8 bq[NS];
+        expand(bq, 0);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
             const int pos = (ks * 4 + (lane >> 4)) ^ (lrow & (CPR - 1));
             f16x8 af[MA];
 #pragma unroll
             for (int m = 0; m < MA; ++m) af[m] = *(const f16x8*)(abuf + (m * 16 + lrow) * KC + pos * 8);
+            f16x8 bn[NS];
+            if (ks + 1 < KSTEPS) expand(bn, ks + 1);
 #pragma unroll
             for (int m = 0; m < MA; ++m)
 #pragma unroll
-                for (int c = 0; c < NS; ++c) acc[m][c] = mfma16x16x32(af[m], bq[c], acc[m][c]);
+                for (int c = 0; c < NS; ++c) acc[m][c] = mfma16x16x32(bq[c], af[m], acc[m][c]);
+            if (ks + 1 < KSTEPS) {
+#pragma unroll
+                for (int c = 0; c < NS; ++c) bq[c] = bn[c];
+            }
         }
         store_a((st + 1) & 1);
         __syncthreads();
@@ -351,34 +374,36 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         }
     }
 
-    // epilogue
+    // epilogue: lane holds row (lane & 15) of each subtile, 4 consecutive columns per block
+    const int q4 = 4 * (lane >> 4);
     if constexpr (!GROUPED && WT != MOE_W_FP16) {
 #pragma unroll
         for (int c = 0; c < NS; ++c) {
-            const float sc = f16_bits_to_f32(sp[ncol[c]]);
+            const int cbw = SWI ? ob[c % NO] + (c / NO) * nbo : ob[c];
+            const f32x4 sc = load4_scale(sp + cbw * 16 + q4);
 #pragma unroll
             for (int m = 0; m < MA; ++m) acc[m][c] *= sc;
         }
     }
     const int n_out = SWI ? N / 2 : N;
-    const int rbase = 4 * (lane >> 4);
 #pragma unroll
     for (int m = 0; m < MA; ++m) {
+        const int r = m * 16 + lrow;
+        if (r >= rows) continue;
+        const float rs = p.row_scale ? p.row_scale[row0 + r] : 1.0f;
+        uint16_t* orow = p.out + (size_t)(row0 + r) * n_out + q4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = m * 16 + rbase + i;
-            if (r >= rows) continue;
-            const float rs = p.row_scale ? p.row_scale[row0 + r] : 1.0f;
-            uint16_t* orow = p.out + (size_t)(row0 + r) * n_out + (lane & 15);
+        for (int c = 0; c < NO; ++c) {
+            if (!ob_ok[c]) continue;
+            float v[4];
 #pragma unroll
-            for (int c = 0; c < NO; ++c) {
-                if (!ob_ok[c]) continue;
-                float v;
-                if constexpr (SWI) v = silu(acc[m][c][i]) * acc[m][c + NO][i];
-                else if constexpr (ACT == MOE_ACT_RELU) v = fmaxf(acc[m][c][i], 0.0f);
-                else v = acc[m][c][i];
-                orow[ob[c] * 16] = f32_to_f16_bits(v * rs);
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (SWI) v[i] = silu(acc[m][c][i]) * acc[m][c + NO][i];
+                else if constexpr (ACT == MOE_ACT_RELU) v[i] = fmaxf(acc[m][c][i], 0.0f);
+                else v[i] = acc[m][c][i];
+                v[i] *= rs;
             }
+            store4_f16(orow + ob[c] * 16, v[0], v[1], v[2], v[3]);
         }
     }
 }
@@ -428,30 +453,37 @@ int gemm_choose_split(int R, int E, int K, int N, int wtype, int act, int forced
     const int active = R < E ? R : E;
     const int nbo = (act == MOE_ACT_SWIGLU) ? N / 32 : N / 16;
     const long waves = (long)active * cdiv(R, active > 0 ? active * 16 : 16) * nbo;
-    // aim for >= 4096 streaming waves (16 per CU); keep >= 8 super-blocks per slice
+    // split only when there would be fewer than 2 streaming waves per CU: the fixed-order
+    // reduction is a second launch, which costs more than a moderately long stream
     int s = 1;
-    while (s < MOE_MAX_SPLIT_K && waves * s < 4096 && nSB / (2 * s) >= 8) s *= 2;
+    while (s < MOE_MAX_SPLIT_K && waves * s < 512 && nSB / (2 * s) >= 8) s *= 2;
     return s;
 }
 
 template <int WT, int ACT, bool GROUPED>
 static hipError_t stream_dispatch(const GemmParams& p, hipStream_t stream) {
     const int nbo = (ACT == MOE_ACT_SWIGLU) ? p.N / 32 : p.N / 16;
-    const int ncbg = cdiv(nbo, 4);
     const int active = p.R < p.E ? p.R : p.E;
     const int mt_ub = cdiv(p.R, 16) + active;
-    const long blocks = (long)mt_ub * ncbg * p.split;
+    const long blocks = (long)mt_ub * nbo * p.split;
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-    constexpr int PF = (WT == MOE_W_FP16) ? 4 : 4;
+    // few rows (a decode step): few streams, so each keeps 8 super-blocks in flight;
+    // otherwise 4, which leaves registers for more resident waves
+    const bool deep = p.R <= 128;
     if (p.split > 1) {
-        gemm_stream_kernel<WT, ACT, GROUPED, true, PF><<<(unsigned)blocks, 256, 0, stream>>>(p, nbo, ncbg);
+        if (deep)
+            gemm_stream_kernel<WT, ACT, GROUPED, true, 8><<<(unsigned)blocks, 64, 0, stream>>>(p, nbo);
+        else
+            gemm_stream_kernel<WT, ACT, GROUPED, true, 4><<<(unsigned)blocks, 64, 0, stream>>>(p, nbo);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         const int n_out = (ACT == MOE_ACT_SWIGLU) ? p.N / 2 : p.N;
         const long want = ((long)p.R * n_out + 255) / 256;
         splitk_reduce_kernel<ACT><<<(unsigned)(want < 16384 ? want : 16384), 256, 0, stream>>>(p);
+    } else if (deep) {
+        gemm_stream_kernel<WT, ACT, GROUPED, false, 8><<<(unsigned)blocks, 64, 0, stream>>>(p, nbo);
     } else {
-        gemm_stream_kernel<WT, ACT, GROUPED, false, PF><<<(unsigned)blocks, 256, 0, stream>>>(p, nbo, ncbg);
+        gemm_stream_kernel<WT, ACT, GROUPED, false, 4><<<(unsigned)blocks, 64, 0, stream>>>(p, nbo);
     }
     return hipGetLastError();
 }
