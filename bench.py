@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--wtype", default="int4")
     ap.add_argument("--active", type=int, default=0, help="restrict routing to experts [0, A)")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 stream, 2 tile")
+    ap.add_argument("--tile", type=int, default=0,
+                    help="tile-path block tile: 0 auto, 1 64x256, 2 64x128, 3 128x128")
     ap.add_argument("--rotate-gb", type=float, default=1.0,
                     help="cycle weight copies totalling at least this many GB (cold weights)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -104,7 +106,7 @@ def main():
     inp = synth.make_inputs(cfg, T, wtype=args.wtype, active=args.active)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    layer = q.DeviceLayer.from_inputs(inp, device=dev, gemm_path=args.path)
+    layer = q.DeviceLayer.from_inputs(inp, device=dev, gemm_path=args.path, gemm_tile=args.tile)
     ws = layer.workspace(T)
     x = torch.from_numpy(inp.x).to(dev)
     logits = torch.from_numpy(inp.logits).to(dev)
@@ -175,8 +177,8 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         try:
             rec = json.load(open(TRAFFIC_FILE)).get(workload, {})
-            if rec.get("kernel_source_hash") == src_hash and rec.get("kernel") == dom_name:
-                traffic = rec.get("bytes_per_launch")
+            if rec.get("kernel_source_hash") == src_hash and dom_name in rec:
+                traffic = rec[dom_name].get("bytes_per_launch")
         except Exception:
             traffic = None
     roof["traffic"] = traffic

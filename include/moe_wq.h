@@ -60,10 +60,16 @@ enum moe_path  { MOE_PATH_AUTO = 0,           /* chosen from R, E, K, N         
                  MOE_PATH_TILE = 2 };         /* LDS-staged MFMA tile path, 128-row tiles */
 
 /* Optional per-call GEMM settings.  Pass NULL for the defaults (all fields 0). */
+enum moe_tile  { MOE_TILE_AUTO = 0,           /* chosen from R, E, K, N                  */
+                 MOE_TILE_64x256 = 1,         /* tile path: 64 rows x 256 weight columns */
+                 MOE_TILE_64x128 = 2,         /*            64 rows x 128 weight columns */
+                 MOE_TILE_128x128 = 3 };      /*           128 rows x 128 weight columns */
+
 typedef struct moe_gemm_opts {
     int32_t path;      /* enum moe_path                                              */
     int32_t split_k;   /* 0 = automatic; >= 1 forces the K split of the stream path  */
-    int32_t reserved[6];
+    int32_t tile;      /* enum moe_tile: block tile of the tile path                 */
+    int32_t reserved[5];
 } moe_gemm_opts;
 
 /* Limits. */

@@ -18,7 +18,8 @@ __all__ = [
     "MOE_OK", "MOE_ERR_INVALID", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
     "MOE_ERR_NO_DEVICE", "MOE_ERR_HIP",
     "GATE_TOPK", "GATE_ALL", "W_INT4", "W_INT8", "W_FP16", "ACT_NONE", "ACT_RELU",
-    "ACT_SWIGLU", "PATH_AUTO", "PATH_STREAM", "PATH_TILE",
+    "ACT_SWIGLU", "PATH_AUTO", "PATH_STREAM", "PATH_TILE", "TILE_AUTO", "TILE_64x256",
+    "TILE_64x128", "TILE_128x128",
     "MoEError", "MoELibraryError", "lib", "lib_path", "status_str", "version",
     "moe_route_topk", "moe_permute", "moe_grouped_gemm_wq", "moe_unpermute_combine",
     "moe_dequant", "moe_pack_wq", "moe_packed_bytes", "moe_gemm_workspace_size",
@@ -31,6 +32,7 @@ GATE_TOPK, GATE_ALL = 0, 1
 W_INT4, W_INT8, W_FP16 = 0, 1, 2
 ACT_NONE, ACT_RELU, ACT_SWIGLU = 0, 1, 2
 PATH_AUTO, PATH_STREAM, PATH_TILE = 0, 1, 2
+TILE_AUTO, TILE_64x256, TILE_64x128, TILE_128x128 = 0, 1, 2, 3
 
 WTYPES = {"int4": W_INT4, "int8": W_INT8, "fp16": W_FP16}
 ACTS = {"none": ACT_NONE, "relu": ACT_RELU, "swiglu": ACT_SWIGLU}
@@ -58,7 +60,7 @@ class MoELibraryError(ImportError):
 
 class GemmOpts(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("split_k", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("tile", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
 _lib = None
@@ -154,11 +156,11 @@ def _need(t, dtype, name, numel=None):
         raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
 
 
-def _opts(path=PATH_AUTO, split_k=0):
-    if path == PATH_AUTO and split_k == 0:
+def _opts(path=PATH_AUTO, split_k=0, tile=TILE_AUTO):
+    if path == PATH_AUTO and split_k == 0 and tile == TILE_AUTO:
         return None
     o = GemmOpts()
-    o.path, o.split_k = int(path), int(split_k)
+    o.path, o.split_k, o.tile = int(path), int(split_k), int(tile)
     return o
 
 
@@ -220,7 +222,7 @@ def moe_permute_workspace_size(T, k, E):
 
 def moe_grouped_gemm_wq(a, expert_offsets, E, K, N, w_packed, scales, wtype, group_size, act,
                         row_scale=None, out=None, path=PATH_AUTO, split_k=0, ws=None,
-                        stream=None):
+                        stream=None, tile=TILE_AUTO):
     torch = _torch()
     R = a.shape[0]
     wt = WTYPES.get(wtype, wtype)
@@ -228,7 +230,7 @@ def moe_grouped_gemm_wq(a, expert_offsets, E, K, N, w_packed, scales, wtype, gro
     n_out = N // 2 if ac == ACT_SWIGLU else N
     if out is None:
         out = torch.empty((R, n_out), dtype=torch.float16, device=a.device)
-    o = _opts(path, split_k)
+    o = _opts(path, split_k, tile)
     need_ws = lib().moe_gemm_workspace_size(R, E, K, N, wt, ac, ctypes.byref(o) if o else None)
     if need_ws and ws is None:
         ws = torch.empty(need_ws, dtype=torch.uint8, device=a.device)

@@ -116,6 +116,21 @@ __device__ __forceinline__ u32x4 load_weights16(const u32x4* p) {
 // its row count taken from the offsets, clamped into [0, R] so that any offsets array
 // yields in-bounds rows.  Executed by a whole wave; returns false when mt is past the end.
 // ------------------------------------------------------------------------------------
+// Total number of m-tiles (wave-uniform): sum over experts of ceil(c_e / BM).
+template <int BM>
+__device__ __forceinline__ int count_m_tiles(const int32_t* __restrict__ offsets, int E, int R) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int tiles = 0;
+    for (int e = lane; e < E; e += kWave) {
+        const int lo = min(max(offsets[e], 0), R);
+        const int hi = min(max(offsets[e + 1], 0), R);
+        tiles += (max(hi - lo, 0) + BM - 1) / BM;
+    }
+#pragma unroll
+    for (int s = 1; s < kWave; s <<= 1) tiles += __shfl_xor(tiles, s, kWave);
+    return __builtin_amdgcn_readfirstlane(tiles);
+}
+
 template <int BM>
 __device__ __forceinline__ bool find_m_tile(const int32_t* __restrict__ offsets, int E, int R,
                                             int mt, int& e_out, int& row0, int& rows) {

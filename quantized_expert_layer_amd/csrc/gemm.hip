@@ -410,25 +410,34 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
 
 template <int WT, int ACT, bool GROUPED, int MS, int NS>
 __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmParams p, int ncbg, int mt_ub,
-                                                           int grid_real) {
+                                                           int grid_real, int a_major) {
     constexpr int BM = 16 * MS;
     __shared__ __attribute__((aligned(16))) f16 lds[2 * BM * tile_kc<WT>()];
 
-    // XCD-aware order: hardware block b runs on XCD b % 8; each XCD gets a contiguous range
-    // of logical tiles, so the m-tiles that share a weight block share an L2.
-    const int G8 = gridDim.x / 8;
-    const int L = (blockIdx.x % 8) * G8 + blockIdx.x / 8;
-    if (L >= grid_real) return;
-    const int mt = L % mt_ub;
-    const int cbg = L / mt_ub;
+    // XCD-aware order: hardware block b runs on XCD b % 8.  The real tiles (counted from the
+    // offsets, not the host's upper bound) are split into 8 equal contiguous ranges, one per
+    // XCD, so that tiles sharing an operand share an L2.  a_major: m-tile slowest, so an
+    // activation tile is read by one XCD (for all its column groups); otherwise column group
+    // slowest, so an expert's weight block is read by one XCD.
+    (void)mt_ub; (void)grid_real;
+    const int mtiles = count_m_tiles<BM>(p.offsets, p.E, p.R);
+    const int real = mtiles * ncbg;
+    const int G8 = (real + 7) / 8;
+    const int j = blockIdx.x / 8;
+    const int L = (blockIdx.x % 8) * G8 + j;
+    if (j >= G8 || L >= real) return;
+    const int mt = a_major ? L / ncbg : L % mtiles;
+    const int cbg = a_major ? L % ncbg : L / mtiles;
     int e, row0, rows;
     if (!find_m_tile<BM>(p.offsets, p.E, p.R, mt, e, row0, rows)) return;
-    static_assert(MS == 4, "bodies below are instantiated for up to 4 subtiles");
+    // body specialised for the tile's number of 16-row subtiles (rounded up to 1, 2, 4, 6, 8)
     switch ((rows + 15) / 16) {
         case 1: tile_body<WT, ACT, GROUPED, 1, NS, BM>(p, lds, e, row0, rows, cbg); break;
         case 2: tile_body<WT, ACT, GROUPED, 2, NS, BM>(p, lds, e, row0, rows, cbg); break;
-        case 3: tile_body<WT, ACT, GROUPED, 3, NS, BM>(p, lds, e, row0, rows, cbg); break;
-        default: tile_body<WT, ACT, GROUPED, 4, NS, BM>(p, lds, e, row0, rows, cbg); break;
+        case 3: case 4: tile_body<WT, ACT, GROUPED, 4, NS, BM>(p, lds, e, row0, rows, cbg); break;
+        case 5: case 6:
+            tile_body<WT, ACT, GROUPED, (MS >= 6 ? 6 : 4), NS, BM>(p, lds, e, row0, rows, cbg); break;
+        default: tile_body<WT, ACT, GROUPED, MS, NS, BM>(p, lds, e, row0, rows, cbg); break;
     }
 }
 
@@ -488,27 +497,51 @@ static hipError_t stream_dispatch(const GemmParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int WT, int ACT, bool GROUPED>
-static hipError_t tile_dispatch(const GemmParams& p, hipStream_t stream) {
-    constexpr int MS = 4, BM = 16 * MS;
+template <int WT, int ACT, bool GROUPED, int MS, int NS>
+static hipError_t tile_launch(const GemmParams& p, hipStream_t stream) {
+    constexpr int BM = 16 * MS;
     const int ncbw = p.N / 16;
     const int nbo = (ACT == MOE_ACT_SWIGLU) ? ncbw / 2 : ncbw;
+    const int out_per_wave = (ACT == MOE_ACT_SWIGLU) ? NS / 2 : NS;
+    const int ncbg = cdiv(nbo, 4 * out_per_wave);
     const int active = p.R < p.E ? p.R : p.E;
     const int mt_ub = cdiv(p.R, BM) + active;
-    // 4 column blocks per wave when that still gives >= 4 blocks per CU, else 2
-    const int out_per_wave4 = (ACT == MOE_ACT_SWIGLU) ? 2 : 4;
-    const long blocks4 = (long)cdiv(nbo, 4 * out_per_wave4) * (cdiv(p.R, BM) + active / 2);
-    const bool wide = blocks4 >= 4L * 256;
-    const int out_per_wave = wide ? out_per_wave4 : out_per_wave4 / 2;
-    const int ncbg = cdiv(nbo, 4 * out_per_wave);
     const long real = (long)mt_ub * ncbg;
     const long grid = (real + 7) / 8 * 8;
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
-    if (wide)
-        gemm_tile_kernel<WT, ACT, GROUPED, MS, 4><<<(unsigned)grid, 256, 0, stream>>>(p, ncbg, mt_ub, (int)real);
-    else
-        gemm_tile_kernel<WT, ACT, GROUPED, MS, 2><<<(unsigned)grid, 256, 0, stream>>>(p, ncbg, mt_ub, (int)real);
+    // Which operand to keep XCD-local: re-reading the activations once per column group
+    // costs (ncbg - 1) * R*K*2 bytes; re-reading weights across the XCDs an expert's tiles
+    // span costs about the weight bytes of the active experts once more.
+    const int wbits = (WT == MOE_W_INT4) ? 4 : (WT == MOE_W_INT8 ? 8 : 16);
+    const double a_bytes = 2.0 * p.R * p.K;
+    const double w_bytes = (double)active * p.K * p.N * wbits / 8.0;
+    const int a_major = a_bytes * (ncbg - 1) > w_bytes ? 1 : 0;
+    gemm_tile_kernel<WT, ACT, GROUPED, MS, NS><<<(unsigned)grid, 256, 0, stream>>>(
+        p, ncbg, mt_ub, (int)real, a_major);
     return hipGetLastError();
+}
+
+// Block tile of the tile path.  64x256 (4 subtiles x 4 column blocks per wave) expands each
+// weight fragment for 4 MFMAs; 64x128 gives twice the blocks when N is small; 128x128
+// (8 x 2) expands each fragment for 8 MFMAs but measured slower at every shape here (it
+// holds 64 KB of LDS per block and reads twice the A fragments per MFMA), so it is only
+// used when asked for.
+int gemm_choose_tile(int R, int E, int N, int act, int forced) {
+    if (forced >= MOE_TILE_64x256 && forced <= MOE_TILE_128x128) return forced;
+    const int active = R < E ? R : E;
+    const int nbo = (act == MOE_ACT_SWIGLU) ? N / 32 : N / 16;
+    const int opw = (act == MOE_ACT_SWIGLU) ? 2 : 4;
+    const long blocks_wide = (long)cdiv(nbo, 4 * opw) * (cdiv(R, 64) + active / 2);
+    return blocks_wide >= 4L * 256 ? MOE_TILE_64x256 : MOE_TILE_64x128;
+}
+
+template <int WT, int ACT, bool GROUPED>
+static hipError_t tile_dispatch(const GemmParams& p, hipStream_t stream) {
+    switch (gemm_choose_tile(p.R, p.E, p.N, ACT, p.tile)) {
+        case MOE_TILE_64x256: return tile_launch<WT, ACT, GROUPED, 4, 4>(p, stream);
+        case MOE_TILE_128x128: return tile_launch<WT, ACT, GROUPED, 8, 2>(p, stream);
+        default: return tile_launch<WT, ACT, GROUPED, 4, 2>(p, stream);
+    }
 }
 
 #define MOE_DISPATCH(FN, p, stream)                                                        \

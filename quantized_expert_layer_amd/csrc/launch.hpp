@@ -34,11 +34,13 @@ struct GemmParams {
     int R, E, K, N;
     int wtype, group, act;
     int split;           // S
+    int tile;            // enum moe_tile (0 = automatic)
 };
 
 // Path/split decisions (host-only, deterministic in the arguments).
 int gemm_choose_path(int R, int E, int K, int N, int wtype, int act, int forced);
 int gemm_choose_split(int R, int E, int K, int N, int wtype, int act, int forced);
+int gemm_choose_tile(int R, int E, int N, int act, int forced);
 
 hipError_t launch_gemm_stream(const GemmParams& p, hipStream_t stream);
 hipError_t launch_gemm_tile(const GemmParams& p, hipStream_t stream);

@@ -35,13 +35,14 @@ class DeviceLayer:
     def __init__(self, *, E: int, k: int, d: int, inter: int, act: str, wtype: str, group: int,
                  gate_mode: str, codes1: np.ndarray, scales1: np.ndarray, codes2: np.ndarray,
                  scales2: np.ndarray, shared: Optional[List[Tuple[np.ndarray, np.ndarray]]] = None,
-                 device: str = "cuda", gemm_path: int = 0):
+                 device: str = "cuda", gemm_path: int = 0, gemm_tile: int = 0):
         import torch
         self.E, self.k, self.d, self.inter = E, k, d, inter
         self.act, self.wtype, self.group, self.gate_mode = act, wtype, group, gate_mode
         self.n1 = 2 * inter if act == "swiglu" else inter
         self.device = torch.device(device)
         self.gemm_path = gemm_path
+        self.gemm_tile = gemm_tile
         self.w1 = _dev(moe_pack_wq(codes1, wtype), self.device)
         self.w2 = _dev(moe_pack_wq(codes2, wtype), self.device)
         self.s1 = _dev(scales1.astype(np.float16), self.device)
@@ -61,12 +62,13 @@ class DeviceLayer:
                            _dev(moe_pack_wq(sw2.astype(np.float16), "fp16"), self.device))
 
     @classmethod
-    def from_inputs(cls, inp, device="cuda", gemm_path=0):
+    def from_inputs(cls, inp, device="cuda", gemm_path=0, gemm_tile=0):
         c = inp.cfg
         return cls(E=c.E, k=c.k, d=c.d, inter=c.inter, act=c.act, wtype=inp.wtype,
                    group=c.group, gate_mode=c.gate_mode, codes1=inp.codes1,
                    scales1=inp.scales1, codes2=inp.codes2, scales2=inp.scales2,
-                   shared=inp.shared or None, device=device, gemm_path=gemm_path)
+                   shared=inp.shared or None, device=device, gemm_path=gemm_path,
+                   gemm_tile=gemm_tile)
 
     def workspace(self, T: int) -> Workspace:
         import torch
@@ -111,11 +113,11 @@ class DeviceLayer:
                     out=(b["perm"], b["inv"], b["off"], b["xp"], b["wp"]), stream=stream)
         moe_grouped_gemm_wq(b["xp"], b["off"], self.E, self.d, self.n1, self.w1, self.s1,
                             self.wtype, self.group, self.act, out=b["h"], path=path,
-                            ws=b["ws"], stream=stream)
+                            ws=b["ws"], stream=stream, tile=self.gemm_tile)
         moe_grouped_gemm_wq(b["h"], b["off"], self.E, self.inter, self.d, self.w2, self.s2,
                             self.wtype, self.group, "none",
                             row_scale=b["wp"] if gate_in_gemm else None, out=b["y"],
-                            path=path, ws=b["ws"], stream=stream)
+                            path=path, ws=b["ws"], stream=stream, tile=self.gemm_tile)
         addend = None
         if self.shared is not None:
             moe_grouped_gemm_wq(x, b["sh_off"], 1, self.d, 2 * self.shared_inter,
@@ -140,10 +142,11 @@ class DeviceLayer:
         st = _stream(stream)
         path = self.gemm_path
         opts = None
-        if path:
+        if path or self.gemm_tile:
             from . import GemmOpts
             opts = GemmOpts()
             opts.path = path
+            opts.tile = self.gemm_tile
         ob = ctypes.byref(opts) if opts is not None else None
         wsp, wsn = _ptr(b["ws"]), b["ws"].numel()
         wt, ac = WTYPES[self.wtype], ACTS[self.act]

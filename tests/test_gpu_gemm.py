@@ -82,18 +82,23 @@ GEMM_CASES = [
 ]
 
 
-@pytest.mark.parametrize("path", [q.PATH_STREAM, q.PATH_TILE])
+PATHS = [(q.PATH_STREAM, q.TILE_AUTO), (q.PATH_TILE, q.TILE_64x256),
+         (q.PATH_TILE, q.TILE_64x128), (q.PATH_TILE, q.TILE_128x128)]
+
+
+@pytest.mark.parametrize("path,tile", PATHS)
 @pytest.mark.parametrize("act", ["none", "relu", "swiglu"])
 @pytest.mark.parametrize("E,K,N,wtype,group,T,k", GEMM_CASES)
-def test_grouped_gemm_matches_oracle(E, K, N, wtype, group, T, k, act, path):
+def test_grouped_gemm_matches_oracle(E, K, N, wtype, group, T, k, act, path, tile):
     if act == "swiglu" and N % 32:
         pytest.skip("SwiGLU needs an even number of 16-column blocks")
     codes, scales, off, a = _gemm_case(E, K, N, wtype, group, T, k, seed=E * K + N)
     R = a.shape[0]
     rs = np.random.default_rng(3).random(R, dtype=np.float32)
-    case(f"gemm E={E} K={K} N={N} {wtype} g={group} T={T} k={k} act={act} path={path}")
+    case(f"gemm E={E} K={K} N={N} {wtype} g={group} T={T} k={k} act={act} path={path} tile={tile}")
     out = q.moe_grouped_gemm_wq(dev(a), dev(off), E, K, N, dev(q.moe_pack_wq(codes, wtype)),
-                                dev(scales), wtype, group, act, row_scale=dev(rs), path=path)
+                                dev(scales), wtype, group, act, row_scale=dev(rs), path=path,
+                                tile=tile)
     wdq = oracle.dequant_algorithm1(codes, scales, group)
     ref = oracle.grouped_gemm(a, off, wdq, act, row_scale=rs)
     assert_layer_close(host(out), ref, "grouped gemm")
@@ -116,9 +121,9 @@ def test_stream_split_k_matches_oracle_and_unsplit(split):
         assert_layer_close(o1, ref, "unsplit")
 
 
-@pytest.mark.parametrize("path", [q.PATH_STREAM, q.PATH_TILE])
+@pytest.mark.parametrize("path,tile", PATHS)
 @pytest.mark.parametrize("wtype,group", [("int4", 0), ("int4", 128), ("int8", 0), ("int8", 128)])
-def test_one_hot_rows_reproduce_dequantized_weight_rows(wtype, group, path):
+def test_one_hot_rows_reproduce_dequantized_weight_rows(wtype, group, path, tile):
     # a one-hot row i of expert e gives exactly W_dq[e, i, :] (pins packing, nibble order,
     # scale indexing and the fragment layout inside the fused kernel)
     E, K, N = 3, 256, 64
@@ -126,16 +131,16 @@ def test_one_hot_rows_reproduce_dequantized_weight_rows(wtype, group, path):
     rows = [np.arange(0, K, 3), np.arange(1, K, 5), np.arange(2, K, 2)]   # ragged row counts
     a = np.concatenate([np.eye(K, dtype=np.float16)[r] for r in rows])
     off = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
-    case(f"one-hot {wtype} g={group} path={path}")
+    case(f"one-hot {wtype} g={group} path={path} tile={tile}")
     out = host(q.moe_grouped_gemm_wq(dev(a), dev(off), E, K, N, dev(q.moe_pack_wq(codes, wtype)),
-                                     dev(scales), wtype, group, "none", path=path))
+                                     dev(scales), wtype, group, "none", path=path, tile=tile))
     wdq = oracle.dequant_algorithm1(codes, scales, group)
     ref = np.concatenate([wdq[e][r] for e, r in enumerate(rows)])
     assert np.array_equal(out.view(np.uint16), ref.view(np.uint16))
 
 
-@pytest.mark.parametrize("path", [q.PATH_STREAM, q.PATH_TILE])
-def test_fp16_weights_and_zero_row_experts(path):
+@pytest.mark.parametrize("path,tile", PATHS)
+def test_fp16_weights_and_zero_row_experts(path, tile):
     E, K, N, T = 6, 256, 128, 40
     rng = np.random.default_rng(8)
     w = (rng.standard_normal((E, K, N)) * 0.05).astype(np.float16)
@@ -144,7 +149,7 @@ def test_fp16_weights_and_zero_row_experts(path):
     for act in ("none", "swiglu"):
         case(f"fp16 weights act={act} path={path}")
         out = q.moe_grouped_gemm_wq(dev(a), dev(off), E, K, N, dev(q.moe_pack_wq(w, "fp16")), None,
-                                    "fp16", 0, act, path=path)
+                                    "fp16", 0, act, path=path, tile=tile)
         ref = oracle.grouped_gemm(a, off, w.astype(np.float64), act)
         assert_layer_close(host(out), ref, "fp16 gemm")
 
