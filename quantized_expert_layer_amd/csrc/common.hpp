@@ -116,58 +116,63 @@ __device__ __forceinline__ u32x4 load_weights16(const u32x4* p) {
 // its row count taken from the offsets, clamped into [0, R] so that any offsets array
 // yields in-bounds rows.  Executed by a whole wave; returns false when mt is past the end.
 // ------------------------------------------------------------------------------------
-// Total number of m-tiles (wave-uniform): sum over experts of ceil(c_e / BM).
-template <int BM>
-__device__ __forceinline__ int count_m_tiles(const int32_t* __restrict__ offsets, int E, int R) {
+// Tile lookup in one pass over the offsets: the total number of m-tiles (sum over experts of
+// ceil(c_e / BM)) and, for logical tile index `want` (a function of that total), the expert,
+// first row and row count.  Row counts come from the offsets clamped into [0, R], so any
+// offsets array yields in-bounds rows.  Executed by a whole wave; results are wave-uniform.
+// Returns false when `want` maps past the last tile.
+template <int BM, typename F>
+__device__ __forceinline__ bool lookup_m_tile(const int32_t* __restrict__ offsets, int E, int R,
+                                              F want_of_total, int& mt_out, int& e_out,
+                                              int& row0, int& rows) {
     const int lane = threadIdx.x & (kWave - 1);
-    int tiles = 0;
-    for (int e = lane; e < E; e += kWave) {
-        const int lo = min(max(offsets[e], 0), R);
-        const int hi = min(max(offsets[e + 1], 0), R);
-        tiles += (max(hi - lo, 0) + BM - 1) / BM;
-    }
+    constexpr int MAXC = (MOE_MAX_EXPERTS + kWave - 1) / kWave;
+    int lo[MAXC], hi[MAXC], tl[MAXC], incl[MAXC];
+    int total = 0;
 #pragma unroll
-    for (int s = 1; s < kWave; s <<= 1) tiles += __shfl_xor(tiles, s, kWave);
-    return __builtin_amdgcn_readfirstlane(tiles);
+    for (int c = 0; c < MAXC; ++c) {
+        const int e = c * kWave + lane;
+        lo[c] = hi[c] = 0;
+        if (e < E) {
+            lo[c] = min(max(offsets[e], 0), R);
+            hi[c] = min(max(offsets[e + 1], 0), R);
+        }
+        tl[c] = (max(hi[c] - lo[c], 0) + BM - 1) / BM;
+        int v = tl[c];
+#pragma unroll
+        for (int s = 1; s < kWave; s <<= 1) {
+            const int u = __shfl_up(v, s, kWave);
+            if (lane >= s) v += u;
+        }
+        incl[c] = total + v;
+        total += __shfl(v, kWave - 1, kWave);
+    }
+    total = __builtin_amdgcn_readfirstlane(total);
+    const int mt = want_of_total(total);
+    if (mt < 0 || mt >= total) return false;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int excl = incl[c] - tl[c];
+        const unsigned long long hit = __ballot(tl[c] > 0 && mt >= excl && mt < incl[c]);
+        if (hit) {
+            const int src = __builtin_ctzll(hit);
+            const int my_row0 = lo[c] + (mt - excl) * BM;
+            const int my_rows = min(BM, hi[c] - my_row0);
+            mt_out = mt;
+            e_out = __builtin_amdgcn_readfirstlane(__shfl(c * kWave + lane, src, kWave));
+            row0 = __builtin_amdgcn_readfirstlane(__shfl(my_row0, src, kWave));
+            rows = __builtin_amdgcn_readfirstlane(__shfl(my_rows, src, kWave));
+            return true;
+        }
+    }
+    return false;
 }
 
 template <int BM>
 __device__ __forceinline__ bool find_m_tile(const int32_t* __restrict__ offsets, int E, int R,
                                             int mt, int& e_out, int& row0, int& rows) {
-    const int lane = threadIdx.x & (kWave - 1);
-    int base = 0;
-    for (int e0 = 0; e0 < E; e0 += kWave) {
-        const int e = e0 + lane;
-        int lo = 0, hi = 0;
-        if (e < E) {
-            lo = min(max(offsets[e], 0), R);
-            hi = min(max(offsets[e + 1], 0), R);
-        }
-        const int cnt = max(hi - lo, 0);
-        const int tiles = (cnt + BM - 1) / BM;
-        // inclusive prefix sum of tiles across the wave
-        int incl = tiles;
-#pragma unroll
-        for (int s = 1; s < kWave; s <<= 1) {
-            const int v = __shfl_up(incl, s, kWave);
-            if (lane >= s) incl += v;
-        }
-        const int excl = incl - tiles;
-        const unsigned long long hit = __ballot(tiles > 0 && mt >= base + excl && mt < base + incl);
-        if (hit) {
-            const int src = __builtin_ctzll(hit);
-            const int my_row0 = lo + (mt - base - excl) * BM;
-            const int my_rows = min(BM, hi - my_row0);
-            // readfirstlane: the results are wave-uniform, keep them in scalar registers so
-            // that branches on them are scalar branches rather than exec-mask regions
-            e_out = __builtin_amdgcn_readfirstlane(__shfl(e, src, kWave));
-            row0 = __builtin_amdgcn_readfirstlane(__shfl(my_row0, src, kWave));
-            rows = __builtin_amdgcn_readfirstlane(__shfl(my_rows, src, kWave));
-            return true;
-        }
-        base += __shfl(incl, kWave - 1, kWave);
-    }
-    return false;
+    int m;
+    return lookup_m_tile<BM>(offsets, E, R, [mt](int) { return mt; }, m, e_out, row0, rows);
 }
 
 }  // namespace moe

@@ -234,6 +234,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
 //                 16-row subtiles (1..MS), so it neither loads nor multiplies absent rows.
 //   occupancy   = 2+ blocks per CU, so each SIMD interleaves at least two waves.
 // ------------------------------------------------------------------------------------
+// K per stage: 128 rows for int4/int8 codes (one 128-group), 64 for fp16 weights (whose
+// register double buffer is 4x larger per row).  256-row int4 stages measured slower: the
+// extra registers cost more than the longer cover of the next stage's load latency.
 template <int WT> constexpr int tile_kc() { return WT == MOE_W_FP16 ? 64 : 128; }
 
 template <int WT, int ACT, bool GROUPED, int MA, int NS, int BM>
@@ -300,14 +303,19 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
                 *(u32x4*)(lds + buf * LDS_BUF + adst[i]) = areg[i];
     };
 
+    // group scales: one per (column block, super-block) -- a super-block never spans groups
+    constexpr int SCS = GROUPED ? SBPS : 1;
     u32x4 bcur[NS][SBPS], bnext[NS][SBPS];
-    uint16_t scur[NS] = {}, snext[NS] = {};
-    auto load_b = [&](u32x4 (&b)[NS][SBPS], uint16_t (&sc)[NS], int st) {
+    uint32_t scur[NS][SCS] = {}, snext[NS][SCS] = {};
+    auto load_b = [&](u32x4 (&b)[NS][SBPS], uint32_t (&sc)[NS][SCS], int st) {
 #pragma unroll
         for (int c = 0; c < NS; ++c) {
 #pragma unroll
-            for (int q = 0; q < SBPS; ++q) b[c][q] = wp[c][(size_t)(st * SBPS + q) * kWave];
-            if constexpr (GROUPED) sc[c] = sp[(size_t)((st * KC) >> 7) * N + ncol[c]];
+            for (int q = 0; q < SBPS; ++q) {
+                b[c][q] = wp[c][(size_t)(st * SBPS + q) * kWave];
+                if constexpr (GROUPED)
+                    sc[c][q] = (uint32_t)sp[(size_t)((st * KC + q * KSB) >> 7) * N + ncol[c]];
+            }
         }
     };
 
@@ -340,7 +348,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         auto expand = [&](f16x8 (&bq)[NS], int ks) {
 #pragma unroll
             for (int c = 0; c < NS; ++c) {
-                const f16 sv = __builtin_bit_cast(f16, scur[c]);
+                const f16 sv = __builtin_bit_cast(f16, (uint16_t)scur[c][GROUPED ? ks / KSPS : 0]);
                 const f16x2 s2 = {sv, sv};
                 bq[c] = weight_frag<WT, GROUPED>(bcur[c][ks / KSPS], ks % KSPS, s2, k4);
             }
@@ -370,7 +378,8 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         for (int c = 0; c < NS; ++c) {
 #pragma unroll
             for (int q = 0; q < SBPS; ++q) bcur[c][q] = bnext[c][q];
-            scur[c] = snext[c];
+#pragma unroll
+            for (int q = 0; q < SCS; ++q) scur[c][q] = snext[c][q];
         }
     }
 
@@ -420,16 +429,19 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmParams p, int ncb
     // activation tile is read by one XCD (for all its column groups); otherwise column group
     // slowest, so an expert's weight block is read by one XCD.
     (void)mt_ub; (void)grid_real;
-    const int mtiles = count_m_tiles<BM>(p.offsets, p.E, p.R);
-    const int real = mtiles * ncbg;
-    const int G8 = (real + 7) / 8;
-    const int j = blockIdx.x / 8;
-    const int L = (blockIdx.x % 8) * G8 + j;
-    if (j >= G8 || L >= real) return;
-    const int mt = a_major ? L / ncbg : L % mtiles;
+    int L = -1, mtiles = 0;
+    auto logical_mt = [&](int total) {
+        mtiles = total;
+        const int real = total * ncbg;
+        const int G8 = (real + 7) / 8;
+        const int j = blockIdx.x / 8;
+        L = (blockIdx.x % 8) * G8 + j;
+        if (j >= G8 || L >= real) return -1;
+        return a_major ? L / ncbg : L % total;
+    };
+    int mt, e, row0, rows;
+    if (!lookup_m_tile<BM>(p.offsets, p.E, p.R, logical_mt, mt, e, row0, rows)) return;
     const int cbg = a_major ? L % ncbg : L / mtiles;
-    int e, row0, rows;
-    if (!find_m_tile<BM>(p.offsets, p.E, p.R, mt, e, row0, rows)) return;
     // body specialised for the tile's number of 16-row subtiles (rounded up to 1, 2, 4, 6, 8)
     switch ((rows + 15) / 16) {
         case 1: tile_body<WT, ACT, GROUPED, 1, NS, BM>(p, lds, e, row0, rows, cbg); break;

@@ -35,6 +35,11 @@ __device__ __forceinline__ Match wave_match(int key, bool valid, int nbits, int 
     return m;
 }
 
+constexpr int kSortLdsKeys = 16384;     // keys staged in LDS when R fits (64 KB)
+
+// KEYS_IN_LDS: all R keys are first copied to LDS with one coalesced pass, so the two walks
+// below read LDS instead of issuing one dependent global load per 64-key chunk.
+template <bool KEYS_IN_LDS>
 __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ ids,
                                                     const float* __restrict__ wts, int R, int E,
                                                     int32_t* __restrict__ perm,
@@ -42,6 +47,7 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ offsets,
                                                     float* __restrict__ w_perm) {
     __shared__ int cnt[kSortWaves][MOE_MAX_EXPERTS];
+    __shared__ int keys[KEYS_IN_LDS ? kSortLdsKeys : 1];
     __shared__ int wave_sum[4];
     __shared__ int n_valid;
     const int lane = threadIdx.x & (kWave - 1);
@@ -49,7 +55,15 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
 
     for (int i = threadIdx.x; i < kSortWaves * MOE_MAX_EXPERTS; i += blockDim.x)
         (&cnt[0][0])[i] = 0;
+    if constexpr (KEYS_IN_LDS) {
+        for (int i = threadIdx.x; i < R; i += blockDim.x) keys[i] = ids[i];
+    }
     __syncthreads();
+    auto key_of = [&](int f) -> int {
+        if (f >= R) return -1;
+        if constexpr (KEYS_IN_LDS) return keys[f];
+        else return ids[f];
+    };
 
     const int nbits = (E <= 1) ? 0 : 32 - __clz(E - 1);
     const int chunks = (R + kWave - 1) / kWave;
@@ -59,7 +73,7 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
     // pass 1: per-wave key counts
     for (int c = c0; c < c1; ++c) {
         const int f = c * kWave + lane;
-        const int key = (f < R) ? ids[f] : -1;
+        const int key = key_of(f);
         const bool valid = (unsigned)key < (unsigned)E;
         const Match m = wave_match(key, valid, nbits, lane);
         if (valid && m.rank == m.total - 1) cnt[wave][key] += m.total;
@@ -105,7 +119,7 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
     // pass 2: scatter
     for (int c = c0; c < c1; ++c) {
         const int f = c * kWave + lane;
-        const int key = (f < R) ? ids[f] : -1;
+        const int key = key_of(f);
         const bool valid = (unsigned)key < (unsigned)E;
         const Match m = wave_match(key, valid, nbits, lane);
         if (valid) {
@@ -144,8 +158,12 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x
 
 hipError_t launch_sort(const int32_t* ids, const float* wts, int R, int E, int32_t* perm,
                        int32_t* inv_perm, int32_t* offsets, float* w_perm, hipStream_t stream) {
-    sort_kernel<<<1, kSortWaves * kWave, 0, stream>>>(ids, wts, R, E, perm, inv_perm, offsets,
-                                                      w_perm);
+    if (R <= kSortLdsKeys)
+        sort_kernel<true><<<1, kSortWaves * kWave, 0, stream>>>(ids, wts, R, E, perm, inv_perm,
+                                                                offsets, w_perm);
+    else
+        sort_kernel<false><<<1, kSortWaves * kWave, 0, stream>>>(ids, wts, R, E, perm, inv_perm,
+                                                                 offsets, w_perm);
     return hipGetLastError();
 }
 

@@ -182,7 +182,10 @@ class DeviceLayer:
         calls.append(("combine", L.moe_unpermute_combine,
                       (_ptr(b["y"]), _ptr(b["inv"]), None if gate_in_gemm else _ptr(b["w"]),
                        _ptr(addend), T, self.k, self.d, _ptr(b["out"]), st)))
-        return LayerPlan(calls, b["out"], keep=(opts, x, logits, w1, w2))
+        # the plan holds raw device pointers: keep every tensor they point into alive for as
+        # long as the plan exists (the layer itself may be dropped by the caller)
+        return LayerPlan(calls, b["out"], keep=(opts, x, logits, w1, w2, self.s1, self.s2,
+                                                self.shared, ws))
 
 
 class LayerPlan:

@@ -82,3 +82,28 @@ def test_layer_is_deterministic_and_token_order_equivariant(name, T):
     p = np.random.default_rng(1).permutation(T)
     c = host(layer.forward(dev(inp.x[p]), dev(inp.logits[p])))
     assert np.array_equal(c.view(np.uint16), a[p].view(np.uint16))
+
+
+@pytest.mark.parametrize("name,T", [("qwen15_moe", 544), ("dsv2_lite", 9)])
+def test_plan_outlives_its_layer(name, T):
+    """A pre-marshalled plan holds raw device pointers (weights, scales, shared-expert weights,
+    workspace); it must keep them alive after the caller drops the layer and the workspace."""
+    import gc
+
+    import torch
+
+    inp = synth.make_inputs(synth.get_config(name), T)
+    x, logits = dev(inp.x), dev(inp.logits)
+    layer = q.DeviceLayer.from_inputs(inp)
+    want = host(layer.forward(x, logits))
+    plan = layer.plan(layer.workspace(T), x, logits)
+    del layer
+    gc.collect()
+    # churn the caching allocator so freed blocks would be handed out again and overwritten
+    junk = [torch.full((1 << 20,), float("nan"), dtype=torch.float16, device="cuda")
+            for _ in range(64)]
+    case(f"plan without its layer {name} T={T}")
+    plan.run()
+    got = host(plan.out)
+    del junk
+    np.testing.assert_array_equal(got, want)

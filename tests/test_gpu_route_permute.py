@@ -47,7 +47,7 @@ def test_route_topk_tie_heavy(E, k):
 PERMUTE_CASES = [(16, 2, 8, 128, False), (17, 4, 60, 2048, True), (544, 4, 60, 64, True),
                  (288, 6, 64, 64, True), (1, 2, 16, 4096, False), (3840, 1, 32, 1024, True),
                  (8192, 2, 16, 64, False), (97, 8, 256, 24, True), (5, 1, 1, 8, False),
-                 (2049, 3, 7, 16, True)]
+                 (2049, 3, 7, 16, True), (5000, 4, 64, 16, True)]
 
 
 @pytest.mark.parametrize("T,k,E,d,skew", PERMUTE_CASES)
