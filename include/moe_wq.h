@@ -57,7 +57,7 @@ enum moe_wtype { MOE_W_INT4 = 0, MOE_W_INT8 = 1, MOE_W_FP16 = 2 };
 enum moe_act   { MOE_ACT_NONE = 0, MOE_ACT_RELU = 1, MOE_ACT_SWIGLU = 2 };
 enum moe_path  { MOE_PATH_AUTO = 0,           /* chosen from R, E, K, N                  */
                  MOE_PATH_STREAM = 1,         /* weight-streaming path, 16-row tiles     */
-                 MOE_PATH_TILE = 2 };         /* LDS-staged MFMA tile path, 128-row tiles */
+                 MOE_PATH_TILE = 2 };         /* LDS-staged MFMA tile path, 64-row tiles  */
 
 /* Optional per-call GEMM settings.  Pass NULL for the defaults (all fields 0). */
 enum moe_tile  { MOE_TILE_AUTO = 0,           /* chosen from R, E, K, N                  */
@@ -67,7 +67,8 @@ enum moe_tile  { MOE_TILE_AUTO = 0,           /* chosen from R, E, K, N         
 
 typedef struct moe_gemm_opts {
     int32_t path;      /* enum moe_path                                              */
-    int32_t split_k;   /* 0 = automatic; >= 1 forces the K split of the stream path  */
+    int32_t split_k;   /* 0 = automatic; 1..MOE_MAX_SPLIT_K forces the number of  */
+                       /* waves that split K per stream-path block                 */
     int32_t tile;      /* enum moe_tile: block tile of the tile path                 */
     int32_t reserved[5];
 } moe_gemm_opts;
@@ -75,7 +76,7 @@ typedef struct moe_gemm_opts {
 /* Limits. */
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK      8
-#define MOE_MAX_SPLIT_K  16
+#define MOE_MAX_SPLIT_K   8
 
 /*
  * moe_route_topk -- top-k gating.   [S] Background / MoE: the router scores every expert
@@ -140,7 +141,8 @@ size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E);
  *                   (the gate weight, w_perm) after the activation.
  *   out             fp16 [R, N or N/2]; rows at or beyond offsets[E] are not written.
  *   opts            [host] NULL or settings (path, split).
- *   ws, ws_bytes    workspace of at least moe_gemm_workspace_size(...) bytes.
+ *   ws, ws_bytes    workspace of at least moe_gemm_workspace_size(...) bytes (currently
+ *                   0 for every argument set: NULL / 0 may be passed).
  *   Accumulation is fp32, the result is rounded once to fp16 (nearest even).
  *   Requires K % 128 == 0, N % 16 == 0 (N % 32 for SWIGLU), E <= 256, group_size in
  *   {0, 128} (0 only for FP16 weights).

@@ -19,7 +19,7 @@ __all__ = [
     "MOE_ERR_NO_DEVICE", "MOE_ERR_HIP",
     "GATE_TOPK", "GATE_ALL", "W_INT4", "W_INT8", "W_FP16", "ACT_NONE", "ACT_RELU",
     "ACT_SWIGLU", "PATH_AUTO", "PATH_STREAM", "PATH_TILE", "TILE_AUTO", "TILE_64x256",
-    "TILE_64x128", "TILE_128x128",
+    "TILE_64x128", "TILE_128x128", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SPLIT_K",
     "MoEError", "MoELibraryError", "lib", "lib_path", "status_str", "version",
     "moe_route_topk", "moe_permute", "moe_grouped_gemm_wq", "moe_unpermute_combine",
     "moe_dequant", "moe_pack_wq", "moe_packed_bytes", "moe_gemm_workspace_size",
@@ -33,6 +33,7 @@ W_INT4, W_INT8, W_FP16 = 0, 1, 2
 ACT_NONE, ACT_RELU, ACT_SWIGLU = 0, 1, 2
 PATH_AUTO, PATH_STREAM, PATH_TILE = 0, 1, 2
 TILE_AUTO, TILE_64x256, TILE_64x128, TILE_128x128 = 0, 1, 2, 3
+MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_SPLIT_K = 256, 8, 8
 
 WTYPES = {"int4": W_INT4, "int8": W_INT8, "fp16": W_FP16}
 ACTS = {"none": ACT_NONE, "relu": ACT_RELU, "swiglu": ACT_SWIGLU}

@@ -52,7 +52,7 @@ GemmPlan plan_gemm(int32_t R, int32_t E, int32_t K, int32_t N, int32_t wtype, in
     pl.path = moe::gemm_choose_path(R, E, K, N, wtype, act, forced_path);
     pl.split = 1;
     if (pl.path == MOE_PATH_STREAM) pl.split = moe::gemm_choose_split(R, E, K, N, wtype, act, forced_split);
-    pl.ws = pl.split > 1 ? (size_t)pl.split * (size_t)R * (size_t)N * sizeof(float) : 0;
+    pl.ws = 0;                                   // no kernel of either path needs one
     return pl;
 }
 
@@ -171,7 +171,6 @@ int32_t moe_grouped_gemm_wq(const uint16_t* a, const int32_t* expert_offsets, in
     p.scales = scales;
     p.row_scale = row_scale;
     p.out = out;
-    p.partial = (float*)ws;
     p.R = R;
     p.E = E;
     p.K = K;

@@ -105,6 +105,15 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
     return (float)__builtin_bit_cast(f16, b);
 }
 
+// Marks a register value as read here, so its load has completed and its registers are not
+// handed to other values before this point.  Used where a prefetch ring ends: the ring's last
+// (repeated) loads are never consumed otherwise, and a register that still awaits one must not
+// be reused by the epilogue.
+template <typename T>
+__device__ __forceinline__ void consume(const T& v) {
+    asm volatile("; consume %0" : : "v"(v));
+}
+
 // Non-temporal 16-byte load of packed weights (streamed once; keep caches for activations).
 __device__ __forceinline__ u32x4 load_weights16(const u32x4* p) {
     return __builtin_nontemporal_load(p);

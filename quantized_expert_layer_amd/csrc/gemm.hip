@@ -65,33 +65,39 @@ __device__ __forceinline__ f32x4 load4_scale(const uint16_t* src) {
 
 // ------------------------------------------------------------------------------------
 // Stream path.
-//   grid  = m-tiles(upper bound) x NBo x S one-wave blocks (small blocks balance the few
-//           hundred to few thousand streams of a decode step evenly over the CUs).
-//   wave  = one 16-column output block; for SwiGLU it streams the gate block and the up
-//           block (columns I + ...) of the same 16 outputs.
+//   grid  = m-tiles(upper bound) x NBo blocks of S waves (S = p.split, 1..MOE_MAX_SPLIT_K).
+//   block = one 16-row m-tile x one 16-column output block; for SwiGLU the gate block and
+//           the up block (columns I + ...) of the same 16 outputs.  Wave w of the block
+//           streams the w-th of S equal K slices; the S partial sums meet in LDS and are
+//           added in the fixed order 0, 1, .., S-1 by wave 0, which runs the epilogue.
+//           Splitting K inside the block multiplies the waves of a decode step (which has
+//           few output blocks) without a second launch or a workspace.
+//   scales= per-channel and group scales multiply fp32 sums: a group-128 scale the sum of
+//           one super-block's MFMAs, a per-channel scale the final sum.  Mathematically this
+//           is the sum over the scaled weights; it skips the fp16 rounding of each scaled
+//           weight and saves a packed multiply per weight pair.
 // ------------------------------------------------------------------------------------
-template <int WT, int ACT, bool GROUPED, bool SPLIT, int PF>
-__global__ __launch_bounds__(64) void gemm_stream_kernel(GemmParams p, int nbo) {
+template <int WT, int ACT, bool GROUPED, int PF>
+__global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmParams p, int nbo) {
     constexpr int KSB = WTraits<WT>::KSB;
     constexpr int KSTEPS = KSB / 32;
     constexpr int NCB = (ACT == MOE_ACT_SWIGLU) ? 2 : 1;
+    extern __shared__ f32x4 red[];          // [S - 1][NCB][64] partial sums of waves 1..S-1
     const int lane = threadIdx.x & (kWave - 1);
-    const int S = p.split;
+    const int w = threadIdx.x / kWave;
+    const int S = blockDim.x / kWave;
 
-    // one wave per block: (m-tile, output column block, K slice), m-tile slowest so that the
-    // blocks of existing tiles come first and the surplus of the upper-bound grid exits last
-    int b = blockIdx.x;
-    const int s = b % S;
-    b /= S;
-    const int cbo = b % nbo;
-    const int mt = b / nbo;
+    // (m-tile, output column block), m-tile slowest so that the blocks of existing tiles come
+    // first and the surplus of the upper-bound grid exits last
+    const int cbo = blockIdx.x % nbo;
+    const int mt = blockIdx.x / nbo;
     int e, row0, rows;
-    if (!find_m_tile<16>(p.offsets, p.E, p.R, mt, e, row0, rows)) return;
+    if (!find_m_tile<16>(p.offsets, p.E, p.R, mt, e, row0, rows)) return;   // block-uniform
 
     const int K = p.K, N = p.N;
     const int nSB = K / KSB;
     const int chunk = (nSB + S - 1) / S;
-    const int kb0 = s * chunk;
+    const int kb0 = min(nSB, w * chunk);
     const int kb1 = min(nSB, kb0 + chunk);
 
     const int ncbw = N / 16;
@@ -131,15 +137,24 @@ __global__ __launch_bounds__(64) void gemm_stream_kernel(GemmParams p, int nbo) 
     };
 
     const I2F4Consts k4;
+    const f16x2 one2 = {(f16)1.0f, (f16)1.0f};
     auto compute = [&](const u32x4 (&bq)[NCB], const uint32_t (&sq)[NCB],
                        const f16x8 (&aq)[KSTEPS]) {
 #pragma unroll
         for (int c = 0; c < NCB; ++c) {
-            const f16 sv = __builtin_bit_cast(f16, (uint16_t)sq[c]);
-            const f16x2 s2 = {sv, sv};
+            if constexpr (GROUPED) {
+                f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < KSTEPS; ++j)
-                acc[c] = mfma16x16x32(weight_frag<WT, GROUPED>(bq[c], j, s2, k4), aq[j], acc[c]);
+                for (int j = 0; j < KSTEPS; ++j)
+                    t = mfma16x16x32(aq[j], weight_frag<WT, false>(bq[c], j, one2, k4), t);
+                const float s = (float)__builtin_bit_cast(f16, (uint16_t)sq[c]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[c][i] = __builtin_fmaf(t[i], s, acc[c][i]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < KSTEPS; ++j)
+                    acc[c] = mfma16x16x32(aq[j], weight_frag<WT, false>(bq[c], j, one2, k4), acc[c]);
+            }
         }
     };
 
@@ -161,61 +176,57 @@ __global__ __launch_bounds__(64) void gemm_stream_kernel(GemmParams p, int nbo) 
 #pragma unroll
         for (int u = 0; u < PF; ++u)
             if (kc + u < kb1) compute(braw[u], sraw[u], araw[u]);
+        // every ring slot holds a load (a repeat of the last block where the slice ran out)
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+#pragma unroll
+            for (int c = 0; c < NCB; ++c) {
+                consume(braw[u][c]);
+                if constexpr (GROUPED) consume(sraw[u][c]);
+            }
+#pragma unroll
+            for (int j = 0; j < KSTEPS; ++j) consume(araw[u][j]);
+        }
     }
 
-    // per-channel scales on the fp32 sums (4 consecutive output columns per lane)
-    const int q4 = 4 * (lane >> 4);
+    // fixed-order reduction of the K slices
+    if (S > 1) {
+        if (w > 0) {
+#pragma unroll
+            for (int c = 0; c < NCB; ++c) red[((w - 1) * NCB + c) * kWave + lane] = acc[c];
+        }
+        __syncthreads();
+        if (w > 0) return;
+        for (int s = 1; s < S; ++s) {
+#pragma unroll
+            for (int c = 0; c < NCB; ++c) acc[c] += red[((s - 1) * NCB + c) * kWave + lane];
+        }
+    }
+
+    // The activation fragment is the MFMA's first operand here, so lane l holds output
+    // column (l & 15) of rows 4*(l >> 4) .. +3: one scale per lane, the same column as the
+    // lane's weight fragment (the output of a decode block is a few hundred bytes, so its
+    // 2-byte stores cost nothing).
     if constexpr (!GROUPED && WT != MOE_W_FP16) {
 #pragma unroll
-        for (int c = 0; c < NCB; ++c) acc[c] *= load4_scale(sp + (cbo + c * nbo) * 16 + q4);
-    }
-
-    const int r = lane & 15;                 // row of this lane within the tile
-    if (r < rows) {
-        if constexpr (SPLIT) {
-            // fp32 partial sums of this K slice: partial[s][row][n], 16 bytes per lane
-            float* dst = p.partial + ((size_t)s * p.R + row0 + r) * N;
+        for (int c = 0; c < NCB; ++c) {
+            const float sc = f16_bits_to_f32(sp[ncol[c]]);
 #pragma unroll
-            for (int c = 0; c < NCB; ++c) *(f32x4*)(dst + (cbo + c * nbo) * 16 + q4) = acc[c];
-        } else {
-            const int n_out = (ACT == MOE_ACT_SWIGLU) ? N / 2 : N;
-            const float rs = p.row_scale ? p.row_scale[row0 + r] : 1.0f;
-            float v[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if constexpr (ACT == MOE_ACT_SWIGLU) v[i] = silu(acc[0][i]) * acc[1][i];
-                else if constexpr (ACT == MOE_ACT_RELU) v[i] = fmaxf(acc[0][i], 0.0f);
-                else v[i] = acc[0][i];
-                v[i] *= rs;
-            }
-            store4_f16(p.out + (size_t)(row0 + r) * n_out + cbo * 16 + q4, v[0], v[1], v[2], v[3]);
+            for (int i = 0; i < 4; ++i) acc[c][i] *= sc;
         }
     }
-}
-
-// Fixed-order reduction of the split-K partial sums, then activation and row scale.
-template <int ACT>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
-    const int N = p.N;
     const int n_out = (ACT == MOE_ACT_SWIGLU) ? N / 2 : N;
-    const int rows = min(max(p.offsets[p.E], 0), p.R);
-    const size_t total = (size_t)rows * n_out;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (size_t)gridDim.x * blockDim.x) {
-        const int r = (int)(i / n_out);
-        const int c = (int)(i - (size_t)r * n_out);
-        float g = 0.f, u = 0.f;
-        for (int s = 0; s < p.split; ++s) {
-            const float* src = p.partial + ((size_t)s * p.R + r) * N;
-            g += src[c];
-            if constexpr (ACT == MOE_ACT_SWIGLU) u += src[n_out + c];
-        }
+    uint16_t* ocol = p.out + cbo * 16 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * (lane >> 4) + i;      // row of the tile
+        if (r >= rows) break;
         float v;
-        if constexpr (ACT == MOE_ACT_SWIGLU) v = silu(g) * u;
-        else if constexpr (ACT == MOE_ACT_RELU) v = fmaxf(g, 0.0f);
-        else v = g;
-        if (p.row_scale) v *= p.row_scale[r];
-        p.out[i] = f32_to_f16_bits(v);
+        if constexpr (ACT == MOE_ACT_SWIGLU) v = silu(acc[0][i]) * acc[1][i];
+        else if constexpr (ACT == MOE_ACT_RELU) v = fmaxf(acc[0][i], 0.0f);
+        else v = acc[0][i];
+        if (p.row_scale) v *= p.row_scale[row0 + r];
+        ocol[(size_t)(row0 + r) * n_out] = f32_to_f16_bits(v);
     }
 }
 
@@ -383,6 +394,15 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         }
     }
 
+    // the last stage prefetched a repeat of itself, which nothing reads
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+#pragma unroll
+        for (int q = 0; q < SBPS; ++q) consume(bnext[c][q]);
+#pragma unroll
+        for (int q = 0; q < SCS; ++q) consume(snext[c][q]);
+    }
+
     // epilogue: lane holds row (lane & 15) of each subtile, 4 consecutive columns per block
     const int q4 = 4 * (lane >> 4);
     if constexpr (!GROUPED && WT != MOE_W_FP16) {
@@ -473,11 +493,13 @@ int gemm_choose_split(int R, int E, int K, int N, int wtype, int act, int forced
     const int nSB = K / KSB;
     const int active = R < E ? R : E;
     const int nbo = (act == MOE_ACT_SWIGLU) ? N / 32 : N / 16;
-    const long waves = (long)active * cdiv(R, active > 0 ? active * 16 : 16) * nbo;
-    // split only when there would be fewer than 2 streaming waves per CU: the fixed-order
-    // reduction is a second launch, which costs more than a moderately long stream
+    const long blocks = (long)active * cdiv(R, active > 0 ? active * 16 : 16) * nbo;
+    // Split only a launch with fewer than two blocks per CU: with a few hundred streams or
+    // more, extra waves per SIMD measured no faster (the streams already share each SIMD's
+    // VALU issue for the in-register dequantization), and each slice keeps at least 8
+    // super-blocks so its load ring stays filled.
     int s = 1;
-    while (s < MOE_MAX_SPLIT_K && waves * s < 512 && nSB / (2 * s) >= 8) s *= 2;
+    while (s < MOE_MAX_SPLIT_K && blocks * s < 512 && nSB / (2 * s) >= 8) s *= 2;
     return s;
 }
 
@@ -486,26 +508,17 @@ static hipError_t stream_dispatch(const GemmParams& p, hipStream_t stream) {
     const int nbo = (ACT == MOE_ACT_SWIGLU) ? p.N / 32 : p.N / 16;
     const int active = p.R < p.E ? p.R : p.E;
     const int mt_ub = cdiv(p.R, 16) + active;
-    const long blocks = (long)mt_ub * nbo * p.split;
-    if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+    const long blocks = (long)mt_ub * nbo;
+    if (blocks > 0x7fffffffL || p.split < 1 || p.split > MOE_MAX_SPLIT_K) return hipErrorInvalidValue;
+    constexpr int NCB = (ACT == MOE_ACT_SWIGLU) ? 2 : 1;
+    const unsigned threads = 64u * (unsigned)p.split;
+    const size_t lds = (size_t)(p.split - 1) * NCB * 64 * sizeof(f32x4);
     // few rows (a decode step): few streams, so each keeps 8 super-blocks in flight;
     // otherwise 4, which leaves registers for more resident waves
-    const bool deep = p.R <= 128;
-    if (p.split > 1) {
-        if (deep)
-            gemm_stream_kernel<WT, ACT, GROUPED, true, 8><<<(unsigned)blocks, 64, 0, stream>>>(p, nbo);
-        else
-            gemm_stream_kernel<WT, ACT, GROUPED, true, 4><<<(unsigned)blocks, 64, 0, stream>>>(p, nbo);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
-        const int n_out = (ACT == MOE_ACT_SWIGLU) ? p.N / 2 : p.N;
-        const long want = ((long)p.R * n_out + 255) / 256;
-        splitk_reduce_kernel<ACT><<<(unsigned)(want < 16384 ? want : 16384), 256, 0, stream>>>(p);
-    } else if (deep) {
-        gemm_stream_kernel<WT, ACT, GROUPED, false, 8><<<(unsigned)blocks, 64, 0, stream>>>(p, nbo);
-    } else {
-        gemm_stream_kernel<WT, ACT, GROUPED, false, 4><<<(unsigned)blocks, 64, 0, stream>>>(p, nbo);
-    }
+    if (p.R <= 128)
+        gemm_stream_kernel<WT, ACT, GROUPED, 8><<<(unsigned)blocks, threads, lds, stream>>>(p, nbo);
+    else
+        gemm_stream_kernel<WT, ACT, GROUPED, 4><<<(unsigned)blocks, threads, lds, stream>>>(p, nbo);
     return hipGetLastError();
 }
 

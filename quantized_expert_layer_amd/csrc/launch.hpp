@@ -30,10 +30,9 @@ struct GemmParams {
     const uint16_t* scales;
     const float* row_scale;
     uint16_t* out;
-    float* partial;      // split-K partial sums [S][R][N] (stream path, S > 1)
     int R, E, K, N;
     int wtype, group, act;
-    int split;           // S
+    int split;           // stream path: waves per block splitting K (1..MOE_MAX_SPLIT_K)
     int tile;            // enum moe_tile (0 = automatic)
 };
 

@@ -183,11 +183,15 @@ def test_gemm_validation():
     o = q.GemmOpts()
     o.path = 9
     assert g(*_gemm_args(opts=ctypes.byref(o))) == q.MOE_ERR_INVALID
-    o.path, o.split_k = q.PATH_STREAM, 4                               # needs a workspace
-    need = L.moe_gemm_workspace_size(64, 8, 256, 64, 0, 1, ctypes.byref(o))
-    assert need == 4 * 64 * 64 * 4
-    assert g(*_gemm_args(opts=ctypes.byref(o))) == q.MOE_ERR_WORKSPACE
-    assert g(*_gemm_args(opts=ctypes.byref(o), ws=FAKE, wsb=need - 1)) == q.MOE_ERR_WORKSPACE
+    o.path, o.split_k = q.PATH_STREAM, q.MOE_MAX_SPLIT_K + 1            # beyond the limit
+    assert g(*_gemm_args(opts=ctypes.byref(o))) == q.MOE_ERR_INVALID
+    o.split_k = -1
+    assert g(*_gemm_args(opts=ctypes.byref(o))) == q.MOE_ERR_INVALID
+    # the K split happens inside a block: no path needs a workspace
+    for path in (q.PATH_AUTO, q.PATH_STREAM, q.PATH_TILE):
+        for split in (0, 1, q.MOE_MAX_SPLIT_K):
+            o.path, o.split_k = path, split
+            assert L.moe_gemm_workspace_size(64, 8, 256, 64, 0, 1, ctypes.byref(o)) == 0
 
 
 def test_combine_and_dequant_validation():
@@ -206,3 +210,12 @@ def test_valid_calls_report_no_device_without_gpu():
     assert L.moe_route_topk(FAKE, 4, 8, 2, 0, FAKE, FAKE, None) == q.MOE_ERR_NO_DEVICE
     assert L.moe_grouped_gemm_wq(*_gemm_args()) == q.MOE_ERR_NO_DEVICE
     assert L.moe_dequant(FAKE, FAKE, 0, 0, 2, 128, 16, FAKE, None) == q.MOE_ERR_NO_DEVICE
+
+
+def test_binding_limits_match_header():
+    import re
+    text = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                             "include", "moe_wq.h")).read()
+    for name in ("MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SPLIT_K"):
+        m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
+        assert m and int(m.group(1)) == getattr(q, name), name

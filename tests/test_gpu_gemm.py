@@ -104,8 +104,10 @@ def test_grouped_gemm_matches_oracle(E, K, N, wtype, group, T, k, act, path, til
     assert_layer_close(host(out), ref, "grouped gemm")
 
 
-@pytest.mark.parametrize("split", [2, 3, 4, 16])
+@pytest.mark.parametrize("split", [2, 3, 4, 5, 8])
 def test_stream_split_k_matches_oracle_and_unsplit(split):
+    # K = 2048 is 16 int4 super-blocks: splits 3 and 5 leave a short last slice, 8 gives
+    # slices of 2 (shorter than the 8-deep load ring)
     E, K, N = 4, 2048, 256
     codes, scales, off, a = _gemm_case(E, K, N, "int4", 128, 3, 2, seed=split)
     w = dev(q.moe_pack_wq(codes, "int4"))
