@@ -23,7 +23,7 @@ __all__ = [
     "MoEError", "MoELibraryError", "lib", "lib_path", "status_str", "version",
     "moe_route_topk", "moe_permute", "moe_grouped_gemm_wq", "moe_unpermute_combine",
     "moe_dequant", "moe_pack_wq", "moe_packed_bytes", "moe_gemm_workspace_size",
-    "moe_permute_workspace_size", "GemmOpts", "EXPORTED_SYMBOLS",
+    "moe_permute_workspace_size", "GemmOpts", "EXPORTED_SYMBOLS", "new_output",
 ]
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE = 0, -1, -2, -3
@@ -125,6 +125,21 @@ def _check(fn, status):
 
 
 # ---------------------------------------------------------------- tensor marshalling
+# MOE_WQ_POISON=1: outputs (and layer workspaces) the binding allocates start as NaN (floating
+# point) or 0 (integer) instead of whatever the allocator hands back, so an element a kernel
+# failed to write cannot pass a test by holding a previous call's correct value.
+_POISON = os.environ.get("MOE_WQ_POISON", "") not in ("", "0")
+
+
+def new_output(shape, dtype, device):
+    """torch.empty, pre-filled with the poison pattern when MOE_WQ_POISON is set."""
+    torch = _torch()
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if _POISON:
+        t.fill_(float("nan") if t.is_floating_point() else 0)
+    return t
+
+
 def _torch():
     import torch
     return torch
@@ -171,9 +186,9 @@ def moe_route_topk(logits, k, gate_mode, topk_ids=None, topk_w=None, stream=None
     T, E = logits.shape
     gm = GATES.get(gate_mode, gate_mode)
     if topk_ids is None:
-        topk_ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+        topk_ids = new_output((T, k), torch.int32, logits.device)
     if topk_w is None:
-        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+        topk_w = new_output((T, k), torch.float32, logits.device)
     _need(logits, torch.float32, "logits")
     _need(topk_ids, torch.int32, "topk_ids", T * k)
     _need(topk_w, torch.float32, "topk_w", T * k)
@@ -190,11 +205,11 @@ def moe_permute(topk_ids, topk_w, x, E, want_w_perm=True, out=None, stream=None)
     R = T * k
     dev = x.device
     if out is None:
-        out = (torch.empty(R, dtype=torch.int32, device=dev),
-               torch.empty(R, dtype=torch.int32, device=dev),
-               torch.empty(E + 1, dtype=torch.int32, device=dev),
-               torch.empty((R, d), dtype=torch.float16, device=dev),
-               torch.empty(R, dtype=torch.float32, device=dev)
+        out = (new_output(R, torch.int32, dev),
+               new_output(R, torch.int32, dev),
+               new_output(E + 1, torch.int32, dev),
+               new_output((R, d), torch.float16, dev),
+               new_output(R, torch.float32, dev)
                if (want_w_perm and topk_w is not None) else None)
     perm, inv_perm, offsets, x_perm, w_perm = out
     _need(topk_ids, torch.int32, "topk_ids")
@@ -230,7 +245,7 @@ def moe_grouped_gemm_wq(a, expert_offsets, E, K, N, w_packed, scales, wtype, gro
     ac = ACTS.get(act, act)
     n_out = N // 2 if ac == ACT_SWIGLU else N
     if out is None:
-        out = torch.empty((R, n_out), dtype=torch.float16, device=a.device)
+        out = new_output((R, n_out), torch.float16, a.device)
     o = _opts(path, split_k, tile)
     need_ws = lib().moe_gemm_workspace_size(R, E, K, N, wt, ac, ctypes.byref(o) if o else None)
     if need_ws and ws is None:
@@ -253,7 +268,7 @@ def moe_unpermute_combine(y_perm, inv_perm, topk_w, addend, T, k, out=None, stre
     torch = _torch()
     d = y_perm.shape[1]
     if out is None:
-        out = torch.empty((T, d), dtype=torch.float16, device=y_perm.device)
+        out = new_output((T, d), torch.float16, y_perm.device)
     _need(y_perm, torch.float16, "y_perm")
     _need(inv_perm, torch.int32, "inv_perm", T * k)
     _need(topk_w, torch.float32, "topk_w", T * k)
@@ -268,7 +283,7 @@ def moe_unpermute_combine(y_perm, inv_perm, topk_w, addend, T, k, out=None, stre
 def moe_dequant(w_packed, scales, wtype, group_size, E, K, N, out=None, stream=None):
     torch = _torch()
     if out is None:
-        out = torch.empty((E, K, N), dtype=torch.float16, device=w_packed.device)
+        out = new_output((E, K, N), torch.float16, w_packed.device)
     _need(w_packed, torch.uint8, "w_packed")
     _need(scales, torch.float16, "scales")
     _need(out, torch.float16, "w_out", E * K * N)

@@ -250,6 +250,18 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmP
 // extra registers cost more than the longer cover of the next stage's load latency.
 template <int WT> constexpr int tile_kc() { return WT == MOE_W_FP16 ? 64 : 128; }
 
+// Epilogue staging: row stride (halves) of a wave's output region in LDS, padded by 16 bytes
+// so the 16 rows of one fragment store start in different banks.
+template <int ACT, int NS> constexpr int tile_epi_stride() {
+    return (ACT == MOE_ACT_SWIGLU ? NS / 2 : NS) * 16 + 8;
+}
+// LDS of one block: the double-buffered A stages, or the 4 waves' epilogue regions if larger.
+template <int WT, int ACT, int MS, int NS> constexpr int tile_lds_halves() {
+    const int stages = 2 * 16 * MS * tile_kc<WT>();
+    const int epi = 4 * 16 * MS * tile_epi_stride<ACT, NS>();
+    return stages > epi ? stages : epi;
+}
+
 template <int WT, int ACT, bool GROUPED, int MA, int NS, int BM>
 __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__ lds, int e,
                                           int row0, int rows, int cbg) {
@@ -414,16 +426,19 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
             for (int m = 0; m < MA; ++m) acc[m][c] *= sc;
         }
     }
-    const int n_out = SWI ? N / 2 : N;
+    // The results leave through LDS (free once the last stage's barrier has passed): each
+    // wave writes its rows x (NO * 16) tile into a private region, then reads it back row-wise
+    // so every global store writes whole 16-byte pieces of an output row, 8 or 4 lanes per
+    // row back to back -- full cache lines instead of 32-byte pieces of 16 rows.
+    constexpr int RW = NO * 16;                    // output columns of the wave
+    constexpr int RS = tile_epi_stride<ACT, NS>(); // LDS row stride in halves
+    f16* region = lds + wave * (BM * RS);
 #pragma unroll
     for (int m = 0; m < MA; ++m) {
         const int r = m * 16 + lrow;
-        if (r >= rows) continue;
-        const float rs = p.row_scale ? p.row_scale[row0 + r] : 1.0f;
-        uint16_t* orow = p.out + (size_t)(row0 + r) * n_out + q4;
+        const float rs = (p.row_scale && r < rows) ? p.row_scale[row0 + r] : 1.0f;
 #pragma unroll
         for (int c = 0; c < NO; ++c) {
-            if (!ob_ok[c]) continue;
             float v[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -432,8 +447,26 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
                 else v[i] = acc[m][c][i];
                 v[i] *= rs;
             }
-            store4_f16(orow + ob[c] * 16, v[0], v[1], v[2], v[3]);
+            const f16x2 lo = {(f16)v[0], (f16)v[1]}, hi = {(f16)v[2], (f16)v[3]};
+            uint2 w2;
+            w2.x = __builtin_bit_cast(uint32_t, lo);
+            w2.y = __builtin_bit_cast(uint32_t, hi);
+            *(uint2*)(region + r * RS + c * 16 + q4) = w2;
         }
+    }
+    constexpr int LPR = RW / 8;                    // lanes per output row (16 bytes each)
+    constexpr int RPI = kWave / LPR;               // rows per store instruction
+    const int lr = lane / LPR, lc = lane % LPR;
+    const int n_out = SWI ? N / 2 : N;
+    const int ob0 = (cbg * 4 + wave) * NO;         // first output block of the wave
+    const bool col_ok = ob0 + lc / 2 < nbo;
+    uint16_t* obase = p.out + (size_t)row0 * n_out + ob0 * 16 + lc * 8;
+    static_assert(RPI <= BM, "a store pass reads rows inside the wave's region");
+#pragma unroll
+    for (int i = 0; i < (MA * 16 + RPI - 1) / RPI; ++i) {
+        const int r = i * RPI + lr;
+        const u32x4 v = *(const u32x4*)(region + r * RS + lc * 8);
+        if (r < rows && col_ok) *(u32x4*)(obase + (size_t)r * n_out) = v;
     }
 }
 
@@ -441,7 +474,7 @@ template <int WT, int ACT, bool GROUPED, int MS, int NS>
 __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmParams p, int ncbg, int mt_ub,
                                                            int grid_real, int a_major) {
     constexpr int BM = 16 * MS;
-    __shared__ __attribute__((aligned(16))) f16 lds[2 * BM * tile_kc<WT>()];
+    __shared__ __attribute__((aligned(16))) f16 lds[tile_lds_halves<WT, ACT, MS, NS>()];
 
     // XCD-aware order: hardware block b runs on XCD b % 8.  The real tiles (counted from the
     // offsets, not the host's upper bound) are split into 8 equal contiguous ranges, one per

@@ -16,7 +16,7 @@ import ctypes
 
 from . import (ACTS, GATES, WTYPES, MoEError, _ptr, _stream, lib, moe_gemm_workspace_size,
                moe_grouped_gemm_wq, moe_pack_wq, moe_permute, moe_route_topk,
-               moe_unpermute_combine)
+               moe_unpermute_combine, new_output)
 
 
 def _dev(a, device):
@@ -75,29 +75,29 @@ class DeviceLayer:
         dev, R, d = self.device, T * self.k, self.d
         n_h = self.inter
         b = {
-            "ids": torch.empty((T, self.k), dtype=torch.int32, device=dev),
-            "w": torch.empty((T, self.k), dtype=torch.float32, device=dev),
-            "perm": torch.empty(R, dtype=torch.int32, device=dev),
-            "inv": torch.empty(R, dtype=torch.int32, device=dev),
-            "off": torch.empty(self.E + 1, dtype=torch.int32, device=dev),
-            "xp": torch.empty((R, d), dtype=torch.float16, device=dev),
-            "wp": torch.empty(R, dtype=torch.float32, device=dev),
-            "h": torch.empty((R, n_h), dtype=torch.float16, device=dev),
-            "y": torch.empty((R, d), dtype=torch.float16, device=dev),
-            "out": torch.empty((T, d), dtype=torch.float16, device=dev),
+            "ids": new_output((T, self.k), torch.int32, dev),
+            "w": new_output((T, self.k), torch.float32, dev),
+            "perm": new_output(R, torch.int32, dev),
+            "inv": new_output(R, torch.int32, dev),
+            "off": new_output(self.E + 1, torch.int32, dev),
+            "xp": new_output((R, d), torch.float16, dev),
+            "wp": new_output(R, torch.float32, dev),
+            "h": new_output((R, n_h), torch.float16, dev),
+            "y": new_output((R, d), torch.float16, dev),
+            "out": new_output((T, d), torch.float16, dev),
         }
         ws1 = moe_gemm_workspace_size(R, self.E, d, self.n1, self.wtype, self.act, self.gemm_path)
         ws2 = moe_gemm_workspace_size(R, self.E, self.inter, d, self.wtype, "none", self.gemm_path)
         wsz = max(ws1, ws2)
         if self.shared is not None:
             b["sh_off"] = torch.tensor([0, T], dtype=torch.int32, device=dev)
-            b["sh_h"] = torch.empty((T, self.shared_inter), dtype=torch.float16, device=dev)
-            b["sh_y"] = torch.empty((T, d), dtype=torch.float16, device=dev)
+            b["sh_h"] = new_output((T, self.shared_inter), torch.float16, dev)
+            b["sh_y"] = new_output((T, d), torch.float16, dev)
             wsz = max(wsz, moe_gemm_workspace_size(T, 1, d, 2 * self.shared_inter, "fp16",
                                                    "swiglu", self.gemm_path),
                       moe_gemm_workspace_size(T, 1, self.shared_inter, d, "fp16", "none",
                                               self.gemm_path))
-        b["ws"] = torch.empty(max(wsz, 16), dtype=torch.uint8, device=dev)
+        b["ws"] = new_output(max(wsz, 16), torch.uint8, dev)
         return Workspace(T=T, bufs=b)
 
     def forward(self, x, logits, ws: Optional[Workspace] = None, gate_in_gemm: bool = True,
