@@ -6,12 +6,13 @@
 // construction.  The dequantized weight is Algorithm 1's W_dq = code * S.
 //
 // Two paths share the packed layout and the MFMA 16x16x32 fp16 fragment shapes:
-//   stream : 16-row m-tiles, one wave per 16 output columns, A fragments straight from
+//   stream : 16-row m-tiles, one block per 16 output columns, A fragments straight from
 //            global memory, weights streamed once with a deep register prefetch.  Meant for
 //            the few rows per expert of decode / verify (the Specter page's fine-grained
-//            expert kernels); optional split along K with a fixed-order reduction.
-//   tile   : 128-row m-tiles, 4 waves x 64 weight columns, A staged through LDS (double
-//            buffered), weights double buffered in registers.  Meant for large M.
+//            expert kernels); optional K split across the waves of a block, reduced in LDS
+//            in a fixed order.
+//   tile   : 64-row m-tiles, 4 waves x (64 or 32) weight columns, A staged through LDS
+//            (double buffered), weights double buffered in registers.  Meant for large M.
 // Experts with no rows launch no work that reads weights.
 #include <type_traits>
 
