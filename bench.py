@@ -59,6 +59,9 @@ def parse():
                     help="tile-path block tile: 0 auto, 1 64x256, 2 64x128, 3 128x128")
     ap.add_argument("--rotate-gb", type=float, default=1.0,
                     help="cycle weight copies totalling at least this many GB (cold weights)")
+    ap.add_argument("--no-fuse-rows", action="store_true",
+                    help="copy x_perm and run the combine instead of reading and writing rows "
+                         "through perm inside the GEMMs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-graph", action="store_true",
@@ -113,7 +116,8 @@ def main():
     inp = synth.make_inputs(cfg, T, wtype=args.wtype, active=args.active)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    layer = q.DeviceLayer.from_inputs(inp, device=dev, gemm_path=args.path, gemm_tile=args.tile)
+    layer = q.DeviceLayer.from_inputs(inp, device=dev, gemm_path=args.path, gemm_tile=args.tile,
+                                      fuse_rows=not args.no_fuse_rows)
     ws = layer.workspace(T)
     x = torch.from_numpy(inp.x).to(dev)
     logits = torch.from_numpy(inp.logits).to(dev)

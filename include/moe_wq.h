@@ -101,12 +101,14 @@ int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int
  *
  *   topk_ids        int32 [T, k]  expert of flat slot f = t*k + j (values in [0, E))
  *   topk_w          fp32  [T, k]  gate weights, or NULL (then w_perm must be NULL)
- *   x               fp16  [T, d]  token activations
+ *   x               fp16  [T, d]  token activations (may be NULL when x_perm is NULL)
  *   perm            int32 [T*k]   out: perm[p] = flat slot at sorted position p; slots of one
  *                                 expert keep ascending f (stable)
  *   inv_perm        int32 [T*k]   out: inv_perm[f] = sorted position of slot f
  *   expert_offsets  int32 [E+1]   out: rows of expert e are positions offsets[e]..offsets[e+1]-1
- *   x_perm          fp16  [T*k, d] out: x_perm[p] = x[perm[p] / k] (bit copy)
+ *   x_perm          fp16  [T*k, d] out: x_perm[p] = x[perm[p] / k] (bit copy), or NULL to
+ *                                 skip the copy (moe_grouped_gemm_wq_rows then reads x
+ *                                 through perm itself)
  *   w_perm          fp32  [T*k]   out (optional): w_perm[p] = topk_w.flat[perm[p]]
  *   ws, ws_bytes    workspace of at least moe_permute_workspace_size(T, k, E) bytes
  *                   (currently 0: NULL allowed)
@@ -156,6 +158,37 @@ int32_t moe_grouped_gemm_wq(const uint16_t* a, const int32_t* expert_offsets,
                             void* stream);
 size_t moe_gemm_workspace_size(int32_t R, int32_t E, int32_t K, int32_t N, int32_t wtype,
                                int32_t act, const moe_gemm_opts* opts);
+
+/*
+ * moe_grouped_gemm_wq_rows -- moe_grouped_gemm_wq with the permute and the unpermute of
+ * [W] section 3's workflow folded into its loads and stores: GEMM row p (sorted position p,
+ * the rows of expert e being offsets[e] .. offsets[e+1]-1 as above) reads activation row
+ *     a[a_rows[p] / a_row_div]      (a[p] when a_rows is NULL)
+ * and writes output row
+ *     out[out_rows[p]]              (out[p] when out_rows is NULL).
+ * With a = x, a_rows = perm and a_row_div = k this is the first GEMM without x_perm; with
+ * k = 1, out = the layer output and out_rows = perm it is the second GEMM plus the
+ * unpermute (the gate weight goes in row_scale, indexed by p).  Everything else -- weights,
+ * scales, act, row_scale, opts, workspace, numerics -- is as for moe_grouped_gemm_wq.
+ *
+ *   a_nrows      rows of a when a_rows is given (source rows are clamped into [0, a_nrows);
+ *                in-range a_rows are the caller's duty, a clamped row gives a wrong but
+ *                harmless result)
+ *   a_rows       int32 [R] or NULL;  a_row_div >= 1
+ *   out_nrows    rows of out when out_rows is given; a destination outside [0, out_nrows) is
+ *                not written.  Destinations must be distinct (rows are written, not added).
+ *   out_rows     int32 [R] or NULL
+ * Errors: as moe_grouped_gemm_wq, plus MOE_ERR_INVALID for a_row_div < 1, negative row
+ * counts or misaligned (non-4-byte) row maps.
+ */
+int32_t moe_grouped_gemm_wq_rows(const uint16_t* a, int32_t a_nrows, const int32_t* a_rows,
+                                 int32_t a_row_div, const int32_t* expert_offsets, int32_t R,
+                                 int32_t E, int32_t K, int32_t N, const void* w_packed,
+                                 const uint16_t* scales, int32_t wtype, int32_t group_size,
+                                 int32_t act, const float* row_scale, uint16_t* out,
+                                 int32_t out_nrows, const int32_t* out_rows,
+                                 const moe_gemm_opts* opts, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /*
  * moe_unpermute_combine -- [W] section 3 workflow: rows are restored to the original order

@@ -21,7 +21,8 @@ __all__ = [
     "ACT_SWIGLU", "PATH_AUTO", "PATH_STREAM", "PATH_TILE", "TILE_AUTO", "TILE_64x256",
     "TILE_64x128", "TILE_128x128", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SPLIT_K",
     "MoEError", "MoELibraryError", "lib", "lib_path", "status_str", "version",
-    "moe_route_topk", "moe_permute", "moe_grouped_gemm_wq", "moe_unpermute_combine",
+    "moe_route_topk", "moe_permute", "moe_grouped_gemm_wq", "moe_grouped_gemm_wq_rows",
+    "moe_unpermute_combine",
     "moe_dequant", "moe_pack_wq", "moe_packed_bytes", "moe_gemm_workspace_size",
     "moe_permute_workspace_size", "GemmOpts", "EXPORTED_SYMBOLS", "new_output",
 ]
@@ -44,7 +45,7 @@ lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_wq.s
 # Every symbol include/moe_wq.h declares.
 EXPORTED_SYMBOLS = (
     "moe_route_topk", "moe_permute", "moe_permute_workspace_size", "moe_grouped_gemm_wq",
-    "moe_gemm_workspace_size", "moe_unpermute_combine", "moe_dequant", "moe_packed_bytes",
+    "moe_grouped_gemm_wq_rows", "moe_gemm_workspace_size", "moe_unpermute_combine", "moe_dequant", "moe_packed_bytes",
     "moe_pack_wq", "moe_status_str", "moe_version",
 )
 
@@ -95,6 +96,8 @@ def lib():
         "moe_permute_workspace_size": (_SZ, [_I, _I, _I]),
         "moe_grouped_gemm_wq": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _P, _P, _P,
                                      _P, _SZ, _P]),
+        "moe_grouped_gemm_wq_rows": (_I, [_P, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _I, _I,
+                                          _I, _P, _P, _I, _P, _P, _P, _SZ, _P]),
         "moe_gemm_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _P]),
         "moe_unpermute_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
         "moe_dequant": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
@@ -197,8 +200,10 @@ def moe_route_topk(logits, k, gate_mode, topk_ids=None, topk_w=None, stream=None
     return topk_ids, topk_w
 
 
-def moe_permute(topk_ids, topk_w, x, E, want_w_perm=True, out=None, stream=None):
-    """Returns (perm, inv_perm, expert_offsets, x_perm, w_perm or None)."""
+def moe_permute(topk_ids, topk_w, x, E, want_w_perm=True, out=None, stream=None,
+                want_x_perm=True):
+    """Returns (perm, inv_perm, expert_offsets, x_perm or None, w_perm or None).
+    want_x_perm=False skips the row copy (the first GEMM then reads x through perm)."""
     torch = _torch()
     T, k = topk_ids.shape
     d = x.shape[1]
@@ -208,7 +213,7 @@ def moe_permute(topk_ids, topk_w, x, E, want_w_perm=True, out=None, stream=None)
         out = (new_output(R, torch.int32, dev),
                new_output(R, torch.int32, dev),
                new_output(E + 1, torch.int32, dev),
-               new_output((R, d), torch.float16, dev),
+               new_output((R, d), torch.float16, dev) if want_x_perm else None,
                new_output(R, torch.float32, dev)
                if (want_w_perm and topk_w is not None) else None)
     perm, inv_perm, offsets, x_perm, w_perm = out
@@ -261,6 +266,35 @@ def moe_grouped_gemm_wq(a, expert_offsets, E, K, N, w_packed, scales, wtype, gro
         _ptr(a), _ptr(expert_offsets), R, E, K, N, _ptr(w_packed), _ptr(scales), wt,
         int(group_size), ac, _ptr(row_scale), _ptr(out), ctypes.byref(o) if o else None,
         _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return out
+
+
+def moe_grouped_gemm_wq_rows(a, a_rows, a_row_div, expert_offsets, R, E, K, N, w_packed, scales,
+                             wtype, group_size, act, row_scale=None, out=None, out_rows=None,
+                             path=PATH_AUTO, split_k=0, stream=None, tile=TILE_AUTO):
+    """GEMM row p reads a[a_rows[p] // a_row_div] (a[p] if a_rows is None) and writes
+    out[out_rows[p]] (out[p] if out_rows is None); R = number of GEMM rows."""
+    torch = _torch()
+    wt = WTYPES.get(wtype, wtype)
+    ac = ACTS.get(act, act)
+    n_out = N // 2 if ac == ACT_SWIGLU else N
+    if out is None:
+        out = new_output((R, n_out), torch.float16, a.device)
+    o = _opts(path, split_k, tile)
+    a_nrows = a.shape[0]
+    out_nrows = out.shape[0]
+    _need(a, torch.float16, "a", a_nrows * K)
+    _need(a_rows, torch.int32, "a_rows", R)
+    _need(expert_offsets, torch.int32, "expert_offsets", E + 1)
+    _need(w_packed, torch.uint8, "w_packed")
+    _need(scales, torch.float16, "scales")
+    _need(row_scale, torch.float32, "row_scale", R)
+    _need(out, torch.float16, "out", out_nrows * n_out)
+    _need(out_rows, torch.int32, "out_rows", R)
+    _check("moe_grouped_gemm_wq_rows", lib().moe_grouped_gemm_wq_rows(
+        _ptr(a), a_nrows, _ptr(a_rows), int(a_row_div), _ptr(expert_offsets), R, E, K, N,
+        _ptr(w_packed), _ptr(scales), wt, int(group_size), ac, _ptr(row_scale), _ptr(out),
+        out_nrows, _ptr(out_rows), ctypes.byref(o) if o else None, None, 0, _stream(stream)))
     return out
 
 

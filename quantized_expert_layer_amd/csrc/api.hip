@@ -130,10 +130,11 @@ int32_t moe_permute(const int32_t* topk_ids, const float* topk_w, const uint16_t
     const int64_t R = (int64_t)T * k;
     if (R >= (int64_t)1 << 31 || R * (d / 8) >= (int64_t)1 << 32) return MOE_ERR_UNSUPPORTED;
     if (T == 0) return MOE_OK;
-    if (!topk_ids || !x || !perm || !inv_perm || !expert_offsets || !x_perm) return MOE_ERR_INVALID;
+    if (!topk_ids || !perm || !inv_perm || !expert_offsets) return MOE_ERR_INVALID;
+    if (x_perm && !x) return MOE_ERR_INVALID;
     if (w_perm && !topk_w) return MOE_ERR_INVALID;
-    if (!aligned(x, 16) || !aligned(x_perm, 16) || !aligned(topk_ids, 4) || !aligned(perm, 4) ||
-        !aligned(inv_perm, 4) || !aligned(expert_offsets, 4))
+    if ((x_perm && (!aligned(x, 16) || !aligned(x_perm, 16))) || !aligned(topk_ids, 4) ||
+        !aligned(perm, 4) || !aligned(inv_perm, 4) || !aligned(expert_offsets, 4))
         return MOE_ERR_INVALID;
     if ((topk_w && !aligned(topk_w, 4)) || (w_perm && !aligned(w_perm, 4))) return MOE_ERR_INVALID;
     if (int32_t st = check_device()) return st;
@@ -141,6 +142,7 @@ int32_t moe_permute(const int32_t* topk_ids, const float* topk_w, const uint16_t
     hipError_t e = moe::launch_sort(topk_ids, topk_w, (int)R, E, perm, inv_perm, expert_offsets,
                                     w_perm, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
+    if (!x_perm) return MOE_OK;               // the caller gathers inside the first GEMM
     return hip_status(moe::launch_gather(x, perm, (int)R, k, d, x_perm, s));
 }
 
@@ -150,22 +152,34 @@ size_t moe_gemm_workspace_size(int32_t R, int32_t E, int32_t K, int32_t N, int32
     return plan_gemm(R, E, K, N, wtype, act, opts).ws;
 }
 
-int32_t moe_grouped_gemm_wq(const uint16_t* a, const int32_t* expert_offsets, int32_t R,
-                            int32_t E, int32_t K, int32_t N, const void* w_packed,
-                            const uint16_t* scales, int32_t wtype, int32_t group_size,
-                            int32_t act, const float* row_scale, uint16_t* out,
-                            const moe_gemm_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+static int32_t grouped_gemm(const uint16_t* a, int32_t a_nrows, const int32_t* a_rows,
+                            int32_t a_div, const int32_t* expert_offsets, int32_t R, int32_t E,
+                            int32_t K, int32_t N, const void* w_packed, const uint16_t* scales,
+                            int32_t wtype, int32_t group_size, int32_t act,
+                            const float* row_scale, uint16_t* out, int32_t out_nrows,
+                            const int32_t* out_rows, const moe_gemm_opts* opts, void* ws,
+                            size_t ws_bytes, void* stream) {
     if (int32_t st = validate_gemm(a, expert_offsets, R, E, K, N, w_packed, scales, wtype,
                                    group_size, act, out, opts))
         return st;
+    if (a_rows && (a_div < 1 || a_nrows < 1)) return MOE_ERR_INVALID;
+    if (out_rows && out_nrows < 0) return MOE_ERR_INVALID;
+    if ((int64_t)a_nrows * K >= (int64_t)1 << 40) return MOE_ERR_UNSUPPORTED;
     if (R == 0) return MOE_OK;
     if (row_scale && !aligned(row_scale, 4)) return MOE_ERR_INVALID;
+    if ((a_rows && !aligned(a_rows, 4)) || (out_rows && !aligned(out_rows, 4)))
+        return MOE_ERR_INVALID;
     const GemmPlan pl = plan_gemm(R, E, K, N, wtype, act, opts);
     if (pl.ws > 0 && (!ws || ws_bytes < pl.ws || !aligned(ws, 16))) return MOE_ERR_WORKSPACE;
     if (int32_t st = check_device()) return st;
 
     moe::GemmParams p;
     p.a = a;
+    p.a_rows = a_rows;
+    p.a_div = a_rows ? a_div : 1;
+    p.a_nrows = a_rows ? a_nrows : R;
+    p.out_rows = out_rows;
+    p.out_nrows = out_rows ? out_nrows : R;
     p.offsets = expert_offsets;
     p.w = w_packed;
     p.scales = scales;
@@ -183,6 +197,29 @@ int32_t moe_grouped_gemm_wq(const uint16_t* a, const int32_t* expert_offsets, in
     hipStream_t s = (hipStream_t)stream;
     return hip_status(pl.path == MOE_PATH_TILE ? moe::launch_gemm_tile(p, s)
                                                : moe::launch_gemm_stream(p, s));
+}
+
+int32_t moe_grouped_gemm_wq(const uint16_t* a, const int32_t* expert_offsets, int32_t R,
+                            int32_t E, int32_t K, int32_t N, const void* w_packed,
+                            const uint16_t* scales, int32_t wtype, int32_t group_size,
+                            int32_t act, const float* row_scale, uint16_t* out,
+                            const moe_gemm_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+    return grouped_gemm(a, R, nullptr, 1, expert_offsets, R, E, K, N, w_packed, scales, wtype,
+                        group_size, act, row_scale, out, R, nullptr, opts, ws, ws_bytes, stream);
+}
+
+int32_t moe_grouped_gemm_wq_rows(const uint16_t* a, int32_t a_nrows, const int32_t* a_rows,
+                                 int32_t a_row_div, const int32_t* expert_offsets, int32_t R,
+                                 int32_t E, int32_t K, int32_t N, const void* w_packed,
+                                 const uint16_t* scales, int32_t wtype, int32_t group_size,
+                                 int32_t act, const float* row_scale, uint16_t* out,
+                                 int32_t out_nrows, const int32_t* out_rows,
+                                 const moe_gemm_opts* opts, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    if (a_nrows < 0 || out_nrows < 0) return MOE_ERR_INVALID;
+    return grouped_gemm(a, a_rows ? a_nrows : R, a_rows, a_row_div, expert_offsets, R, E, K, N,
+                        w_packed, scales, wtype, group_size, act, row_scale, out,
+                        out_rows ? out_nrows : R, out_rows, opts, ws, ws_bytes, stream);
 }
 
 int32_t moe_unpermute_combine(const uint16_t* y_perm, const int32_t* inv_perm, const float* topk_w,

@@ -64,6 +64,19 @@ __device__ __forceinline__ f32x4 load4_scale(const uint16_t* src) {
     return f32x4{(float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]};
 }
 
+// Row maps of a GEMM call: the A row read for GEMM row p (a gather fused into the load) and
+// the output row written for it (a scatter fused into the store).  Source rows are clamped
+// into a; a destination outside out is skipped (-1).
+__device__ __forceinline__ int a_source_row(const GemmParams& p, int gp) {
+    if (!p.a_rows) return gp;
+    return min(max(p.a_rows[gp] / p.a_div, 0), p.a_nrows - 1);
+}
+__device__ __forceinline__ int out_dest_row(const GemmParams& p, int gp) {
+    if (!p.out_rows) return gp;
+    const int d = p.out_rows[gp];
+    return (d >= 0 && d < p.out_nrows) ? d : -1;
+}
+
 // ------------------------------------------------------------------------------------
 // Stream path.
 //   grid  = m-tiles(upper bound) x NBo blocks of S waves (S = p.split, 1..MOE_MAX_SPLIT_K).
@@ -116,7 +129,8 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmP
     // A fragment source: row (lane & 15) of the tile, 8 halves at k = 8 * (lane >> 4).
     const int arow = lane & 15;
     const bool arow_ok = arow < rows;
-    const f16x8* ap = (const f16x8*)(p.a + (size_t)(row0 + (arow_ok ? arow : 0)) * K) + (lane >> 4);
+    const int asrc = a_source_row(p, row0 + (arow_ok ? arow : 0));
+    const f16x8* ap = (const f16x8*)(p.a + (size_t)asrc * K) + (lane >> 4);
 
     f32x4 acc[NCB];
 #pragma unroll
@@ -227,7 +241,8 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmP
         else if constexpr (ACT == MOE_ACT_RELU) v = fmaxf(acc[0][i], 0.0f);
         else v = acc[0][i];
         if (p.row_scale) v *= p.row_scale[row0 + r];
-        ocol[(size_t)(row0 + r) * n_out] = f32_to_f16_bits(v);
+        const int dst = out_dest_row(p, row0 + r);
+        if (dst >= 0) ocol[(size_t)dst * n_out] = f32_to_f16_bits(v);
     }
 }
 
@@ -311,7 +326,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
     for (int i = 0; i < ACH; ++i) {
         const int q = min((int)threadIdx.x + 256 * i, ATOT - 1);
         const int r = q / CPR, c = q % CPR;
-        asrc[i] = (const u32x4*)(p.a + (size_t)(row0 + min(r, rows - 1)) * K) + c;
+        asrc[i] = (const u32x4*)(p.a + (size_t)a_source_row(p, row0 + min(r, rows - 1)) * K) + c;
         adst[i] = r * KC + ((c ^ (r & (CPR - 1))) * 8);
     }
     u32x4 areg[ACH];
@@ -461,13 +476,16 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
     const int n_out = SWI ? N / 2 : N;
     const int ob0 = (cbg * 4 + wave) * NO;         // first output block of the wave
     const bool col_ok = ob0 + lc / 2 < nbo;
-    uint16_t* obase = p.out + (size_t)row0 * n_out + ob0 * 16 + lc * 8;
+    uint16_t* obase = p.out + ob0 * 16 + lc * 8;
     static_assert(RPI <= BM, "a store pass reads rows inside the wave's region");
 #pragma unroll
     for (int i = 0; i < (MA * 16 + RPI - 1) / RPI; ++i) {
         const int r = i * RPI + lr;
         const u32x4 v = *(const u32x4*)(region + r * RS + lc * 8);
-        if (r < rows && col_ok) *(u32x4*)(obase + (size_t)r * n_out) = v;
+        if (r < rows && col_ok) {
+            const int dst = out_dest_row(p, row0 + r);
+            if (dst >= 0) *(u32x4*)(obase + (size_t)dst * n_out) = v;
+        }
     }
 }
 

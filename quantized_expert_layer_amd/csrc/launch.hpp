@@ -25,6 +25,10 @@ hipError_t launch_dequant(const void* w, const uint16_t* scales, int wtype, int 
 
 struct GemmParams {
     const uint16_t* a;
+    const int32_t* a_rows;   // NULL: GEMM row p reads a[p]; else a[a_rows[p] / a_div]
+    int a_div, a_nrows;      // divisor of a_rows, rows of a (source rows are clamped into it)
+    const int32_t* out_rows; // NULL: GEMM row p writes out[p]; else out[out_rows[p]]
+    int out_nrows;           // rows of out (other destinations are not written)
     const int32_t* offsets;
     const void* w;
     const uint16_t* scales;

@@ -15,8 +15,8 @@ import numpy as np
 import ctypes
 
 from . import (ACTS, GATES, WTYPES, MoEError, _ptr, _stream, lib, moe_gemm_workspace_size,
-               moe_grouped_gemm_wq, moe_pack_wq, moe_permute, moe_route_topk,
-               moe_unpermute_combine, new_output)
+               moe_grouped_gemm_wq, moe_grouped_gemm_wq_rows, moe_pack_wq, moe_permute,
+               moe_route_topk, moe_unpermute_combine, new_output)
 
 
 def _dev(a, device):
@@ -35,7 +35,8 @@ class DeviceLayer:
     def __init__(self, *, E: int, k: int, d: int, inter: int, act: str, wtype: str, group: int,
                  gate_mode: str, codes1: np.ndarray, scales1: np.ndarray, codes2: np.ndarray,
                  scales2: np.ndarray, shared: Optional[List[Tuple[np.ndarray, np.ndarray]]] = None,
-                 device: str = "cuda", gemm_path: int = 0, gemm_tile: int = 0):
+                 device: str = "cuda", gemm_path: int = 0, gemm_tile: int = 0,
+                 fuse_rows: bool = True):
         import torch
         self.E, self.k, self.d, self.inter = E, k, d, inter
         self.act, self.wtype, self.group, self.gate_mode = act, wtype, group, gate_mode
@@ -43,6 +44,9 @@ class DeviceLayer:
         self.device = torch.device(device)
         self.gemm_path = gemm_path
         self.gemm_tile = gemm_tile
+        # fuse_rows: the first GEMM reads x through perm (no x_perm copy), and with k = 1 the
+        # second GEMM writes the output rows through perm (no combine launch)
+        self.fuse_rows = fuse_rows
         self.w1 = _dev(moe_pack_wq(codes1, wtype), self.device)
         self.w2 = _dev(moe_pack_wq(codes2, wtype), self.device)
         self.s1 = _dev(scales1.astype(np.float16), self.device)
@@ -62,13 +66,18 @@ class DeviceLayer:
                            _dev(moe_pack_wq(sw2.astype(np.float16), "fp16"), self.device))
 
     @classmethod
-    def from_inputs(cls, inp, device="cuda", gemm_path=0, gemm_tile=0):
+    def from_inputs(cls, inp, device="cuda", gemm_path=0, gemm_tile=0, fuse_rows=True):
         c = inp.cfg
         return cls(E=c.E, k=c.k, d=c.d, inter=c.inter, act=c.act, wtype=inp.wtype,
                    group=c.group, gate_mode=c.gate_mode, codes1=inp.codes1,
                    scales1=inp.scales1, codes2=inp.codes2, scales2=inp.scales2,
                    shared=inp.shared or None, device=device, gemm_path=gemm_path,
-                   gemm_tile=gemm_tile)
+                   gemm_tile=gemm_tile, fuse_rows=fuse_rows)
+
+    def _scatter_out(self, gate_in_gemm: bool) -> bool:
+        """Whether the second GEMM writes the layer output itself: one expert per token, the
+        gate weight applied in the GEMM and nothing to add."""
+        return self.fuse_rows and self.k == 1 and gate_in_gemm and self.shared is None
 
     def workspace(self, T: int) -> Workspace:
         import torch
@@ -109,14 +118,29 @@ class DeviceLayer:
         b = ws.bufs
         path = self.gemm_path
         moe_route_topk(logits, self.k, self.gate_mode, b["ids"], b["w"], stream=stream)
+        fused = self.fuse_rows
+        scatter = self._scatter_out(gate_in_gemm)
+        R = T * self.k
         moe_permute(b["ids"], b["w"], x, self.E,
-                    out=(b["perm"], b["inv"], b["off"], b["xp"], b["wp"]), stream=stream)
-        moe_grouped_gemm_wq(b["xp"], b["off"], self.E, self.d, self.n1, self.w1, self.s1,
-                            self.wtype, self.group, self.act, out=b["h"], path=path,
-                            ws=b["ws"], stream=stream, tile=self.gemm_tile)
+                    out=(b["perm"], b["inv"], b["off"], None if fused else b["xp"], b["wp"]),
+                    stream=stream)
+        if fused:
+            moe_grouped_gemm_wq_rows(x, b["perm"], self.k, b["off"], R, self.E, self.d, self.n1,
+                                     self.w1, self.s1, self.wtype, self.group, self.act,
+                                     out=b["h"], path=path, stream=stream, tile=self.gemm_tile)
+        else:
+            moe_grouped_gemm_wq(b["xp"], b["off"], self.E, self.d, self.n1, self.w1, self.s1,
+                                self.wtype, self.group, self.act, out=b["h"], path=path,
+                                ws=b["ws"], stream=stream, tile=self.gemm_tile)
+        rs = b["wp"] if gate_in_gemm else None
+        if scatter:
+            moe_grouped_gemm_wq_rows(b["h"], None, 1, b["off"], R, self.E, self.inter, self.d,
+                                     self.w2, self.s2, self.wtype, self.group, "none",
+                                     row_scale=rs, out=b["out"], out_rows=b["perm"], path=path,
+                                     stream=stream, tile=self.gemm_tile)
+            return b["out"]
         moe_grouped_gemm_wq(b["h"], b["off"], self.E, self.inter, self.d, self.w2, self.s2,
-                            self.wtype, self.group, "none",
-                            row_scale=b["wp"] if gate_in_gemm else None, out=b["y"],
+                            self.wtype, self.group, "none", row_scale=rs, out=b["y"],
                             path=path, ws=b["ws"], stream=stream, tile=self.gemm_tile)
         addend = None
         if self.shared is not None:
@@ -150,22 +174,38 @@ class DeviceLayer:
         ob = ctypes.byref(opts) if opts is not None else None
         wsp, wsn = _ptr(b["ws"]), b["ws"].numel()
         wt, ac = WTYPES[self.wtype], ACTS[self.act]
+        fused = self.fuse_rows
+        scatter = self._scatter_out(gate_in_gemm)
+        R = T * self.k
+        rs = _ptr(b["wp"]) if gate_in_gemm else None
         calls = [
             ("route", L.moe_route_topk, (_ptr(logits), T, self.E, self.k, GATES[self.gate_mode],
                                          _ptr(b["ids"]), _ptr(b["w"]), st)),
             ("permute", L.moe_permute, (_ptr(b["ids"]), _ptr(b["w"]), _ptr(x), T, self.k, self.E,
                                         self.d, _ptr(b["perm"]), _ptr(b["inv"]), _ptr(b["off"]),
-                                        _ptr(b["xp"]), _ptr(b["wp"]), None, 0, st)),
-            ("gemm1", L.moe_grouped_gemm_wq, (_ptr(b["xp"]), _ptr(b["off"]), T * self.k, self.E,
-                                              self.d, self.n1, _ptr(w1), _ptr(self.s1), wt,
-                                              self.group, ac, None, _ptr(b["h"]), ob, wsp, wsn,
-                                              st)),
-            ("gemm2", L.moe_grouped_gemm_wq, (_ptr(b["h"]), _ptr(b["off"]), T * self.k, self.E,
-                                              self.inter, self.d, _ptr(w2), _ptr(self.s2), wt,
-                                              self.group, 0,
-                                              _ptr(b["wp"]) if gate_in_gemm else None,
-                                              _ptr(b["y"]), ob, wsp, wsn, st)),
+                                        None if fused else _ptr(b["xp"]), _ptr(b["wp"]), None, 0,
+                                        st)),
         ]
+        if fused:
+            calls.append(("gemm1", L.moe_grouped_gemm_wq_rows,
+                          (_ptr(x), T, _ptr(b["perm"]), self.k, _ptr(b["off"]), R, self.E, self.d,
+                           self.n1, _ptr(w1), _ptr(self.s1), wt, self.group, ac, None,
+                           _ptr(b["h"]), R, None, ob, wsp, wsn, st)))
+        else:
+            calls.append(("gemm1", L.moe_grouped_gemm_wq,
+                          (_ptr(b["xp"]), _ptr(b["off"]), R, self.E, self.d, self.n1, _ptr(w1),
+                           _ptr(self.s1), wt, self.group, ac, None, _ptr(b["h"]), ob, wsp, wsn,
+                           st)))
+        if scatter:
+            calls.append(("gemm2", L.moe_grouped_gemm_wq_rows,
+                          (_ptr(b["h"]), R, None, 1, _ptr(b["off"]), R, self.E, self.inter, self.d,
+                           _ptr(w2), _ptr(self.s2), wt, self.group, 0, rs, _ptr(b["out"]), T,
+                           _ptr(b["perm"]), ob, wsp, wsn, st)))
+            return LayerPlan(calls, b["out"], keep=(opts, x, logits, w1, w2, self.s1, self.s2,
+                                                    self.shared, ws))
+        calls.append(("gemm2", L.moe_grouped_gemm_wq,
+                      (_ptr(b["h"]), _ptr(b["off"]), R, self.E, self.inter, self.d, _ptr(w2),
+                       _ptr(self.s2), wt, self.group, 0, rs, _ptr(b["y"]), ob, wsp, wsn, st)))
         addend = None
         if self.shared is not None:
             calls += [

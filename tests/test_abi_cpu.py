@@ -155,6 +155,8 @@ def test_permute_validation():
     assert L.moe_permute(*args(w=None)) == q.MOE_ERR_INVALID          # w_perm needs topk_w
     assert L.moe_permute(*args(perm=None)) == q.MOE_ERR_INVALID
     assert L.moe_permute(*args(T=0, ids=None, x=None)) == q.MOE_OK
+    assert L.moe_permute(*args(x=None)) == q.MOE_ERR_INVALID          # x_perm needs x
+    assert L.moe_permute(*args(x=None, xp=None, T=0)) == q.MOE_OK      # x may go with x_perm
 
 
 def _gemm_args(**kw):
@@ -219,3 +221,29 @@ def test_binding_limits_match_header():
     for name in ("MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SPLIT_K"):
         m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == getattr(q, name), name
+
+
+def test_gemm_rows_validation():
+    L = q.lib()
+    g = L.moe_grouped_gemm_wq_rows
+
+    def args(**kw):
+        d = dict(a=FAKE, an=64, ar=FAKE, div=2, off=FAKE, R=64, E=8, K=256, N=64, w=FAKE, s=FAKE,
+                 wt=0, g=128, act=1, rs=None, out=FAKE, on=64, orows=None, opts=None, ws=None,
+                 wsb=0, stream=None)
+        d.update(kw)
+        return [d[n] for n in ("a", "an", "ar", "div", "off", "R", "E", "K", "N", "w", "s", "wt",
+                               "g", "act", "rs", "out", "on", "orows", "opts", "ws", "wsb",
+                               "stream")]
+
+    assert g(*args(div=0)) == q.MOE_ERR_INVALID
+    assert g(*args(an=-1)) == q.MOE_ERR_INVALID
+    assert g(*args(on=-1)) == q.MOE_ERR_INVALID
+    assert g(*args(ar=MIS)) == q.MOE_ERR_INVALID
+    assert g(*args(ar=None, orows=MIS)) == q.MOE_ERR_INVALID
+    assert g(*args(an=0)) == q.MOE_ERR_INVALID                          # a_rows needs rows of a
+    assert g(*args(K=200)) == q.MOE_ERR_UNSUPPORTED                    # the plain checks apply
+    assert g(*args(R=0, a=None, out=None, ar=None)) == q.MOE_OK
+    if not gpu_available():
+        assert g(*args()) == q.MOE_ERR_NO_DEVICE
+        assert g(*args(ar=None, div=0, orows=FAKE)) == q.MOE_ERR_NO_DEVICE   # div unused

@@ -166,3 +166,50 @@ def test_gemm_rows_beyond_offsets_are_untouched():
     q.moe_grouped_gemm_wq(dev(a), dev(off), E, K, N, dev(q.moe_pack_wq(codes, "int4")),
                           dev(scales), "int4", 0, "relu", out=out)
     assert (host(out)[12:] == 7.0).all()
+
+
+@pytest.mark.parametrize("path,tile", PATHS)
+@pytest.mark.parametrize("act", ["relu", "swiglu"])
+def test_row_mapped_gemm_gathers_and_scatters(path, tile, act):
+    """moe_grouped_gemm_wq_rows: row p reads a[a_rows[p] // div] and writes out[out_rows[p]]
+    ([W] section 3 workflow's permute and unpermute folded into the GEMM's loads and stores)."""
+    import torch
+    E, K, N, T, k = 12, 512, 256, 150, 3
+    codes, scales, off, _ = _gemm_case(E, K, N, "int4", 128, T, k, seed=77)
+    R = T * k
+    rng = np.random.default_rng(78)
+    x = rng.standard_normal((T, K)).astype(np.float16)
+    ids = synth.gen.random_ids(T, k, E, seed=77, skew=True)
+    perm, _, off = oracle.stable_expert_sort(ids, E)
+    rs = rng.random(R, dtype=np.float32)
+    wdq = oracle.dequant_algorithm1(codes, scales, 128)
+    ref = oracle.grouped_gemm(oracle.permute_rows(x, perm, k), off, wdq, act, row_scale=rs)
+    w = dev(q.moe_pack_wq(codes, "int4"))
+    case(f"row-mapped gemm gather path={path} tile={tile} act={act}")
+    got = host(q.moe_grouped_gemm_wq_rows(dev(x), dev(perm.astype(np.int32)), k, dev(off), R, E,
+                                          K, N, w, dev(scales), "int4", 128, act,
+                                          row_scale=dev(rs), path=path, tile=tile))
+    assert_layer_close(got, ref, "gathered rows")
+    # scatter: a is already permuted, the destinations are a permutation of R rows
+    dst = rng.permutation(R).astype(np.int32)
+    n_out = N // 2 if act == "swiglu" else N
+    out = torch.full((R, n_out), float("nan"), dtype=torch.float16, device="cuda")
+    case(f"row-mapped gemm scatter path={path} tile={tile} act={act}")
+    q.moe_grouped_gemm_wq_rows(dev(oracle.permute_rows(x, perm, k)), None, 1, dev(off), R, E, K,
+                               N, w, dev(scales), "int4", 128, act, row_scale=dev(rs), out=out,
+                               out_rows=dev(dst), path=path, tile=tile)
+    got = host(out)
+    assert_layer_close(got[dst], ref, "scattered rows")
+    # destinations outside out are skipped, the rest still land
+    dst2 = dst.copy()
+    dst2[::7] = -1
+    dst2[1::7] = R + 5
+    out2 = torch.full((R, n_out), float("nan"), dtype=torch.float16, device="cuda")
+    q.moe_grouped_gemm_wq_rows(dev(oracle.permute_rows(x, perm, k)), None, 1, dev(off), R, E, K,
+                               N, w, dev(scales), "int4", 128, act, row_scale=dev(rs), out=out2,
+                               out_rows=dev(dst2), path=path, tile=tile)
+    got2 = host(out2)
+    keep = (dst2 >= 0) & (dst2 < R)
+    assert_layer_close(got2[dst2[keep]], ref[keep], "scattered rows with skips")
+    untouched = np.setdiff1d(np.arange(R), dst2[keep])
+    assert np.isnan(got2[untouched].astype(np.float64)).all()

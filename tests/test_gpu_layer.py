@@ -65,10 +65,30 @@ def test_layer_paths_and_gate_placement_agree(name, T):
     for path in (q.PATH_STREAM, q.PATH_TILE):
         inp, layer = _layer(name, T, path=path)
         ref = oracle.moe_layer(inp)
-        for gate_in_gemm in (True, False):
-            case(f"layer {name} T={T} path={path} gate_in_gemm={gate_in_gemm}")
-            out = host(layer.forward(dev(inp.x), dev(inp.logits), gate_in_gemm=gate_in_gemm))
-            assert_layer_close(out, ref, f"path {path} gate_in_gemm {gate_in_gemm}")
+        for fuse in (True, False):
+            layer.fuse_rows = fuse
+            for gate_in_gemm in (True, False):
+                case(f"layer {name} T={T} path={path} fuse_rows={fuse} gate_in_gemm={gate_in_gemm}")
+                out = host(layer.forward(dev(inp.x), dev(inp.logits), gate_in_gemm=gate_in_gemm))
+                assert_layer_close(out, ref, f"path {path} fuse {fuse} gate_in_gemm {gate_in_gemm}")
+        layer.fuse_rows = True
+
+
+@pytest.mark.parametrize("fuse", [True, False])
+def test_layer_row_fusion_is_bit_identical_to_the_copies(fuse):
+    """Gathering x through perm inside the first GEMM, and (k = 1) writing the output through
+    perm from the second, computes exactly what x_perm + combine compute."""
+    name, T = "mt_encoder", 3840
+    inp, layer = _layer(name, T)
+    x, L = dev(inp.x), dev(inp.logits)
+    layer.fuse_rows = False
+    case(f"row fusion reference {name} T={T}")
+    want = host(layer.forward(x, L)).copy()
+    layer.fuse_rows = fuse
+    case(f"row fusion {fuse} {name} T={T}")
+    got = host(layer.forward(x, L))
+    layer.fuse_rows = True
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
 
 
 @pytest.mark.parametrize("name,T", [("qwen15_moe", 544), ("mt_encoder", 3840), ("phi35_moe", 17)])
