@@ -287,6 +287,9 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
     constexpr int KSPS = KSB / 32;                   // K-steps per super-block
     constexpr int SBPS = KC / KSB;                   // super-blocks per stage per column block
     constexpr int CPR = KC / 8;                      // 16-byte chunks per LDS row
+    // the fragment reads below XOR with (lane row & (CPR - 1)), which equals the staged row's
+    // (r & (CPR - 1)) only while CPR divides 16
+    static_assert(CPR <= 16, "A swizzle assumes at most 16 chunks per LDS row");
     constexpr int ATOT = MA * 16 * CPR;              // A chunks per stage
     constexpr int ACH = (ATOT + 255) / 256;          // A chunks per thread per stage
     constexpr int LDS_BUF = BM * KC;                 // halves per buffer
