@@ -164,8 +164,8 @@ def main():
     counts = np.diff(off)
     active = int((counts > 0).sum())
     R = T * cfg.k
-    per_expert_w1 = layer.w1.numel() // cfg.E + 2 * inp.scales1[0].size
-    per_expert_w2 = layer.w2.numel() // cfg.E + 2 * inp.scales2[0].size
+    per_expert_w1 = layer.w1.numel() // cfg.E + (0 if inp.scales1 is None else 2 * inp.scales1[0].size)
+    per_expert_w2 = layer.w2.numel() // cfg.E + (0 if inp.scales2 is None else 2 * inp.scales2[0].size)
     g1 = {"flops": 2.0 * R * cfg.d * layer.n1, "bytes": active * per_expert_w1}
     g2 = {"flops": 2.0 * R * cfg.inter * cfg.d, "bytes": active * per_expert_w2}
     dom_name, dom = max((("gemm1", g1), ("gemm2", g2)), key=lambda kv: stage_us[kv[0]])

@@ -204,8 +204,13 @@ def moe_layer_tokens(inp, tokens, gate_mode=None, act=None):
     x = inp.x[tokens]
     out = np.zeros((tokens.size, cfg.d), dtype=np.float64)
     for e in np.unique(ids):
-        w1 = dequant_algorithm1(inp.codes1[e:e + 1], inp.scales1[e:e + 1], cfg.group)[0]
-        w2 = dequant_algorithm1(inp.codes2[e:e + 1], inp.scales2[e:e + 1], cfg.group)[0]
+        if inp.wtype == "fp16":
+            # unquantized experts (the FP16 baseline of [W] section 4's quantized-vs-FP16
+            # comparison): the weights are used as they are
+            w1, w2 = dense_weights(inp.codes1[e]), dense_weights(inp.codes2[e])
+        else:
+            w1 = dequant_algorithm1(inp.codes1[e:e + 1], inp.scales1[e:e + 1], cfg.group)[0]
+            w2 = dequant_algorithm1(inp.codes2[e:e + 1], inp.scales2[e:e + 1], cfg.group)[0]
         rows, slots = np.nonzero(ids == e)
         y = expert_ffn(x[rows], w1, w2, act)
         out[rows] += w[rows, slots][:, None] * y

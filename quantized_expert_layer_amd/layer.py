@@ -49,10 +49,11 @@ class DeviceLayer:
         self.fuse_rows = fuse_rows
         self.w1 = _dev(moe_pack_wq(codes1, wtype), self.device)
         self.w2 = _dev(moe_pack_wq(codes2, wtype), self.device)
-        self.s1 = _dev(scales1.astype(np.float16), self.device)
-        self.s2 = _dev(scales2.astype(np.float16), self.device)
+        # fp16 experts (wtype "fp16") carry no scales
+        self.s1 = None if scales1 is None else _dev(scales1.astype(np.float16), self.device)
+        self.s2 = None if scales2 is None else _dev(scales2.astype(np.float16), self.device)
         self.weight_bytes_per_expert = (self.w1.numel() + self.w2.numel()) // E + \
-            2 * (scales1[0].size + scales2[0].size)
+            (0 if scales1 is None else 2 * (scales1[0].size + scales2[0].size))
         self.shared = None
         if shared:
             # n always-on SwiGLU experts summed = one expert whose intermediate columns are

@@ -26,6 +26,7 @@ class LayerConfig:
     k: int               # experts per token
     act: str             # "relu" | "swiglu"
     wtypes: Tuple[str, ...]   # weight code types built for this layer: "int4" | "int8"
+                              # (make_inputs also takes "fp16": unquantized experts)
     group: int           # 0 = per output channel, scales (E,1,N); 128 = groups along K
     gate_mode: str       # "topk" = softmax over the k chosen; "all" = softmax over all E
     zipf_bias: bool      # add the per-expert Zipf(1.1) log-bias to the logits

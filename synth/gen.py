@@ -1,9 +1,12 @@
 """Seeded input generator for the MoE expert layer.
 
 Every array is a pure function of (config, T, weight type, active-expert count,
-coverage flag): a numpy PCG64 stream seeded by
-SeedSequence([cfg_id, variant_id, T, 20261202]) with one spawned child stream per
-tensor.  Value distributions follow the layer shapes being modelled:
+coverage flag), drawn from numpy PCG64 streams spawned from two seed sequences: the
+routing inputs (logits, Zipf permutation, x) from SeedSequence([cfg_id, 10 * A, T,
+20261202]), the layer weights from SeedSequence([cfg_id, 10000 * coverage + 1, 20261202])
+with one child stream per weight matrix and expert.  So the weights are the same layer for
+every T, and int4, int8 and fp16 experts are one normal draw quantized (or kept) three
+ways under the same routing.  Value distributions follow the layer shapes being modelled:
 
   * x ~ fp16(N(0, 1)), gate logits ~ fp32(N(0, 1));
   * optional skew: logit bias b_e = ln p_{pi(e)}, p_r proportional to r^-1.1
@@ -16,6 +19,7 @@ tensor.  Value distributions follow the layer shapes being modelled:
     as in "Who Says Elephants Can't Run" section 3, or per 128-row group along K, shape
     (E,K/128,N), the GPTQ group size the Specter page uses.  Turning codes back into
     weights is the layer's job and does not happen here;
+  * weight type "fp16": the unquantized baseline, fp16 of the same draw, no scales;
   * shared experts (always on, fp16): fp16(N(0, 0.02^2)).
 
 A "coverage" variant replaces the weight draw by codes uniform over the full code
@@ -32,7 +36,7 @@ from .configs import LayerConfig
 
 SEED_TAG = 20261202
 QMAX = {"int4": 7, "int8": 127}
-WTYPE_ID = {"int4": 0, "int8": 1}
+WTYPE_ID = {"int4": 0, "int8": 1, "fp16": 2}
 
 
 @dataclass
@@ -46,9 +50,10 @@ class LayerInputs:
     x: np.ndarray            # fp16 [T, d]
     logits: np.ndarray       # fp32 [T, E]
     codes1: np.ndarray       # int8 [E, d, N1]   N1 = F (ReLU) or 2I, columns [gate | up]
-    scales1: np.ndarray      # fp16 [E, G1, N1]  G1 = 1 (per channel) or d/128
+    scales1: Optional[np.ndarray]  # fp16 [E, G1, N1]  G1 = 1 (per channel) or d/128
     codes2: np.ndarray       # int8 [E, F or I, d]
-    scales2: np.ndarray      # fp16 [E, G2, d]
+    scales2: Optional[np.ndarray]  # fp16 [E, G2, d]
+    # wtype "fp16": codes1 / codes2 are the fp16 weights themselves and the scales are None
     # per shared expert: (w1 fp16 [d, 2*Is] with columns [gate | up], w2 fp16 [Is, d])
     shared: List[Tuple[np.ndarray, np.ndarray]] = field(default_factory=list)
 
@@ -84,13 +89,18 @@ def _rtn_codes(w: np.ndarray, qmax: int, group: int) -> Tuple[np.ndarray, np.nda
 
 
 def _expert_mats(rngs, E, K, N, qmax, group, coverage):
+    """Codes int8 [E, K, N] and fp16 scales [E, G, N]; qmax None: the fp16 weights themselves
+    (same draw, unquantized) and scales None."""
     G = 1 if group == 0 else K // group
-    codes = np.empty((E, K, N), dtype=np.int8)
-    scales = np.empty((E, G, N), dtype=np.float16)
+    fp16 = qmax is None
+    codes = np.empty((E, K, N), dtype=np.float16 if fp16 else np.int8)
+    scales = None if fp16 else np.empty((E, G, N), dtype=np.float16)
 
     def one(e):
         rng = rngs[e]
-        if coverage:
+        if fp16:
+            codes[e] = (rng.standard_normal((K, N), dtype=np.float32) * np.float32(0.02)).astype(np.float16)
+        elif coverage:
             codes[e] = rng.integers(-qmax - 1, qmax + 1, size=(K, N), dtype=np.int8)
             scales[e] = rng.uniform(2.0 ** -8, 2.0 ** -4, size=(G, N)).astype(np.float16)
         else:
@@ -116,10 +126,17 @@ def make_inputs(cfg: LayerConfig, T: int, wtype: Optional[str] = None, active: i
     with_weights=False skips the weight draw (routing-only tests).
     """
     wtype = wtype or cfg.wtypes[0]
-    variant_id = WTYPE_ID[wtype] + 10 * active + 10000 * int(coverage)
-    seed = (cfg.cfg_id, variant_id, T, SEED_TAG)
-    ss = np.random.SeedSequence(list(seed))
-    c_logits, c_perm, c_x, c_w1, c_w2, c_sh = ss.spawn(6)
+    if wtype == "fp16" and (cfg.group or coverage):
+        raise ValueError("fp16 experts have no scale groups and no code coverage variant")
+    # Two seed sequences: the routing inputs (logits, Zipf permutation, x) depend on the token
+    # count and the active-expert restriction; the layer's weights depend on neither, nor on
+    # the weight type -- int4, int8 and fp16 experts are the same normal draw, quantized (or
+    # not) differently, and see the same routing.
+    routing_id = 10 * active
+    seed = (cfg.cfg_id, routing_id, T, SEED_TAG)
+    c_logits, c_perm, c_x = np.random.SeedSequence(list(seed)).spawn(3)
+    c_w1, c_w2, c_sh = np.random.SeedSequence(
+        [cfg.cfg_id, 10000 * int(coverage) + 1, SEED_TAG]).spawn(3)
 
     rl = np.random.Generator(np.random.PCG64(c_logits))
     logits = rl.standard_normal((T, cfg.E), dtype=np.float32)
@@ -131,10 +148,10 @@ def make_inputs(cfg: LayerConfig, T: int, wtype: Optional[str] = None, active: i
     rx = np.random.Generator(np.random.PCG64(c_x))
     x = rx.standard_normal((T, cfg.d), dtype=np.float32).astype(np.float16)
 
-    qmax = QMAX[wtype]
     G1 = 1 if cfg.group == 0 else cfg.d // cfg.group
     G2 = 1 if cfg.group == 0 else cfg.inter // cfg.group
     if with_weights:
+        qmax = None if wtype == "fp16" else QMAX[wtype]
         r1 = [np.random.Generator(np.random.PCG64(s)) for s in c_w1.spawn(cfg.E)]
         r2 = [np.random.Generator(np.random.PCG64(s)) for s in c_w2.spawn(cfg.E)]
         codes1, scales1 = _expert_mats(r1, cfg.E, cfg.d, cfg.n1, qmax, cfg.group, coverage)

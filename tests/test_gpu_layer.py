@@ -32,6 +32,7 @@ LAYER_CASES = [
     ("mt_encoder", 3840, "int8", 0, None),
     ("mt_encoder", 3840, "int4", 1, 512),
     ("mt_encoder", 3840, "int8", 8, 512),
+    ("mt_encoder", 3840, "fp16", 8, 512),
     ("qwen15_moe", 17, None, 0, None),
     ("qwen15_moe", 544, None, 0, None),
     ("dsv2_lite", 9, None, 0, None),

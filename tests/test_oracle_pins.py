@@ -363,3 +363,25 @@ def test_token_subset_equals_full_layer_rows():
     full = oracle.moe_layer(inp)
     sub = np.array([3, 0, 15, 7])
     assert np.array_equal(oracle.moe_layer_tokens(inp, sub), full[sub])
+
+
+def test_fp16_experts_equal_their_dequantized_codes():
+    """The FP16-expert baseline ([W] section 4's comparison) run on Algorithm 1's dequantized
+    weights gives exactly the quantized layer."""
+    import dataclasses
+    inp = synth.make_inputs(synth.get_config("tiny"), 16)
+    w1 = oracle.dequant_algorithm1(inp.codes1, inp.scales1, inp.cfg.group)
+    w2 = oracle.dequant_algorithm1(inp.codes2, inp.scales2, inp.cfg.group)
+    as_fp16 = dataclasses.replace(inp, wtype="fp16", codes1=w1, codes2=w2, scales1=None,
+                                  scales2=None)
+    assert np.array_equal(oracle.moe_layer(as_fp16), oracle.moe_layer(inp))
+
+
+def test_fp16_expert_inputs_are_seeded_normals():
+    inp = synth.make_inputs(synth.get_config("mt_encoder"), 8, wtype="fp16", active=2)
+    assert inp.scales1 is None and inp.scales2 is None
+    assert inp.codes1.dtype == np.float16 and inp.codes1.shape == (32, 1024, 4096)
+    sd = float(inp.codes1[:2].astype(np.float64).std())
+    assert abs(sd - 0.02) < 1e-3
+    again = synth.make_inputs(synth.get_config("mt_encoder"), 8, wtype="fp16", active=2)
+    assert np.array_equal(again.codes2[5], inp.codes2[5])
