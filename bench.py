@@ -72,6 +72,37 @@ def parse():
     return ap.parse_args()
 
 
+def attainable(q, torch, dev):
+    """What plain code reaches on this device: a 1 GiB non-temporal read stream and a loop of
+    independent MFMA 16x16x32 fp16 chains (the library's probe kernels), timed with HIP events."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(8 * cus, dtype=torch.int32, device=dev)
+    out = torch.empty(2 * cus * 256, dtype=torch.float32, device=dev)
+    iters = 4000
+
+    def timed(fn, reps=10):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    t_read = timed(lambda: q.moe_probe_read(buf, 8 * cus, sink=sink))
+    t_mfma = timed(lambda: q.moe_probe_mfma(iters, 2 * cus, out=out))
+    flops = 2 * cus * 4 * iters * 8 * 16384.0
+    del buf
+    return {"hbm_read_GBps": (1 << 30) / t_read / 1e9, "mfma_f16_TFLOPs": flops / t_mfma / 1e12,
+            "how": "library probes: 1 GiB read stream (4 x 16 B in flight per thread, "
+                   f"{8 * cus} blocks); {2 * cus} blocks x 4 waves x {iters} x 8 independent "
+                   "MFMA 16x16x32 fp16"}
+
+
 def cpu_baseline(inp, budget_s):
     """Time the CPU oracle on a bounded sample of the workload's tokens."""
     import numpy as np
@@ -193,6 +224,9 @@ def main():
         except Exception:
             traffic = None
     roof["traffic"] = traffic
+    att = attainable(q, torch, dev)
+    roof["frac_of_attainable"] = roof["achieved"] / (att["hbm_read_GBps"] if roof["bound"] == "hbm"
+                                                     else att["mfma_f16_TFLOPs"])
 
     graph_info = None
     if not args.no_graph:
@@ -256,6 +290,7 @@ def main():
                    "active_experts": active, "max_rows_per_expert": int(counts.max()),
                    "weight_copies_rotated": n_copies, "parallelism": "single-gpu"},
         "roofline": roof,
+        "attainable": att,
         "layer": {"weight_GBps": weight_bytes / layer_s / 1e9,
                   "weight_frac_hbm": weight_bytes / layer_s / 1e9 / HBM_PEAK_GBS,
                   "mfma_TFLOPs": flops / layer_s / 1e12,

@@ -191,6 +191,22 @@ int32_t moe_grouped_gemm_wq_rows(const uint16_t* a, int32_t a_nrows, const int32
                                  void* stream);
 
 /*
+ * Attainable-peak probes (measurement aids, not part of the layer): what plain code reaches on
+ * this device, timed by the caller beside the layer's kernels.
+ *
+ * moe_probe_read  -- reads `bytes` (a multiple of 16) at src once, grid-stride, four 16-byte
+ *                    non-temporal loads in flight per thread, `blocks` blocks of 256 threads;
+ *                    sink[b] (uint32 [blocks]) = XOR of the 32-bit words block b read.
+ * moe_probe_mfma  -- `blocks` blocks of 4 waves, each wave `iters` x 8 independent
+ *                    v_mfma_f32_16x16x32_f16 on all-ones operands (16384 flop each);
+ *                    out[thread] (fp32 [blocks * 256]) = 256 * iters exactly.  iters < 65536.
+ * Errors: MOE_ERR_INVALID for blocks < 1, a misaligned pointer or an out-of-range size.
+ */
+int32_t moe_probe_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
+                       void* stream);
+int32_t moe_probe_mfma(int32_t iters, float* out, int32_t blocks, void* stream);
+
+/*
  * moe_unpermute_combine -- [W] section 3 workflow: rows are restored to the original order
  * and scaled by the gate weight (expert_scale); the k rows of a token are summed.
  *

@@ -25,6 +25,7 @@ __all__ = [
     "moe_unpermute_combine",
     "moe_dequant", "moe_pack_wq", "moe_packed_bytes", "moe_gemm_workspace_size",
     "moe_permute_workspace_size", "GemmOpts", "EXPORTED_SYMBOLS", "new_output",
+    "moe_probe_read", "moe_probe_mfma",
 ]
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE = 0, -1, -2, -3
@@ -46,7 +47,7 @@ lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_wq.s
 EXPORTED_SYMBOLS = (
     "moe_route_topk", "moe_permute", "moe_permute_workspace_size", "moe_grouped_gemm_wq",
     "moe_grouped_gemm_wq_rows", "moe_gemm_workspace_size", "moe_unpermute_combine", "moe_dequant", "moe_packed_bytes",
-    "moe_pack_wq", "moe_status_str", "moe_version",
+    "moe_pack_wq", "moe_status_str", "moe_version", "moe_probe_read", "moe_probe_mfma",
 )
 
 
@@ -105,6 +106,8 @@ def lib():
         "moe_pack_wq": (_I, [_P, _I, _I, _I, _I, _P]),
         "moe_status_str": (ctypes.c_char_p, [_I]),
         "moe_version": (_I, []),
+        "moe_probe_read": (_I, [_P, _SZ, _P, _I, _P]),
+        "moe_probe_mfma": (_I, [_I, _P, _I, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -295,6 +298,32 @@ def moe_grouped_gemm_wq_rows(a, a_rows, a_row_div, expert_offsets, R, E, K, N, w
         _ptr(a), a_nrows, _ptr(a_rows), int(a_row_div), _ptr(expert_offsets), R, E, K, N,
         _ptr(w_packed), _ptr(scales), wt, int(group_size), ac, _ptr(row_scale), _ptr(out),
         out_nrows, _ptr(out_rows), ctypes.byref(o) if o else None, None, 0, _stream(stream)))
+    return out
+
+
+def moe_probe_read(src, blocks, sink=None, stream=None):
+    """Attainable-read probe: reads all of `src` (a device tensor, bytes % 16 == 0) once;
+    returns the per-block XOR sink (uint32 as int32 [blocks])."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.empty(blocks, dtype=torch.int32, device=src.device)
+    _need(sink, torch.int32, "sink", blocks)
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    _check("moe_probe_read", lib().moe_probe_read(_ptr(src), src.numel() * src.element_size(),
+                                                  _ptr(sink), int(blocks), _stream(stream)))
+    return sink
+
+
+def moe_probe_mfma(iters, blocks, out=None, device="cuda", stream=None):
+    """Attainable-MFMA probe: blocks x 4 waves x iters x 8 MFMA 16x16x32 fp16; returns the
+    fp32 [blocks * 256] result (every element 256 * iters)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=device)
+    _need(out, torch.float32, "out", blocks * 256)
+    _check("moe_probe_mfma", lib().moe_probe_mfma(int(iters), _ptr(out), int(blocks),
+                                                  _stream(stream)))
     return out
 
 

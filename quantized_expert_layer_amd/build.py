@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_wq.so")
 
-HIP_SOURCES = ["api.hip", "route_topk.hip", "permute.hip", "gemm.hip", "combine.hip", "dequant.hip"]
+HIP_SOURCES = ["api.hip", "route_topk.hip", "permute.hip", "gemm.hip", "combine.hip", "dequant.hip",
+               "probe.hip"]
 CXX_SOURCES = ["pack.cpp"]
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -83,6 +83,10 @@ int32_t validate_gemm(const uint16_t* a, const int32_t* offsets, int32_t R, int3
 
 }  // namespace
 
+namespace moe {
+int32_t device_status() { return check_device(); }
+}  // namespace moe
+
 extern "C" {
 
 int32_t moe_version(void) { return kVersion; }

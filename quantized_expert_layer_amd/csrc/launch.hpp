@@ -6,6 +6,9 @@
 
 namespace moe {
 
+// MOE_OK when the current device is a usable gfx950, else MOE_ERR_NO_DEVICE (cached per device).
+int32_t device_status();
+
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int gate_all,
                              int32_t* ids, float* wts, hipStream_t stream);
 

@@ -247,3 +247,16 @@ def test_gemm_rows_validation():
     if not gpu_available():
         assert g(*args()) == q.MOE_ERR_NO_DEVICE
         assert g(*args(ar=None, div=0, orows=FAKE)) == q.MOE_ERR_NO_DEVICE   # div unused
+
+
+def test_probe_validation():
+    L = q.lib()
+    assert L.moe_probe_read(FAKE, 64, FAKE, 0, None) == q.MOE_ERR_INVALID       # no blocks
+    assert L.moe_probe_read(FAKE, 60, FAKE, 8, None) == q.MOE_ERR_INVALID       # bytes % 16
+    assert L.moe_probe_read(MIS, 64, FAKE, 8, None) == q.MOE_ERR_INVALID
+    assert L.moe_probe_read(None, 0, None, 8, None) == q.MOE_OK                 # nothing to read
+    assert L.moe_probe_mfma(-1, FAKE, 8, None) == q.MOE_ERR_INVALID
+    assert L.moe_probe_mfma(1 << 16, FAKE, 8, None) == q.MOE_ERR_INVALID
+    assert L.moe_probe_mfma(4, FAKE, 0, None) == q.MOE_ERR_INVALID
+    if not gpu_available():
+        assert L.moe_probe_mfma(4, FAKE, 8, None) == q.MOE_ERR_NO_DEVICE
