@@ -7,7 +7,9 @@
  *   3. moe_grouped_gemm_wq   grouped GEMM over all active experts, int4/int8 codes
  *                            dequantized in registers, fused activation / gate weight
  *   4. moe_unpermute_combine restore token order, scale by gate weight, sum the k rows
- *   and moe_dequant          the standalone per-expert dequantization (Algorithm 1)
+ *   and moe_dequant          the standalone per-expert dequantization (Algorithm 1);
+ *   moe_decode_layer         steps 1-4 for the few tokens of a decode / verify step, in three
+ *                            launches
  *
  * Sources (page, section):
  *   [W] "Who Says Elephants Can't Run: Bringing Large Scale MoE Models into Cloud Scale
@@ -77,6 +79,8 @@ typedef struct moe_gemm_opts {
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK      8
 #define MOE_MAX_SPLIT_K   8
+#define MOE_DECODE_MAX_TOKENS 64    /* moe_decode_layer: T <= 64 ...      */
+#define MOE_DECODE_MAX_ROWS  512    /*                   ... and T*k <= 512 */
 
 /*
  * moe_route_topk -- top-k gating.   [S] Background / MoE: the router scores every expert
@@ -189,6 +193,42 @@ int32_t moe_grouped_gemm_wq_rows(const uint16_t* a, int32_t a_nrows, const int32
                                  int32_t out_nrows, const int32_t* out_rows,
                                  const moe_gemm_opts* opts, void* ws, size_t ws_bytes,
                                  void* stream);
+
+/*
+ * moe_decode_layer -- the whole routed layer for the few tokens of a decode or verify step:
+ * gating, sort, both grouped GEMMs, gate weight, unpermute and combine, in three launches.
+ *   [S] Method steps, step 5 and Technical novelty: the draft's expert sub-computations in
+ *   one fused launch; the verify step groups tokens by expert into one GEMM per expert and
+ *   scatters the results back.  [W] section 3 workflow and Algorithm 1 as for the calls above.
+ *
+ *   logits    fp32 [T, E]      router logits;  x fp16 [T, d]  token activations
+ *   gate_mode enum moe_gate;   act: MOE_ACT_NONE / RELU (W1 is [d, inter]) or SWIGLU (W1 is
+ *             [d, 2*inter], columns [gate | up])
+ *   w1, s1    first-GEMM weights packed by moe_pack_wq for (wtype, E, d, inter or 2*inter) and
+ *             their scales (NULL for MOE_W_FP16), as for moe_grouped_gemm_wq
+ *   w2, s2    second-GEMM weights for (wtype, E, inter, d) and scales
+ *   addend    fp16 [T, d] or NULL: added with weight 1 (e.g. shared experts)
+ *   topk_ids, topk_w  int32 / fp32 [T, k]  out: exactly what moe_route_topk returns
+ *   out       fp16 [T, d]  out: out[t] = fp16( sum_j topk_w[t,j] * FFN_{topk_ids[t,j]}(x[t])
+ *             + addend[t] ).  The hidden activations are rounded to fp16 as in
+ *             moe_grouped_gemm_wq; the k expert outputs are summed in fp32 without the fp16
+ *             rounding of each one, in an order fixed by the routing (deterministic), so out
+ *             agrees with the five-call sequence within rounding, not bit for bit.
+ *   ws        workspace of at least moe_decode_workspace_size(...) bytes; contents on entry
+ *             do not matter, and calls that share one workspace must not overlap in time.
+ * Errors: MOE_ERR_UNSUPPORTED for T > MOE_DECODE_MAX_TOKENS, T*k > MOE_DECODE_MAX_ROWS,
+ * d % 128 != 0 or inter % 128 != 0, group_size not in {0, 128} (0 for FP16); otherwise as
+ * moe_route_topk and moe_grouped_gemm_wq; MOE_ERR_WORKSPACE for a missing or short workspace.
+ */
+int32_t moe_decode_layer(const float* logits, const uint16_t* x, int32_t T, int32_t E,
+                         int32_t k, int32_t gate_mode, int32_t d, int32_t inter, int32_t act,
+                         const void* w1, const uint16_t* s1, const void* w2,
+                         const uint16_t* s2, int32_t wtype, int32_t group_size,
+                         const uint16_t* addend, int32_t* topk_ids, float* topk_w,
+                         uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+/* Workspace bytes of moe_decode_layer (0 for arguments it does not accept). */
+size_t moe_decode_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int32_t inter,
+                                 int32_t wtype);
 
 /*
  * Attainable-peak probes (measurement aids, not part of the layer): what plain code reaches on

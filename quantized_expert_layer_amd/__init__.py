@@ -25,7 +25,8 @@ __all__ = [
     "moe_unpermute_combine",
     "moe_dequant", "moe_pack_wq", "moe_packed_bytes", "moe_gemm_workspace_size",
     "moe_permute_workspace_size", "GemmOpts", "EXPORTED_SYMBOLS", "new_output",
-    "moe_probe_read", "moe_probe_mfma",
+    "moe_probe_read", "moe_probe_mfma", "moe_decode_layer", "moe_decode_workspace_size",
+    "MOE_DECODE_MAX_TOKENS", "MOE_DECODE_MAX_ROWS",
 ]
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE = 0, -1, -2, -3
@@ -36,6 +37,7 @@ ACT_NONE, ACT_RELU, ACT_SWIGLU = 0, 1, 2
 PATH_AUTO, PATH_STREAM, PATH_TILE = 0, 1, 2
 TILE_AUTO, TILE_64x256, TILE_64x128, TILE_128x128 = 0, 1, 2, 3
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_SPLIT_K = 256, 8, 8
+MOE_DECODE_MAX_TOKENS, MOE_DECODE_MAX_ROWS = 64, 512
 
 WTYPES = {"int4": W_INT4, "int8": W_INT8, "fp16": W_FP16}
 ACTS = {"none": ACT_NONE, "relu": ACT_RELU, "swiglu": ACT_SWIGLU}
@@ -48,6 +50,7 @@ EXPORTED_SYMBOLS = (
     "moe_route_topk", "moe_permute", "moe_permute_workspace_size", "moe_grouped_gemm_wq",
     "moe_grouped_gemm_wq_rows", "moe_gemm_workspace_size", "moe_unpermute_combine", "moe_dequant", "moe_packed_bytes",
     "moe_pack_wq", "moe_status_str", "moe_version", "moe_probe_read", "moe_probe_mfma",
+    "moe_decode_layer", "moe_decode_workspace_size",
 )
 
 
@@ -108,6 +111,9 @@ def lib():
         "moe_version": (_I, []),
         "moe_probe_read": (_I, [_P, _SZ, _P, _I, _P]),
         "moe_probe_mfma": (_I, [_I, _P, _I, _P]),
+        "moe_decode_layer": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I,
+                                  _P, _P, _P, _P, _P, _SZ, _P]),
+        "moe_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -325,6 +331,47 @@ def moe_probe_mfma(iters, blocks, out=None, device="cuda", stream=None):
     _check("moe_probe_mfma", lib().moe_probe_mfma(int(iters), _ptr(out), int(blocks),
                                                   _stream(stream)))
     return out
+
+
+def moe_decode_workspace_size(T, k, E, d, inter, wtype):
+    return lib().moe_decode_workspace_size(T, k, E, d, inter, WTYPES.get(wtype, wtype))
+
+
+def moe_decode_layer(logits, x, k, gate_mode, inter, act, w1, s1, w2, s2, wtype, group_size,
+                     addend=None, topk_ids=None, topk_w=None, out=None, ws=None, stream=None):
+    """The routed layer for a decode / verify step (T <= MOE_DECODE_MAX_TOKENS tokens).
+    Returns (out fp16 [T, d], topk_ids int32 [T, k], topk_w fp32 [T, k])."""
+    torch = _torch()
+    T, E = logits.shape
+    d = x.shape[1]
+    wt = WTYPES.get(wtype, wtype)
+    dev = x.device
+    if out is None:
+        out = new_output((T, d), torch.float16, dev)
+    if topk_ids is None:
+        topk_ids = new_output((T, k), torch.int32, dev)
+    if topk_w is None:
+        topk_w = new_output((T, k), torch.float32, dev)
+    if ws is None:
+        need = lib().moe_decode_workspace_size(T, k, E, d, inter, wt)
+        ws = new_output(max(need, 16), torch.uint8, dev)
+    _need(logits, torch.float32, "logits", T * E)
+    _need(x, torch.float16, "x", T * d)
+    _need(w1, torch.uint8, "w1")
+    _need(s1, torch.float16, "s1")
+    _need(w2, torch.uint8, "w2")
+    _need(s2, torch.float16, "s2")
+    _need(addend, torch.float16, "addend", T * d)
+    _need(topk_ids, torch.int32, "topk_ids", T * k)
+    _need(topk_w, torch.float32, "topk_w", T * k)
+    _need(out, torch.float16, "out", T * d)
+    _need(ws, torch.uint8, "ws")
+    _check("moe_decode_layer", lib().moe_decode_layer(
+        _ptr(logits), _ptr(x), T, E, k, GATES.get(gate_mode, gate_mode), d, int(inter),
+        ACTS.get(act, act), _ptr(w1), _ptr(s1), _ptr(w2), _ptr(s2), wt, int(group_size),
+        _ptr(addend), _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(stream)))
+    return out, topk_ids, topk_w
 
 
 def moe_unpermute_combine(y_perm, inv_perm, topk_w, addend, T, k, out=None, stream=None):

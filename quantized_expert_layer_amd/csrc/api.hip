@@ -226,6 +226,76 @@ int32_t moe_grouped_gemm_wq_rows(const uint16_t* a, int32_t a_nrows, const int32
                         out_rows ? out_nrows : R, out_rows, opts, ws, ws_bytes, stream);
 }
 
+static int32_t validate_decode(int32_t T, int32_t E, int32_t k, int32_t gate_mode, int32_t d,
+                               int32_t inter, int32_t act, int32_t wtype, int32_t group) {
+    if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E)
+        return MOE_ERR_INVALID;
+    if (gate_mode != MOE_GATE_SOFTMAX_TOPK && gate_mode != MOE_GATE_SOFTMAX_ALL)
+        return MOE_ERR_INVALID;
+    if (act < MOE_ACT_NONE || act > MOE_ACT_SWIGLU) return MOE_ERR_INVALID;
+    if (wtype < MOE_W_INT4 || wtype > MOE_W_FP16) return MOE_ERR_INVALID;
+    if (d <= 0 || inter <= 0) return MOE_ERR_INVALID;
+    if (group != 0 && group != 128) return MOE_ERR_UNSUPPORTED;
+    if (wtype == MOE_W_FP16 && group != 0) return MOE_ERR_UNSUPPORTED;
+    if (d % 128 != 0 || inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    if (T > MOE_DECODE_MAX_TOKENS || T * k > MOE_DECODE_MAX_ROWS) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)inter * MOE_DECODE_MAX_ROWS >= (int64_t)1 << 31 ||
+        (int64_t)d * MOE_DECODE_MAX_ROWS >= (int64_t)1 << 31)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+size_t moe_decode_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int32_t inter,
+                                 int32_t wtype) {
+    if (validate_decode(T, E, k, MOE_GATE_SOFTMAX_TOPK, d, inter, MOE_ACT_NONE, wtype, 0) !=
+        MOE_OK)
+        return 0;
+    return moe::decode_workspace_layout(T, k, E, d, inter, wtype, nullptr, nullptr);
+}
+
+int32_t moe_decode_layer(const float* logits, const uint16_t* x, int32_t T, int32_t E,
+                         int32_t k, int32_t gate_mode, int32_t d, int32_t inter, int32_t act,
+                         const void* w1, const uint16_t* s1, const void* w2,
+                         const uint16_t* s2, int32_t wtype, int32_t group_size,
+                         const uint16_t* addend, int32_t* topk_ids, float* topk_w,
+                         uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+    if (int32_t st = validate_decode(T, E, k, gate_mode, d, inter, act, wtype, group_size))
+        return st;
+    if (T == 0) return MOE_OK;
+    if (!logits || !x || !w1 || !w2 || !topk_ids || !topk_w || !out) return MOE_ERR_INVALID;
+    if (wtype != MOE_W_FP16 && (!s1 || !s2)) return MOE_ERR_INVALID;
+    if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
+        !aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(out, 16))
+        return MOE_ERR_INVALID;
+    if ((s1 && !aligned(s1, 16)) || (s2 && !aligned(s2, 16)) || (addend && !aligned(addend, 16)))
+        return MOE_ERR_INVALID;
+    const size_t need = moe::decode_workspace_layout(T, k, E, d, inter, wtype, nullptr, nullptr);
+    if (!ws || ws_bytes < need || !aligned(ws, 16)) return MOE_ERR_WORKSPACE;
+    if (int32_t st = check_device()) return st;
+    moe::DecodeArgs a;
+    a.logits = logits;
+    a.x = x;
+    a.T = T;
+    a.E = E;
+    a.k = k;
+    a.gate_all = gate_mode == MOE_GATE_SOFTMAX_ALL;
+    a.d = d;
+    a.inter = inter;
+    a.act = act;
+    a.w1 = w1;
+    a.s1 = s1;
+    a.w2 = w2;
+    a.s2 = s2;
+    a.wtype = wtype;
+    a.group = group_size;
+    a.addend = addend;
+    a.ids = topk_ids;
+    a.wts = topk_w;
+    a.out = out;
+    a.ws = ws;
+    return hip_status(moe::launch_decode(a, (hipStream_t)stream));
+}
+
 int32_t moe_unpermute_combine(const uint16_t* y_perm, const int32_t* inv_perm, const float* topk_w,
                               const uint16_t* addend, int32_t T, int32_t k, int32_t d,
                               uint16_t* out, void* stream) {

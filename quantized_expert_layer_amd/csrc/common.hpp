@@ -92,6 +92,30 @@ __device__ __forceinline__ f16x8 pack8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
     return r;
 }
 
+// ------------------------------------------------------------------------------------
+// Weight fragment expansion: K-step j of a lane's 16-byte super-block slice -> B operand.
+// Group scales (group 128) are folded in by one fp16 multiply, giving exactly Algorithm 1's
+// fp16 weight; per-channel scales are applied to the fp32 result instead.
+// ------------------------------------------------------------------------------------
+template <int WT, bool SCALE>
+__device__ __forceinline__ f16x8 weight_frag(const u32x4& raw, int j, f16x2 s2,
+                                             const I2F4Consts& k4) {
+    f16x2 q[4];
+    if constexpr (WT == MOE_W_INT4) {
+        i2f_int4(raw[j], q, k4);
+    } else if constexpr (WT == MOE_W_INT8) {
+        i2f_int8(raw[2 * j], q);
+        i2f_int8(raw[2 * j + 1], q + 2);
+    } else {
+        return __builtin_bit_cast(f16x8, raw);
+    }
+    if constexpr (SCALE) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) q[h] = q[h] * s2;
+    }
+    return pack8(q[0], q[1], q[2], q[3]);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

@@ -21,31 +21,6 @@
 
 namespace moe {
 
-// ------------------------------------------------------------------------------------
-// Weight fragment expansion: K-step j of a lane's 16-byte super-block slice -> B operand.
-// Group scales (group 128) are folded in by one fp16 multiply, giving exactly Algorithm 1's
-// fp16 weight; per-channel scales are applied to the fp32 result instead.
-// ------------------------------------------------------------------------------------
-template <int WT, bool SCALE>
-__device__ __forceinline__ f16x8 weight_frag(const u32x4& raw, int j, f16x2 s2,
-                                             const I2F4Consts& k4) {
-    f16x2 q[4];
-    if constexpr (WT == MOE_W_INT4) {
-        i2f_int4(raw[j], q, k4);
-    } else if constexpr (WT == MOE_W_INT8) {
-        i2f_int8(raw[2 * j], q);
-        i2f_int8(raw[2 * j + 1], q + 2);
-    } else {
-        return __builtin_bit_cast(f16x8, raw);
-    }
-    if constexpr (SCALE) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h) q[h] = q[h] * s2;
-    }
-    return pack8(q[0], q[1], q[2], q[3]);
-}
-
-
 // Output fragment layout.  The MFMA is issued with the weight fragment as its first operand
 // and the activation fragment as its second, i.e. it computes Y^T = W^T X^T; lane l then holds
 // row (l & 15) of its 16-row subtile and the 4 consecutive columns 4*(l >> 4) .. +3 of its

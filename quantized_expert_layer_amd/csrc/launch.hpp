@@ -51,4 +51,47 @@ int gemm_choose_tile(int R, int E, int N, int act, int forced);
 hipError_t launch_gemm_stream(const GemmParams& p, hipStream_t stream);
 hipError_t launch_gemm_tile(const GemmParams& p, hipStream_t stream);
 
+// ---- decode step (few tokens): gating + sort, GEMM 1, GEMM 2 with the combine ----
+// Workspace of one decode call, carved from the caller's buffer (256-byte aligned parts).
+struct DecodeWs {
+    int32_t* perm;           // [R]
+    int32_t* inv_perm;       // [R]
+    int32_t* offsets;        // [E + 1]
+    float* w_perm;           // [R]
+    uint16_t* h;             // fp16 [R, inter] GEMM 1 output, sorted rows
+};
+
+struct CombineParams {
+    const uint16_t* h;       // fp16 [R, K] rows sorted by expert
+    const int32_t* offsets;  // [E + 1]
+    const int32_t* perm;     // [R] flat slot t*k + j of sorted row p
+    const float* w_perm;     // [R] gate weight of sorted row p
+    const void* w;           // packed weights [E, K, N]
+    const uint16_t* scales;  // [E, G, N], NULL for fp16 weights
+    const uint16_t* addend;  // fp16 [T, N] or NULL
+    uint16_t* out;           // fp16 [T, N]
+    int R, E, K, N, T, k;
+};
+
+struct DecodeArgs {
+    const float* logits;
+    const uint16_t* x;
+    int T, E, k, gate_all, d, inter, act;
+    const void* w1;
+    const uint16_t* s1;
+    const void* w2;
+    const uint16_t* s2;
+    int wtype, group;
+    const uint16_t* addend;
+    int32_t* ids;
+    float* wts;
+    uint16_t* out;
+    void* ws;
+};
+
+// Bytes of the decode workspace; with ws and base given, also the part addresses.
+size_t decode_workspace_layout(int T, int k, int E, int d, int inter, int wtype, DecodeWs* ws,
+                               char* base);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
 }  // namespace moe

@@ -5,7 +5,9 @@ DeviceLayer owns the packed expert weights in device memory; forward() enqueues
   -> moe_grouped_gemm_wq (down or W2, gate weight as row scale)
   [-> shared fp16 experts through the same GEMM entry, E = 1]
   -> moe_unpermute_combine
-on one stream, with no host synchronisation.  Nothing here computes: torch only allocates.
+on one stream, with no host synchronisation.  A step of at most MOE_DECODE_MAX_TOKENS tokens
+(decode / verify) instead makes one moe_decode_layer call (after the shared experts, whose
+output it adds).  Nothing here computes: torch only allocates.
 """
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Tuple
@@ -14,9 +16,10 @@ import numpy as np
 
 import ctypes
 
-from . import (ACTS, GATES, WTYPES, MoEError, _ptr, _stream, lib, moe_gemm_workspace_size,
-               moe_grouped_gemm_wq, moe_grouped_gemm_wq_rows, moe_pack_wq, moe_permute,
-               moe_route_topk, moe_unpermute_combine, new_output)
+from . import (ACTS, GATES, MOE_DECODE_MAX_ROWS, MOE_DECODE_MAX_TOKENS, WTYPES, MoEError, _ptr,
+               _stream, lib, moe_decode_layer, moe_decode_workspace_size,
+               moe_gemm_workspace_size, moe_grouped_gemm_wq, moe_grouped_gemm_wq_rows,
+               moe_pack_wq, moe_permute, moe_route_topk, moe_unpermute_combine, new_output)
 
 
 def _dev(a, device):
@@ -36,7 +39,7 @@ class DeviceLayer:
                  gate_mode: str, codes1: np.ndarray, scales1: np.ndarray, codes2: np.ndarray,
                  scales2: np.ndarray, shared: Optional[List[Tuple[np.ndarray, np.ndarray]]] = None,
                  device: str = "cuda", gemm_path: int = 0, gemm_tile: int = 0,
-                 fuse_rows: bool = True):
+                 fuse_rows: bool = True, decode: Optional[bool] = None):
         import torch
         self.E, self.k, self.d, self.inter = E, k, d, inter
         self.act, self.wtype, self.group, self.gate_mode = act, wtype, group, gate_mode
@@ -47,6 +50,9 @@ class DeviceLayer:
         # fuse_rows: the first GEMM reads x through perm (no x_perm copy), and with k = 1 the
         # second GEMM writes the output rows through perm (no combine launch)
         self.fuse_rows = fuse_rows
+        # decode: None = moe_decode_layer for every step it accepts (and default GEMM
+        # settings); False = always the five calls; True = require it
+        self.decode = decode
         self.w1 = _dev(moe_pack_wq(codes1, wtype), self.device)
         self.w2 = _dev(moe_pack_wq(codes2, wtype), self.device)
         # fp16 experts (wtype "fp16") carry no scales
@@ -67,13 +73,25 @@ class DeviceLayer:
                            _dev(moe_pack_wq(sw2.astype(np.float16), "fp16"), self.device))
 
     @classmethod
-    def from_inputs(cls, inp, device="cuda", gemm_path=0, gemm_tile=0, fuse_rows=True):
+    def from_inputs(cls, inp, device="cuda", gemm_path=0, gemm_tile=0, fuse_rows=True,
+                    decode=None):
         c = inp.cfg
         return cls(E=c.E, k=c.k, d=c.d, inter=c.inter, act=c.act, wtype=inp.wtype,
                    group=c.group, gate_mode=c.gate_mode, codes1=inp.codes1,
                    scales1=inp.scales1, codes2=inp.codes2, scales2=inp.scales2,
                    shared=inp.shared or None, device=device, gemm_path=gemm_path,
-                   gemm_tile=gemm_tile, fuse_rows=fuse_rows)
+                   gemm_tile=gemm_tile, fuse_rows=fuse_rows, decode=decode)
+
+    def uses_decode(self, T: int, gate_in_gemm: bool = True) -> bool:
+        """Whether a step of T tokens runs as one moe_decode_layer call."""
+        fits = (0 < T <= MOE_DECODE_MAX_TOKENS and T * self.k <= MOE_DECODE_MAX_ROWS
+                and self.d % 128 == 0 and self.inter % 128 == 0)
+        if self.decode is True:
+            if not fits:
+                raise ValueError(f"moe_decode_layer does not take T={T}, k={self.k}")
+            return True
+        return (self.decode is None and fits and self.gemm_path == 0 and self.gemm_tile == 0
+                and self.fuse_rows and gate_in_gemm)
 
     def _scatter_out(self, gate_in_gemm: bool) -> bool:
         """Whether the second GEMM writes the layer output itself: one expert per token, the
@@ -108,7 +126,25 @@ class DeviceLayer:
                       moe_gemm_workspace_size(T, 1, self.shared_inter, d, "fp16", "none",
                                               self.gemm_path))
         b["ws"] = new_output(max(wsz, 16), torch.uint8, dev)
+        dws = moe_decode_workspace_size(T, self.k, self.E, d, self.inter, self.wtype)
+        if dws:
+            b["dws"] = new_output(dws, torch.uint8, dev)
         return Workspace(T=T, bufs=b)
+
+    def _shared_calls(self, b, x, T):
+        """(name, C function, args) of the shared experts (fp16, E = 1) into b["sh_y"]."""
+        L, st = lib(), None
+        return [
+            ("shared1", L.moe_grouped_gemm_wq, (_ptr(x), _ptr(b["sh_off"]), T, 1, self.d,
+                                                2 * self.shared_inter, _ptr(self.shared[0]),
+                                                None, 2, 0, 2, None, _ptr(b["sh_h"]), None,
+                                                _ptr(b["ws"]), b["ws"].numel(), st)),
+            ("shared2", L.moe_grouped_gemm_wq, (_ptr(b["sh_h"]), _ptr(b["sh_off"]), T, 1,
+                                                self.shared_inter, self.d,
+                                                _ptr(self.shared[1]), None, 2, 0, 0, None,
+                                                _ptr(b["sh_y"]), None, _ptr(b["ws"]),
+                                                b["ws"].numel(), st)),
+        ]
 
     def forward(self, x, logits, ws: Optional[Workspace] = None, gate_in_gemm: bool = True,
                 stream=None):
@@ -118,6 +154,20 @@ class DeviceLayer:
             ws = self.workspace(T)
         b = ws.bufs
         path = self.gemm_path
+        if self.uses_decode(T, gate_in_gemm):
+            addend = None
+            if self.shared is not None:
+                for name, fn, args in self._shared_calls(b, x, T):
+                    args = args[:-1] + (_stream(stream),)
+                    st = fn(*args)
+                    if st != 0:
+                        raise MoEError(name, st)
+                addend = b["sh_y"]
+            moe_decode_layer(logits, x, self.k, self.gate_mode, self.inter, self.act, self.w1,
+                             self.s1, self.w2, self.s2, self.wtype, self.group, addend=addend,
+                             topk_ids=b["ids"], topk_w=b["w"], out=b["out"], ws=b["dws"],
+                             stream=stream)
+            return b["out"]
         moe_route_topk(logits, self.k, self.gate_mode, b["ids"], b["w"], stream=stream)
         fused = self.fuse_rows
         scatter = self._scatter_out(gate_in_gemm)
@@ -179,6 +229,19 @@ class DeviceLayer:
         scatter = self._scatter_out(gate_in_gemm)
         R = T * self.k
         rs = _ptr(b["wp"]) if gate_in_gemm else None
+        keep = (opts, x, logits, w1, w2, self.s1, self.s2, self.shared, ws)
+        if self.uses_decode(T, gate_in_gemm):
+            calls = []
+            addend = None
+            if self.shared is not None:
+                calls = [(n, fn, args[:-1] + (st,)) for n, fn, args in self._shared_calls(b, x, T)]
+                addend = b["sh_y"]
+            calls.append(("decode", L.moe_decode_layer,
+                          (_ptr(logits), _ptr(x), T, self.E, self.k, GATES[self.gate_mode],
+                           self.d, self.inter, ac, _ptr(w1), _ptr(self.s1), _ptr(w2),
+                           _ptr(self.s2), wt, self.group, _ptr(addend), _ptr(b["ids"]),
+                           _ptr(b["w"]), _ptr(b["out"]), _ptr(b["dws"]), b["dws"].numel(), st)))
+            return LayerPlan(calls, b["out"], keep=keep)
         calls = [
             ("route", L.moe_route_topk, (_ptr(logits), T, self.E, self.k, GATES[self.gate_mode],
                                          _ptr(b["ids"]), _ptr(b["w"]), st)),

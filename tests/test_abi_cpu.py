@@ -218,7 +218,8 @@ def test_binding_limits_match_header():
     import re
     text = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                              "include", "moe_wq.h")).read()
-    for name in ("MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SPLIT_K"):
+    for name in ("MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SPLIT_K", "MOE_DECODE_MAX_TOKENS",
+                 "MOE_DECODE_MAX_ROWS"):
         m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == getattr(q, name), name
 
@@ -260,3 +261,59 @@ def test_probe_validation():
     assert L.moe_probe_mfma(4, FAKE, 0, None) == q.MOE_ERR_INVALID
     if not gpu_available():
         assert L.moe_probe_mfma(4, FAKE, 8, None) == q.MOE_ERR_NO_DEVICE
+
+
+def test_decode_layer_validation():
+    L = q.lib()
+    f = L.moe_decode_layer
+    ws_need = L.moe_decode_workspace_size(4, 2, 8, 256, 512, 0)
+    assert ws_need > 0
+
+    def args(**kw):
+        d = dict(logits=FAKE, x=FAKE, T=4, E=8, k=2, gate=0, d=256, inter=512, act=2, w1=FAKE,
+                 s1=FAKE, w2=FAKE, s2=FAKE, wt=0, g=128, add=None, ids=FAKE, w=FAKE, out=FAKE,
+                 ws=FAKE, wsb=ws_need, stream=None)
+        d.update(kw)
+        return [d[n] for n in ("logits", "x", "T", "E", "k", "gate", "d", "inter", "act", "w1",
+                               "s1", "w2", "s2", "wt", "g", "add", "ids", "w", "out", "ws", "wsb",
+                               "stream")]
+
+    assert f(*args(k=9)) == q.MOE_ERR_INVALID
+    assert f(*args(k=9, E=8)) == q.MOE_ERR_INVALID
+    assert f(*args(gate=3)) == q.MOE_ERR_INVALID
+    assert f(*args(act=3)) == q.MOE_ERR_INVALID
+    assert f(*args(T=-1)) == q.MOE_ERR_INVALID
+    assert f(*args(T=q.MOE_DECODE_MAX_TOKENS + 1)) == q.MOE_ERR_UNSUPPORTED
+    assert f(*args(T=64, k=8, E=16, wsb=0)) == q.MOE_ERR_WORKSPACE
+    assert f(*args(d=200)) == q.MOE_ERR_UNSUPPORTED
+    assert f(*args(inter=1400)) == q.MOE_ERR_UNSUPPORTED
+    assert f(*args(g=64)) == q.MOE_ERR_UNSUPPORTED
+    assert f(*args(wt=2, g=128)) == q.MOE_ERR_UNSUPPORTED                # fp16 has no groups
+    assert f(*args(s1=None)) == q.MOE_ERR_INVALID                        # int codes need scales
+    assert f(*args(ids=None)) == q.MOE_ERR_INVALID
+    assert f(*args(x=MIS)) == q.MOE_ERR_INVALID
+    assert f(*args(add=MIS)) == q.MOE_ERR_INVALID
+    assert f(*args(ws=None)) == q.MOE_ERR_WORKSPACE
+    assert f(*args(wsb=ws_need - 1)) == q.MOE_ERR_WORKSPACE
+    assert f(*args(T=0, logits=None, x=None, ids=None, w=None, out=None, ws=None)) == q.MOE_OK
+    if not gpu_available():
+        assert f(*args()) == q.MOE_ERR_NO_DEVICE
+        # fp16 weights take no scales; the most rows a call takes (T * k = 512) is accepted
+        fp16_ws = L.moe_decode_workspace_size(4, 2, 8, 256, 512, 2)
+        assert f(*args(wt=2, g=0, s1=None, s2=None, wsb=fp16_ws)) == q.MOE_ERR_NO_DEVICE
+        big = L.moe_decode_workspace_size(64, 8, 16, 256, 512, 0)
+        assert f(*args(T=64, k=8, E=16, wsb=big)) == q.MOE_ERR_NO_DEVICE
+
+
+def test_decode_workspace_size():
+    L = q.lib()
+    assert L.moe_decode_workspace_size(65, 1, 8, 256, 512, 0) == 0          # T too large
+    assert L.moe_decode_workspace_size(64, 9, 16, 256, 512, 0) == 0         # k too large
+    assert L.moe_decode_workspace_size(4, 2, 8, 200, 512, 0) == 0           # d % 128
+    T, k, E, d, inter = 17, 4, 60, 2048, 1408 // 128 * 128
+    need = L.moe_decode_workspace_size(T, k, E, d, inter, 0)
+    R = T * k
+    # perm, inv_perm, offsets, w_perm, counters and the fp16 hidden rows at least
+    assert need >= 4 * (3 * R + E + 1) + 4 * (d // 16) + 2 * R * inter
+    # and it grows with the tokens
+    assert L.moe_decode_workspace_size(T + 1, k, E, d, inter, 0) > need
