@@ -228,7 +228,10 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmP
 //                 loaded and expanded by one wave only.  SwiGLU: NS/2 gate blocks + the
 //                 matching NS/2 up blocks.
 //   K stage     = 128 rows of K (64 for fp16 weights).  The A stage (rows x KC fp16) is
-//                 loaded to registers one stage ahead and written to LDS (double buffered).
+//                 loaded to registers two stages ahead (two register sets) and written to
+//                 LDS one stage ahead (double buffered); the weights are loaded one stage
+//                 ahead.  The activation rows are usually not in L2 (a previous kernel's
+//                 output, or x read through perm), so their latency is the longer one.
 //                 LDS rows are not padded: 16-byte chunk c of row r sits at chunk position
 //                 c ^ (r & 15), so the 16 lanes of an A-fragment read (16 rows, one chunk)
 //                 and of a row write hit distinct 4-bank groups.
@@ -307,17 +310,18 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         asrc[i] = (const u32x4*)(p.a + (size_t)a_source_row(p, row0 + min(r, rows - 1)) * K) + c;
         adst[i] = r * KC + ((c ^ (r & (CPR - 1))) * 8);
     }
-    u32x4 areg[ACH];
-    auto load_a = [&](int st) {
+    // two register sets: the A stage two ahead is loaded while the one ahead waits to be stored
+    u32x4 areg[2][ACH];
+    auto load_a = [&](int set, int st) {
 #pragma unroll
         for (int i = 0; i < ACH; ++i)
-            if (ATOT % 256 == 0 || (int)threadIdx.x + 256 * i < ATOT) areg[i] = asrc[i][st * CPR];
+            if (ATOT % 256 == 0 || (int)threadIdx.x + 256 * i < ATOT) areg[set][i] = asrc[i][st * CPR];
     };
-    auto store_a = [&](int buf) {
+    auto store_a = [&](int set, int buf) {
 #pragma unroll
         for (int i = 0; i < ACH; ++i)
             if (ATOT % 256 == 0 || (int)threadIdx.x + 256 * i < ATOT)
-                *(u32x4*)(lds + buf * LDS_BUF + adst[i]) = areg[i];
+                *(u32x4*)(lds + buf * LDS_BUF + adst[i]) = areg[set][i];
     };
 
     // group scales: one per (column block, super-block) -- a super-block never spans groups
@@ -344,18 +348,20 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         for (int c = 0; c < NS; ++c) acc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nstage = K / KC;
-    load_a(0);
+    load_a(0, 0);
     load_b(bcur, scur, 0);
-    store_a(0);
+    load_a(1, min(1, nstage - 1));
+    store_a(0, 0);
     __syncthreads();
 
-    // The loop body is branch-free: the last stage prefetches (and stores to the idle LDS
-    // buffer) a copy of itself, so the compiler can count outstanding loads exactly and keep
-    // the next stage's loads in flight across the whole compute of this one.
+    // The stage body is branch-free: the last stages prefetch (and store to the idle LDS
+    // buffer) copies of the last one, so the compiler can count outstanding loads exactly and
+    // keep the following stages' loads in flight across the whole compute of this one.  The
+    // loop runs two stages per iteration so that the A register sets alternate statically.
     const int lrow = lane & 15;
-    for (int st = 0; st < nstage; ++st) {
+    auto stage = [&](int st, int set_new, int set_old) {
         const int nxt = min(st + 1, nstage - 1);
-        load_a(nxt);
+        load_a(set_new, min(st + 2, nstage - 1));
         load_b(bnext, snext, nxt);
         // keep the prefetch at the top: the scheduler would otherwise sink the loads next to
         // their first use at the end of the stage and expose their full latency
@@ -389,7 +395,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
                 for (int c = 0; c < NS; ++c) bq[c] = bn[c];
             }
         }
-        store_a((st + 1) & 1);
+        store_a(set_old, (st + 1) & 1);
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < NS; ++c) {
@@ -398,7 +404,15 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
 #pragma unroll
             for (int q = 0; q < SCS; ++q) scur[c][q] = snext[c][q];
         }
+    };
+    for (int st = 0; st < nstage; st += 2) {
+        stage(st, 0, 1);
+        if (st + 1 < nstage) stage(st + 1, 1, 0);
     }
+#pragma unroll
+    for (int set = 0; set < 2; ++set)
+#pragma unroll
+        for (int i = 0; i < ACH; ++i) consume(areg[set][i]);
 
     // the last stage prefetched a repeat of itself, which nothing reads
 #pragma unroll
