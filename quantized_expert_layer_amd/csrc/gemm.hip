@@ -244,6 +244,10 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmP
 // extra registers cost more than the longer cover of the next stage's load latency.
 template <int WT> constexpr int tile_kc() { return WT == MOE_W_FP16 ? 64 : 128; }
 
+// A stages held in LDS: a ring of three for integer codes (loaded straight into LDS, two stages
+// ahead), two for fp16 weights (register-staged).
+template <int WT> constexpr int tile_a_stages() { return WT == MOE_W_FP16 ? 2 : 3; }
+
 // Epilogue staging: row stride (halves) of a wave's output region in LDS, padded by 16 bytes
 // so the 16 rows of one fragment store start in different banks.
 template <int ACT, int NS> constexpr int tile_epi_stride() {
@@ -251,7 +255,7 @@ template <int ACT, int NS> constexpr int tile_epi_stride() {
 }
 // LDS of one block: the double-buffered A stages, or the 4 waves' epilogue regions if larger.
 template <int WT, int ACT, int MS, int NS> constexpr int tile_lds_halves() {
-    const int stages = 2 * 16 * MS * tile_kc<WT>();
+    const int stages = tile_a_stages<WT>() * 16 * MS * tile_kc<WT>();
     const int epi = 4 * 16 * MS * tile_epi_stride<ACT, NS>();
     return stages > epi ? stages : epi;
 }
@@ -300,7 +304,36 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
     const int G = GROUPED ? K / 128 : 1;
     const uint16_t* sp = p.scales + (size_t)e * G * N;
 
-    // A staging addresses: chunk q = threadIdx.x + 256 i -> row q / CPR, chunk q % CPR
+    // A staging.  With integer codes (DMA_A) the A stages go straight from memory into an LDS
+    // ring of AD buffers (global_load_lds: lane i of a wave-wide load writes bytes 16 i ..
+    // 16 i + 15 after the wave's LDS base), two stages ahead, with no registers or LDS store
+    // instructions of their own.  Chunk q of a buffer (16 bytes; row q / CPR, position
+    // q % CPR) receives the row's chunk (q % CPR) ^ (row & (CPR - 1)), the same swizzle the
+    // fragment reads below undo.  Rows past the tile repeat its last row.  Each wave issues NA
+    // wave-wide loads per stage.  fp16 weights, whose per-stage weight loads are four times
+    // larger, keep the register-staged path below, which measured faster for them.
+    constexpr bool DMA_A = WT != MOE_W_FP16;
+    constexpr int AD = tile_a_stages<WT>();
+    constexpr int NAB = (ATOT > 256 ? ATOT : 256) / kWave;   // wave-wide loads per stage
+    constexpr int NA = NAB / 4;
+    static_assert(NAB % 4 == 0 && LDS_BUF * 2 >= NAB * 1024, "DMA stage layout");
+    const char* adma[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const int q = (wave * NA + i) * kWave + lane;
+        const int r = q / CPR, cp = q % CPR;
+        const int c = cp ^ (r & (CPR - 1));
+        adma[i] = (const char*)(p.a + (size_t)a_source_row(p, row0 + min(r, rows - 1)) * K) + c * 16;
+    }
+    auto dma_a = [&](int st, int buf) {
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+            __builtin_amdgcn_global_load_lds(
+                adma[i] + (size_t)st * KC * 2,
+                (__attribute__((address_space(3))) void*)(lds + buf * LDS_BUF + (wave * NA + i) * 512),
+                16, 0, 0);
+    };
+    // register-staged A: chunk q = threadIdx.x + 256 i -> row q / CPR, chunk q % CPR
     const u32x4* asrc[ACH];
     int adst[ACH];
 #pragma unroll
@@ -348,25 +381,9 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         for (int c = 0; c < NS; ++c) acc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nstage = K / KC;
-    load_a(0, 0);
-    load_b(bcur, scur, 0);
-    load_a(1, min(1, nstage - 1));
-    store_a(0, 0);
-    __syncthreads();
-
-    // The stage body is branch-free: the last stages prefetch (and store to the idle LDS
-    // buffer) copies of the last one, so the compiler can count outstanding loads exactly and
-    // keep the following stages' loads in flight across the whole compute of this one.  The
-    // loop runs two stages per iteration so that the A register sets alternate statically.
     const int lrow = lane & 15;
-    auto stage = [&](int st, int set_new, int set_old) {
-        const int nxt = min(st + 1, nstage - 1);
-        load_a(set_new, min(st + 2, nstage - 1));
-        load_b(bnext, snext, nxt);
-        // keep the prefetch at the top: the scheduler would otherwise sink the loads next to
-        // their first use at the end of the stage and expose their full latency
-        __builtin_amdgcn_sched_barrier(0);
-        const f16* abuf = lds + (st & 1) * LDS_BUF;
+    // one stage's MFMAs from the A stage in abuf and the weights in bcur / scur
+    auto compute_stage = [&](const f16* abuf) {
         // the weight fragments of K-step ks+1 are expanded while the MFMAs of ks issue
         auto expand = [&](f16x8 (&bq)[NS], int ks) {
 #pragma unroll
@@ -395,8 +412,8 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
                 for (int c = 0; c < NS; ++c) bq[c] = bn[c];
             }
         }
-        store_a(set_old, (st + 1) & 1);
-        __syncthreads();
+    };
+    auto advance_b = [&] {
 #pragma unroll
         for (int c = 0; c < NS; ++c) {
 #pragma unroll
@@ -405,14 +422,75 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
             for (int q = 0; q < SCS; ++q) scur[c][q] = snext[c][q];
         }
     };
-    for (int st = 0; st < nstage; st += 2) {
-        stage(st, 0, 1);
-        if (st + 1 < nstage) stage(st + 1, 1, 0);
+
+    if constexpr (DMA_A) {
+        // prologue: A stages 0 .. AD-2, then the weights of stage 0
+#pragma unroll
+        for (int s0 = 0; s0 < AD - 1; ++s0) dma_a(min(s0, nstage - 1), s0);
+        load_b(bcur, scur, 0);
+
+        // Waits.  Per stage a wave issues, in this order, NB weight / scale loads (stage
+        // st + 1) and NA A loads (stage st + AD - 1); vector memory loads complete in order, so
+        // once at most (AD - 2) * NA + NB loads are outstanding, this wave's A loads of stage
+        // st are done.  The barrier after the wait makes every wave's A loads of stage st
+        // visible and frees the buffer stage st - 1 used, which the stage's new A loads
+        // overwrite.  (The barrier is issued bare: the compiler's fence before a block barrier
+        // would wait for all A loads in flight.)  The count holds for the first stages too,
+        // whose prologue order is the A stages 0 .. AD - 2, then the weights of stage 0.
+        constexpr int NB = NS * SBPS * (GROUPED ? 2 : 1);
+        constexpr int NWAIT = (AD - 2) * NA + NB;
+        static_assert(NWAIT < 64, "vmcnt field");
+        constexpr int WAITCNT = (NWAIT & 15) | ((NWAIT >> 4) << 14) | (7 << 4) | (15 << 8);
+
+        for (int st = 0; st < nstage; ++st) {
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(WAITCNT);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            const int nxt = min(st + 1, nstage - 1);
+            load_b(bnext, snext, nxt);
+            dma_a(min(st + AD - 1, nstage - 1), (st + AD - 1) % AD);
+            // keep the prefetch at the top: the scheduler would otherwise sink the loads next
+            // to their first use at the end of the stage and expose their full latency
+            __builtin_amdgcn_sched_barrier(0);
+            compute_stage(lds + (st % AD) * LDS_BUF);
+            advance_b();
+        }
+        // the last stages loaded repeats of the last one; they must land before the epilogue
+        // reuses the LDS
+        __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));
+        __syncthreads();
+    } else {
+        load_a(0, 0);
+        load_b(bcur, scur, 0);
+        load_a(1, min(1, nstage - 1));
+        store_a(0, 0);
+        __syncthreads();
+
+        // The stage body is branch-free: the last stages prefetch (and store to the idle LDS
+        // buffer) copies of the last one, so the compiler can count outstanding loads exactly
+        // and keep the following stages' loads in flight across the whole compute of this one.
+        // The loop runs two stages per iteration so the A register sets alternate statically.
+        auto stage = [&](int st, int set_new, int set_old) {
+            const int nxt = min(st + 1, nstage - 1);
+            load_a(set_new, min(st + 2, nstage - 1));
+            load_b(bnext, snext, nxt);
+            // keep the prefetch at the top (see above)
+            __builtin_amdgcn_sched_barrier(0);
+            compute_stage(lds + (st & 1) * LDS_BUF);
+            store_a(set_old, (st + 1) & 1);
+            __syncthreads();
+            advance_b();
+        };
+        for (int st = 0; st < nstage; st += 2) {
+            stage(st, 0, 1);
+            if (st + 1 < nstage) stage(st + 1, 1, 0);
+        }
+#pragma unroll
+        for (int set = 0; set < 2; ++set)
+#pragma unroll
+            for (int i = 0; i < ACH; ++i) consume(areg[set][i]);
     }
-#pragma unroll
-    for (int set = 0; set < 2; ++set)
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) consume(areg[set][i]);
 
     // the last stage prefetched a repeat of itself, which nothing reads
 #pragma unroll
