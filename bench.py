@@ -98,11 +98,11 @@ def attainable(q, torch, dev):
 
     t_read = timed(lambda: q.moe_probe_read(buf, 8 * cus, sink=sink))
     t_mfma = timed(lambda: q.moe_probe_mfma(iters, 2 * cus, out=out))
-    flops = 2 * cus * 4 * iters * 8 * 16384.0
+    flops = 2 * cus * 4 * iters * 16 * 16384.0
     del buf
     return {"hbm_read_GBps": (1 << 30) / t_read / 1e9, "mfma_f16_TFLOPs": flops / t_mfma / 1e12,
             "how": "library probes: 1 GiB read stream (4 x 16 B in flight per thread, "
-                   f"{8 * cus} blocks); {2 * cus} blocks x 4 waves x {iters} x 8 independent "
+                   f"{8 * cus} blocks); {2 * cus} blocks x 4 waves x {iters} x 16 independent "
                    "MFMA 16x16x32 fp16"}
 
 

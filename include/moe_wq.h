@@ -237,9 +237,9 @@ size_t moe_decode_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int
  * moe_probe_read  -- reads `bytes` (a multiple of 16) at src once, grid-stride, four 16-byte
  *                    non-temporal loads in flight per thread, `blocks` blocks of 256 threads;
  *                    sink[b] (uint32 [blocks]) = XOR of the 32-bit words block b read.
- * moe_probe_mfma  -- `blocks` blocks of 4 waves, each wave `iters` x 8 independent
+ * moe_probe_mfma  -- `blocks` blocks of 4 waves, each wave `iters` x 16 independent
  *                    v_mfma_f32_16x16x32_f16 on all-ones operands (16384 flop each);
- *                    out[thread] (fp32 [blocks * 256]) = 256 * iters exactly.  iters < 65536.
+ *                    out[thread] (fp32 [blocks * 256]) = 512 * iters exactly.  iters < 32768.
  * Errors: MOE_ERR_INVALID for blocks < 1, a misaligned pointer or an out-of-range size.
  */
 int32_t moe_probe_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,

@@ -322,8 +322,8 @@ def moe_probe_read(src, blocks, sink=None, stream=None):
 
 
 def moe_probe_mfma(iters, blocks, out=None, device="cuda", stream=None):
-    """Attainable-MFMA probe: blocks x 4 waves x iters x 8 MFMA 16x16x32 fp16; returns the
-    fp32 [blocks * 256] result (every element 256 * iters)."""
+    """Attainable-MFMA probe: blocks x 4 waves x iters x 16 MFMA 16x16x32 fp16; returns the
+    fp32 [blocks * 256] result (every element 512 * iters)."""
     torch = _torch()
     if out is None:
         out = torch.empty(blocks * 256, dtype=torch.float32, device=device)

@@ -192,10 +192,14 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_combine_kernel(Comb
         };
         auto consume_unit = [&](int slot) {
             if constexpr (GROUPED) {
-                f32x4 t = {0.f, 0.f, 0.f, 0.f};
+                // two interleaved chains (even / odd K-steps): a dependent MFMA chain stalls
+                f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < KSTEPS; ++j)
-                    t = mfma16x16x32(araw[slot][j], weight_frag<WT, false>(braw[slot], j, one2, k4), t);
+                for (int j = 0; j < KSTEPS; ++j) {
+                    if (j & 1) t1 = mfma16x16x32(araw[slot][j], weight_frag<WT, false>(braw[slot], j, one2, k4), t1);
+                    else t0 = mfma16x16x32(araw[slot][j], weight_frag<WT, false>(braw[slot], j, one2, k4), t0);
+                }
+                const f32x4 t = t0 + t1;
                 const float s = f16_bits_to_f32((uint16_t)sraw[slot]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(t[i], s, acc[i]);

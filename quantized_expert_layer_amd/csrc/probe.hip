@@ -30,23 +30,25 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict
     if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
-// Each wave runs 8 independent chains of v_mfma_f32_16x16x32_f16 on all-ones operands, so
-// every MFMA adds exactly 32 to each accumulator element; out[thread] = sum over the chains of
-// element 0 = 8 * 32 * iters (exact in fp32 for iters < 2^16).
+// Each wave runs 16 independent chains of v_mfma_f32_16x16x32_f16 on all-ones operands (the
+// form needs about 16 accumulators in flight per wave to issue at full rate; 8 reach about
+// 60% of it), so every MFMA adds exactly 32 to each accumulator element; out[thread] = sum
+// over the chains of element 0 = 16 * 32 * iters (exact in fp32 for iters < 2^15).
+constexpr int kProbeChains = 16;
 __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* __restrict__ out) {
     f16x8 a, b;
 #pragma unroll
     for (int i = 0; i < 8; ++i) { a[i] = (f16)1.0f; b[i] = (f16)1.0f; }
-    f32x4 acc[8];
+    f32x4 acc[kProbeChains];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < kProbeChains; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = mfma16x16x32(a, b, acc[c]);
+        for (int c = 0; c < kProbeChains; ++c) acc[c] = mfma16x16x32(a, b, acc[c]);
     }
     float v = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) v += acc[c][0];
+    for (int c = 0; c < kProbeChains; ++c) v += acc[c][0];
     out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = v;
 }
 
@@ -67,7 +69,7 @@ int32_t moe_probe_read(const void* src, size_t bytes, uint32_t* sink, int32_t bl
 }
 
 int32_t moe_probe_mfma(int32_t iters, float* out, int32_t blocks, void* stream) {
-    if (blocks < 1 || iters < 0 || iters >= (1 << 16)) return MOE_ERR_INVALID;
+    if (blocks < 1 || iters < 0 || iters >= (1 << 15)) return MOE_ERR_INVALID;
     if (!out || ((uintptr_t)out & 3u) != 0) return MOE_ERR_INVALID;
     if (int32_t st = moe::device_status()) return st;
     moe::probe_mfma_kernel<<<(unsigned)blocks, 256, 0, (hipStream_t)stream>>>(iters, out);

@@ -257,7 +257,7 @@ def test_probe_validation():
     assert L.moe_probe_read(MIS, 64, FAKE, 8, None) == q.MOE_ERR_INVALID
     assert L.moe_probe_read(None, 0, None, 8, None) == q.MOE_OK                 # nothing to read
     assert L.moe_probe_mfma(-1, FAKE, 8, None) == q.MOE_ERR_INVALID
-    assert L.moe_probe_mfma(1 << 16, FAKE, 8, None) == q.MOE_ERR_INVALID
+    assert L.moe_probe_mfma(1 << 15, FAKE, 8, None) == q.MOE_ERR_INVALID
     assert L.moe_probe_mfma(4, FAKE, 0, None) == q.MOE_ERR_INVALID
     if not gpu_available():
         assert L.moe_probe_mfma(4, FAKE, 8, None) == q.MOE_ERR_NO_DEVICE

@@ -21,4 +21,4 @@ def test_probe_read_xors_every_word():
 def test_probe_mfma_sums_exactly():
     case("probe mfma")
     out = q.moe_probe_mfma(300, 5).cpu().numpy()
-    assert out.shape == (5 * 256,) and np.all(out == 256.0 * 300)
+    assert out.shape == (5 * 256,) and np.all(out == 512.0 * 300)
