@@ -193,17 +193,24 @@ def shared_ffn(x: np.ndarray, shared):
 # [S] Method steps, step 5: grouping tokens by expert and scattering back is equivalent to
 # this per-token definition.
 # --------------------------------------------------------------------------------------
-def moe_layer_tokens(inp, tokens, gate_mode=None, act=None):
+def moe_layer_tokens(inp, tokens, gate_mode=None, act=None, active=None):
     """Layer output (fp64) for the token rows `tokens` only.  Each token needs only its own
-    x row and logits; experts are dequantized one at a time to bound memory."""
+    x row and logits; experts are dequantized one at a time to bound memory.
+
+    active (bool [T] or None): batch pruning ([W] Fig. 1 caption and the list of
+    optimizations: a finished sentence is left out of the computation).  A finished token
+    takes no routed expert, so its row is the shared experts' output alone (0 without
+    shared experts)."""
     cfg = inp.cfg
     gate_mode = gate_mode or cfg.gate_mode
     act = act or cfg.act
     tokens = np.asarray(tokens, dtype=np.int64)
     ids, w = topk_route(inp.logits[tokens], cfg.k, gate_mode)
+    running = np.ones(tokens.size, dtype=bool) if active is None else \
+        np.asarray(active, dtype=bool)[tokens]
     x = inp.x[tokens]
     out = np.zeros((tokens.size, cfg.d), dtype=np.float64)
-    for e in np.unique(ids):
+    for e in np.unique(ids[running]):
         if inp.wtype == "fp16":
             # unquantized experts (the FP16 baseline of [W] section 4's quantized-vs-FP16
             # comparison): the weights are used as they are
@@ -211,7 +218,7 @@ def moe_layer_tokens(inp, tokens, gate_mode=None, act=None):
         else:
             w1 = dequant_algorithm1(inp.codes1[e:e + 1], inp.scales1[e:e + 1], cfg.group)[0]
             w2 = dequant_algorithm1(inp.codes2[e:e + 1], inp.scales2[e:e + 1], cfg.group)[0]
-        rows, slots = np.nonzero(ids == e)
+        rows, slots = np.nonzero((ids == e) & running[:, None])
         y = expert_ffn(x[rows], w1, w2, act)
         out[rows] += w[rows, slots][:, None] * y
     if inp.shared:
@@ -219,6 +226,6 @@ def moe_layer_tokens(inp, tokens, gate_mode=None, act=None):
     return out
 
 
-def moe_layer(inp, gate_mode=None, act=None):
-    """Layer output (fp64) for all T tokens."""
-    return moe_layer_tokens(inp, np.arange(inp.T), gate_mode=gate_mode, act=act)
+def moe_layer(inp, gate_mode=None, act=None, active=None):
+    """Layer output (fp64) for all T tokens (active: batch pruning, as above)."""
+    return moe_layer_tokens(inp, np.arange(inp.T), gate_mode=gate_mode, act=act, active=active)

@@ -85,14 +85,15 @@ def brute_ffn(a, w1, w2, act):
 
 
 def brute_layer(x, logits, codes1, scales1, codes2, scales2, group, k, gate_mode, act,
-                shared=()):
-    """All arguments are nested Python lists of Python numbers."""
+                shared=(), active=None):
+    """All arguments are nested Python lists of Python numbers.  active: list of 0/1 per
+    token or None; a finished token (0) takes no routed expert."""
     T = len(x)
     cache = {}
     out = []
     for t in range(T):
-        ids = brute_topk(logits[t], k)
-        w = brute_gate_weights(logits[t], ids, gate_mode)
+        ids = brute_topk(logits[t], k) if active is None or active[t] else []
+        w = brute_gate_weights(logits[t], ids, gate_mode) if ids else []
         acc = [0.0] * len(x[t])
         for e, we in zip(ids, w):
             if e not in cache:

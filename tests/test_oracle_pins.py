@@ -275,6 +275,46 @@ def test_swiglu_layer_vs_brute_force_with_shared():
     np.testing.assert_allclose(got, np.array(ref), rtol=1e-11, atol=1e-12 * np.abs(ref).max())
 
 
+# ---------------------------------------------------------------- batch pruning pins
+# [W] Fig. 1 caption and the list of optimizations: a finished sentence is left out of the
+# computation.  A finished token takes no routed expert; the shared experts still apply.
+def test_pruned_layer_vs_brute_force():
+    cfg = synth.LayerConfig("tiny_swiglu", 9, d=128, inter=128, E=6, k=3, act="swiglu",
+                            wtypes=("int4",), group=128, gate_mode="all", zipf_bias=True,
+                            T_list=(6,), n_shared=2, shared_inter=64)
+    inp = synth.make_inputs(cfg, 6)
+    active = [1, 0, 1, 1, 0, 0]
+    got = oracle.moe_layer(inp, active=np.array(active, dtype=bool))
+    shared = [(_lists(w1), _lists(w2)) for w1, w2 in inp.shared]
+    ref = brute.brute_layer(_lists(inp.x), _lists(inp.logits), inp.codes1.tolist(),
+                            _lists(inp.scales1), inp.codes2.tolist(), _lists(inp.scales2),
+                            128, 3, "all", "swiglu", shared, active=active)
+    np.testing.assert_allclose(got, np.array(ref), rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+
+
+def test_pruning_special_cases():
+    inp = synth.make_inputs(synth.get_config("tiny"), 16)
+    full = oracle.moe_layer(inp)
+    # nothing pruned: the plain layer
+    assert np.array_equal(oracle.moe_layer(inp, active=np.ones(16, bool)), full)
+    # everything pruned, no shared experts: zeros
+    assert np.array_equal(oracle.moe_layer(inp, active=np.zeros(16, bool)), np.zeros_like(full))
+    # tokens are independent: running rows equal the unpruned rows, finished rows are 0
+    active = np.random.default_rng(4).random(16) < 0.5
+    part = oracle.moe_layer(inp, active=active)
+    np.testing.assert_allclose(part[active], full[active], rtol=1e-13, atol=1e-15)
+    assert np.array_equal(part[~active], np.zeros_like(part[~active]))
+
+
+def test_pruned_rows_keep_the_shared_experts():
+    cfg = synth.LayerConfig("tiny_swiglu", 9, d=128, inter=128, E=6, k=3, act="swiglu",
+                            wtypes=("int4",), group=128, gate_mode="all", zipf_bias=True,
+                            T_list=(5,), n_shared=2, shared_inter=64)
+    inp = synth.make_inputs(cfg, 5)
+    out = oracle.moe_layer(inp, active=np.zeros(5, bool))
+    assert np.array_equal(out, oracle.shared_ffn(inp.x, inp.shared))
+
+
 # ---------------------------------------------------------------- grouped GEMM / FFN pins
 def test_grouped_gemm_one_hot_rows_reproduce_weight_rows():
     inp = synth.make_inputs(synth.get_config("tiny"), 16, coverage=True)
