@@ -65,6 +65,11 @@ def parse():
     ap.add_argument("--no-decode", action="store_true",
                     help="run a decode-sized step as the five separate calls instead of one "
                          "moe_decode_layer call")
+    ap.add_argument("--finished", type=float, default=0.0,
+                    help="batch pruning: this fraction of the sentences is finished (their tokens "
+                         "take no expert); seeded, whole sentences of --sentence-len tokens")
+    ap.add_argument("--sentence-len", type=int, default=40,
+                    help="tokens per sentence for --finished (40: the MT workload's sentences)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-graph", action="store_true",
@@ -156,13 +161,20 @@ def main():
     ws = layer.workspace(T)
     x = torch.from_numpy(inp.x).to(dev)
     logits = torch.from_numpy(inp.logits).to(dev)
+    active = None
+    if args.finished > 0:
+        # whole sentences finish ("Who Says Elephants Can't Run", batch pruning), seeded
+        n_sent = (T + args.sentence_len - 1) // args.sentence_len
+        fin = np.random.default_rng(20261202 + T).random(n_sent) < args.finished
+        running = ~np.repeat(fin, args.sentence_len)[:T]
+        active = torch.from_numpy(running.astype(np.uint8)).to(dev)
 
     # weight rotation: enough copies that each step reads weights the caches do not hold
     wbytes = layer.w1.numel() + layer.w2.numel()
     n_copies = max(1, int(np.ceil(args.rotate_gb * 1e9 / wbytes)))
     copies = [(layer.w1, layer.w2)] + [(layer.w1.clone(), layer.w2.clone())
                                        for _ in range(n_copies - 1)]
-    plans = [layer.plan(ws, x, logits, weights=c) for c in copies]
+    plans = [layer.plan(ws, x, logits, weights=c, active=active) for c in copies]
     names = plans[0].names
 
     if args.calib_copy_mb:
@@ -194,13 +206,14 @@ def main():
         stage_us[nm] = float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]) * 1e3)
 
     # algorithmic work of the two grouped GEMM launches (rows per expert from the routing)
-    counts = np.bincount(ws.bufs["ids"].cpu().numpy().ravel(), minlength=cfg.E)
-    active = int((counts > 0).sum())
-    R = T * cfg.k
+    ids_h = ws.bufs["ids"].cpu().numpy().ravel()
+    counts = np.bincount(ids_h[ids_h >= 0], minlength=cfg.E)
+    n_active = int((counts > 0).sum())
+    R = int(counts.sum())                       # routed rows (finished tokens route nowhere)
     per_expert_w1 = layer.w1.numel() // cfg.E + (0 if inp.scales1 is None else 2 * inp.scales1[0].size)
     per_expert_w2 = layer.w2.numel() // cfg.E + (0 if inp.scales2 is None else 2 * inp.scales2[0].size)
-    g1 = {"flops": 2.0 * R * cfg.d * layer.n1, "bytes": active * per_expert_w1}
-    g2 = {"flops": 2.0 * R * cfg.inter * cfg.d, "bytes": active * per_expert_w2}
+    g1 = {"flops": 2.0 * R * cfg.d * layer.n1, "bytes": n_active * per_expert_w1}
+    g2 = {"flops": 2.0 * R * cfg.inter * cfg.d, "bytes": n_active * per_expert_w2}
     if "decode" in stage_us:
         # one moe_decode_layer call (gating + sort, GEMM 1, GEMM 2 with the combine): its
         # events bracket all three launches, so the unit is the whole call
@@ -223,7 +236,8 @@ def main():
     roof["avg_us"] = dom_us
     traffic = None
     src_hash = kernel_source_hash()
-    workload = f"{cfg.name}_{args.wtype}_T{T}" + (f"_A{args.active}" if args.active else "")
+    workload = f"{cfg.name}_{args.wtype}_T{T}" + (f"_A{args.active}" if args.active else "") + \
+        (f"_fin{args.finished:g}" if args.finished else "")
     if os.path.exists(TRAFFIC_FILE):
         try:
             rec = json.load(open(TRAFFIC_FILE)).get(workload, {})
@@ -241,7 +255,7 @@ def main():
         # one graph per weight copy, captured on a side stream; replays are checked against
         # the eager output of the same weights before they are timed
         gs = torch.cuda.Stream()
-        gplans = [layer.plan(ws, x, logits, weights=c, stream=gs) for c in copies]
+        gplans = [layer.plan(ws, x, logits, weights=c, stream=gs, active=active) for c in copies]
         graphs = []
         ref_out = None
         for gp in gplans:
@@ -295,7 +309,8 @@ def main():
         "config": {"workload": workload, "d": cfg.d, "ffn": cfg.inter, "act": cfg.act,
                    "experts": cfg.E, "top_k": cfg.k, "tokens": T, "weights": args.wtype,
                    "group": cfg.group or "per-channel", "gate": cfg.gate_mode,
-                   "active_experts": active, "max_rows_per_expert": int(counts.max()),
+                   "active_experts": n_active, "max_rows_per_expert": int(counts.max()),
+                   "finished_fraction": float(args.finished), "routed_rows": R,
                    "weight_copies_rotated": n_copies, "parallelism": "single-gpu"},
         "roofline": roof,
         "attainable": att,

@@ -99,6 +99,21 @@ int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int
                        int32_t* topk_ids, float* topk_w, void* stream);
 
 /*
+ * moe_route_topk_active -- moe_route_topk with batch pruning.  [W] Fig. 1 and its list of
+ * optimizations: with batch pruning, finished sentences are removed from the computation, so
+ * experts that only they would use load no weights.
+ *
+ *   active    uint8 [T] or NULL (= all active): a token with active[t] == 0 is finished; its k
+ *             slots get topk_ids -1 and topk_w 0.  moe_permute drops such slots (no rows, so an
+ *             expert with only finished tokens reads no weights), and moe_unpermute_combine
+ *             then writes the token's row as fp16(addend[t]) (0 without an addend).
+ *   Everything else as moe_route_topk, which is this call with active = NULL.
+ */
+int32_t moe_route_topk_active(const float* logits, const uint8_t* active, int32_t T, int32_t E,
+                              int32_t k, int32_t gate_mode, int32_t* topk_ids, float* topk_w,
+                              void* stream);
+
+/*
  * moe_permute -- stable counting sort of routed rows by expert, then row gather.
  *   [W] section 3 workflow: the row index is attached to the gating output, the tuples are
  *   sorted with the expert index as key, and the activation matrix is permuted.
@@ -116,8 +131,10 @@ int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int
  *   w_perm          fp32  [T*k]   out (optional): w_perm[p] = topk_w.flat[perm[p]]
  *   ws, ws_bytes    workspace of at least moe_permute_workspace_size(T, k, E) bytes
  *                   (currently 0: NULL allowed)
- *   Requires 1 <= E <= 256, 1 <= k <= 8, d % 8 == 0.  Ids outside [0, E) are a caller
- *   error: their rows are dropped from the output (no fault), offsets[E] then < T*k.
+ *   Requires 1 <= E <= 256, 1 <= k <= 8, d % 8 == 0.  A slot whose id is outside [0, E)
+ *   (-1 from moe_route_topk_active for a finished token) is not routed: it gets no sorted
+ *   position (inv_perm -1), and offsets[E] = the number of routed slots < T*k; the positions
+ *   from offsets[E] on hold perm -1 (and w_perm 0).
  */
 int32_t moe_permute(const int32_t* topk_ids, const float* topk_w, const uint16_t* x,
                     int32_t T, int32_t k, int32_t E, int32_t d,
@@ -202,6 +219,8 @@ int32_t moe_grouped_gemm_wq_rows(const uint16_t* a, int32_t a_nrows, const int32
  *   scatters the results back.  [W] section 3 workflow and Algorithm 1 as for the calls above.
  *
  *   logits    fp32 [T, E]      router logits;  x fp16 [T, d]  token activations
+ *   active    uint8 [T] or NULL: batch pruning as for moe_route_topk_active (a finished token
+ *             takes no expert, its output row is fp16(addend[t]) or 0)
  *   gate_mode enum moe_gate;   act: MOE_ACT_NONE / RELU (W1 is [d, inter]) or SWIGLU (W1 is
  *             [d, 2*inter], columns [gate | up])
  *   w1, s1    first-GEMM weights packed by moe_pack_wq for (wtype, E, d, inter or 2*inter) and
@@ -220,8 +239,9 @@ int32_t moe_grouped_gemm_wq_rows(const uint16_t* a, int32_t a_nrows, const int32
  * d % 128 != 0 or inter % 128 != 0, group_size not in {0, 128} (0 for FP16); otherwise as
  * moe_route_topk and moe_grouped_gemm_wq; MOE_ERR_WORKSPACE for a missing or short workspace.
  */
-int32_t moe_decode_layer(const float* logits, const uint16_t* x, int32_t T, int32_t E,
-                         int32_t k, int32_t gate_mode, int32_t d, int32_t inter, int32_t act,
+int32_t moe_decode_layer(const float* logits, const uint8_t* active, const uint16_t* x,
+                         int32_t T, int32_t E, int32_t k, int32_t gate_mode, int32_t d,
+                         int32_t inter, int32_t act,
                          const void* w1, const uint16_t* s1, const void* w2,
                          const uint16_t* s2, int32_t wtype, int32_t group_size,
                          const uint16_t* addend, int32_t* topk_ids, float* topk_w,

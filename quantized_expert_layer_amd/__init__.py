@@ -21,7 +21,8 @@ __all__ = [
     "ACT_SWIGLU", "PATH_AUTO", "PATH_STREAM", "PATH_TILE", "TILE_AUTO", "TILE_64x256",
     "TILE_64x128", "TILE_128x128", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SPLIT_K",
     "MoEError", "MoELibraryError", "lib", "lib_path", "status_str", "version",
-    "moe_route_topk", "moe_permute", "moe_grouped_gemm_wq", "moe_grouped_gemm_wq_rows",
+    "moe_route_topk", "moe_route_topk_active", "moe_permute", "moe_grouped_gemm_wq",
+    "moe_grouped_gemm_wq_rows",
     "moe_unpermute_combine",
     "moe_dequant", "moe_pack_wq", "moe_packed_bytes", "moe_gemm_workspace_size",
     "moe_permute_workspace_size", "GemmOpts", "EXPORTED_SYMBOLS", "new_output",
@@ -50,7 +51,7 @@ EXPORTED_SYMBOLS = (
     "moe_route_topk", "moe_permute", "moe_permute_workspace_size", "moe_grouped_gemm_wq",
     "moe_grouped_gemm_wq_rows", "moe_gemm_workspace_size", "moe_unpermute_combine", "moe_dequant", "moe_packed_bytes",
     "moe_pack_wq", "moe_status_str", "moe_version", "moe_probe_read", "moe_probe_mfma",
-    "moe_decode_layer", "moe_decode_workspace_size",
+    "moe_decode_layer", "moe_decode_workspace_size", "moe_route_topk_active",
 )
 
 
@@ -111,8 +112,9 @@ def lib():
         "moe_version": (_I, []),
         "moe_probe_read": (_I, [_P, _SZ, _P, _I, _P]),
         "moe_probe_mfma": (_I, [_I, _P, _I, _P]),
-        "moe_decode_layer": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I,
-                                  _P, _P, _P, _P, _P, _SZ, _P]),
+        "moe_decode_layer": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I,
+                                  _I, _P, _P, _P, _P, _P, _SZ, _P]),
+        "moe_route_topk_active": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
         "moe_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     }
     for name, (res, args) in sig.items():
@@ -193,7 +195,8 @@ def _opts(path=PATH_AUTO, split_k=0, tile=TILE_AUTO):
 
 
 # ---------------------------------------------------------------- the five calls
-def moe_route_topk(logits, k, gate_mode, topk_ids=None, topk_w=None, stream=None):
+def moe_route_topk(logits, k, gate_mode, topk_ids=None, topk_w=None, stream=None, active=None):
+    """active (uint8 [T] device tensor or None): batch pruning, moe_route_topk_active."""
     torch = _torch()
     T, E = logits.shape
     gm = GATES.get(gate_mode, gate_mode)
@@ -204,8 +207,14 @@ def moe_route_topk(logits, k, gate_mode, topk_ids=None, topk_w=None, stream=None
     _need(logits, torch.float32, "logits")
     _need(topk_ids, torch.int32, "topk_ids", T * k)
     _need(topk_w, torch.float32, "topk_w", T * k)
-    _check("moe_route_topk", lib().moe_route_topk(_ptr(logits), T, E, k, gm, _ptr(topk_ids),
-                                                  _ptr(topk_w), _stream(stream)))
+    if active is None:
+        _check("moe_route_topk", lib().moe_route_topk(_ptr(logits), T, E, k, gm, _ptr(topk_ids),
+                                                      _ptr(topk_w), _stream(stream)))
+    else:
+        _need(active, torch.uint8, "active", T)
+        _check("moe_route_topk_active", lib().moe_route_topk_active(
+            _ptr(logits), _ptr(active), T, E, k, gm, _ptr(topk_ids), _ptr(topk_w),
+            _stream(stream)))
     return topk_ids, topk_w
 
 
@@ -338,7 +347,8 @@ def moe_decode_workspace_size(T, k, E, d, inter, wtype):
 
 
 def moe_decode_layer(logits, x, k, gate_mode, inter, act, w1, s1, w2, s2, wtype, group_size,
-                     addend=None, topk_ids=None, topk_w=None, out=None, ws=None, stream=None):
+                     addend=None, topk_ids=None, topk_w=None, out=None, ws=None, stream=None,
+                     active=None):
     """The routed layer for a decode / verify step (T <= MOE_DECODE_MAX_TOKENS tokens).
     Returns (out fp16 [T, d], topk_ids int32 [T, k], topk_w fp32 [T, k])."""
     torch = _torch()
@@ -366,8 +376,9 @@ def moe_decode_layer(logits, x, k, gate_mode, inter, act, w1, s1, w2, s2, wtype,
     _need(topk_w, torch.float32, "topk_w", T * k)
     _need(out, torch.float16, "out", T * d)
     _need(ws, torch.uint8, "ws")
+    _need(active, torch.uint8, "active", T)
     _check("moe_decode_layer", lib().moe_decode_layer(
-        _ptr(logits), _ptr(x), T, E, k, GATES.get(gate_mode, gate_mode), d, int(inter),
+        _ptr(logits), _ptr(active), _ptr(x), T, E, k, GATES.get(gate_mode, gate_mode), d, int(inter),
         ACTS.get(act, act), _ptr(w1), _ptr(s1), _ptr(w2), _ptr(s2), wt, int(group_size),
         _ptr(addend), _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))

@@ -103,8 +103,9 @@ const char* moe_status_str(int32_t s) {
     }
 }
 
-int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t gate_mode,
-                       int32_t* topk_ids, float* topk_w, void* stream) {
+int32_t moe_route_topk_active(const float* logits, const uint8_t* active, int32_t T, int32_t E,
+                              int32_t k, int32_t gate_mode, int32_t* topk_ids, float* topk_w,
+                              void* stream) {
     if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E)
         return MOE_ERR_INVALID;
     if (gate_mode != MOE_GATE_SOFTMAX_TOPK && gate_mode != MOE_GATE_SOFTMAX_ALL)
@@ -114,8 +115,14 @@ int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int
     if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID;
     if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID;
     if (int32_t st = check_device()) return st;
-    return hip_status(moe::launch_route_topk(logits, T, E, k, gate_mode == MOE_GATE_SOFTMAX_ALL,
-                                             topk_ids, topk_w, (hipStream_t)stream));
+    return hip_status(moe::launch_route_topk(logits, active, T, E, k,
+                                             gate_mode == MOE_GATE_SOFTMAX_ALL, topk_ids, topk_w,
+                                             (hipStream_t)stream));
+}
+
+int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t gate_mode,
+                       int32_t* topk_ids, float* topk_w, void* stream) {
+    return moe_route_topk_active(logits, nullptr, T, E, k, gate_mode, topk_ids, topk_w, stream);
 }
 
 size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E) {
@@ -253,8 +260,9 @@ size_t moe_decode_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int
     return moe::decode_workspace_layout(T, k, E, d, inter, wtype, nullptr, nullptr);
 }
 
-int32_t moe_decode_layer(const float* logits, const uint16_t* x, int32_t T, int32_t E,
-                         int32_t k, int32_t gate_mode, int32_t d, int32_t inter, int32_t act,
+int32_t moe_decode_layer(const float* logits, const uint8_t* active, const uint16_t* x,
+                         int32_t T, int32_t E, int32_t k, int32_t gate_mode, int32_t d,
+                         int32_t inter, int32_t act,
                          const void* w1, const uint16_t* s1, const void* w2,
                          const uint16_t* s2, int32_t wtype, int32_t group_size,
                          const uint16_t* addend, int32_t* topk_ids, float* topk_w,
@@ -274,6 +282,7 @@ int32_t moe_decode_layer(const float* logits, const uint16_t* x, int32_t T, int3
     if (int32_t st = check_device()) return st;
     moe::DecodeArgs a;
     a.logits = logits;
+    a.active = active;
     a.x = x;
     a.T = T;
     a.E = E;

@@ -27,17 +27,18 @@ namespace moe {
 // ------------------------------------------------------------------------------------
 template <int PER_LANE>
 __global__ __launch_bounds__(kSortWaves * kWave) void decode_route_sort_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int gate_all,
-    int32_t* __restrict__ ids, float* __restrict__ wts, DecodeWs ws) {
+    const float* __restrict__ logits, const uint8_t* __restrict__ active, int T, int E, int k,
+    int gate_all, int32_t* __restrict__ ids, float* __restrict__ wts, DecodeWs ws) {
     __shared__ int keys[MOE_DECODE_MAX_ROWS];
     __shared__ float kw[MOE_DECODE_MAX_ROWS];
     __shared__ int cnt[MOE_MAX_EXPERTS];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     for (int t = wave; t < T; t += kSortWaves) {
-        int e;
-        float w;
-        topk_token<PER_LANE>(logits + (size_t)t * E, E, k, gate_all, lane, e, w);
+        int e = -1;              // a finished token (active[t] == 0) takes no expert
+        float w = 0.0f;
+        if (!active || active[t])
+            topk_token<PER_LANE>(logits + (size_t)t * E, E, k, gate_all, lane, e, w);
         if (lane < k) {
             ids[t * k + lane] = e;
             wts[t * k + lane] = w;
@@ -299,13 +300,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 
     if (a.E <= 64)
         decode_route_sort_kernel<1><<<1, kSortWaves * kWave, 0, stream>>>(
-            a.logits, a.T, a.E, a.k, a.gate_all, a.ids, a.wts, ws);
+            a.logits, a.active, a.T, a.E, a.k, a.gate_all, a.ids, a.wts, ws);
     else if (a.E <= 128)
         decode_route_sort_kernel<2><<<1, kSortWaves * kWave, 0, stream>>>(
-            a.logits, a.T, a.E, a.k, a.gate_all, a.ids, a.wts, ws);
+            a.logits, a.active, a.T, a.E, a.k, a.gate_all, a.ids, a.wts, ws);
     else
         decode_route_sort_kernel<4><<<1, kSortWaves * kWave, 0, stream>>>(
-            a.logits, a.T, a.E, a.k, a.gate_all, a.ids, a.wts, ws);
+            a.logits, a.active, a.T, a.E, a.k, a.gate_all, a.ids, a.wts, ws);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
 

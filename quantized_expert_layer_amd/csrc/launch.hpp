@@ -9,8 +9,8 @@ namespace moe {
 // MOE_OK when the current device is a usable gfx950, else MOE_ERR_NO_DEVICE (cached per device).
 int32_t device_status();
 
-hipError_t launch_route_topk(const float* logits, int T, int E, int k, int gate_all,
-                             int32_t* ids, float* wts, hipStream_t stream);
+hipError_t launch_route_topk(const float* logits, const uint8_t* active, int T, int E, int k,
+                             int gate_all, int32_t* ids, float* wts, hipStream_t stream);
 
 hipError_t launch_sort(const int32_t* ids, const float* wts, int R, int E,
                        int32_t* perm, int32_t* inv_perm, int32_t* offsets, float* w_perm,
@@ -75,6 +75,7 @@ struct CombineParams {
 
 struct DecodeArgs {
     const float* logits;
+    const uint8_t* active;   // [T] or NULL: tokens with 0 take no expert
     const uint16_t* x;
     int T, E, k, gate_all, d, inter, act;
     const void* w1;

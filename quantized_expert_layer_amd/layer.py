@@ -93,10 +93,12 @@ class DeviceLayer:
         return (self.decode is None and fits and self.gemm_path == 0 and self.gemm_tile == 0
                 and self.fuse_rows and gate_in_gemm)
 
-    def _scatter_out(self, gate_in_gemm: bool) -> bool:
+    def _scatter_out(self, gate_in_gemm: bool, pruned: bool = False) -> bool:
         """Whether the second GEMM writes the layer output itself: one expert per token, the
-        gate weight applied in the GEMM and nothing to add."""
-        return self.fuse_rows and self.k == 1 and gate_in_gemm and self.shared is None
+        gate weight applied in the GEMM and nothing to add.  Not with batch pruning: a finished
+        token has no row in the GEMM, and the combine writes its output row."""
+        return (self.fuse_rows and self.k == 1 and gate_in_gemm and self.shared is None
+                and not pruned)
 
     def workspace(self, T: int) -> Workspace:
         import torch
@@ -147,8 +149,10 @@ class DeviceLayer:
         ]
 
     def forward(self, x, logits, ws: Optional[Workspace] = None, gate_in_gemm: bool = True,
-                stream=None):
-        """Layer output fp16 [T, d] for x fp16 [T, d] and router logits fp32 [T, E]."""
+                stream=None, active=None):
+        """Layer output fp16 [T, d] for x fp16 [T, d] and router logits fp32 [T, E].
+        active: uint8 [T] device tensor or None; batch pruning (a token with 0 is finished,
+        takes no expert, and its output row is the shared experts' output, or 0)."""
         T = x.shape[0]
         if ws is None or ws.T != T:
             ws = self.workspace(T)
@@ -166,11 +170,12 @@ class DeviceLayer:
             moe_decode_layer(logits, x, self.k, self.gate_mode, self.inter, self.act, self.w1,
                              self.s1, self.w2, self.s2, self.wtype, self.group, addend=addend,
                              topk_ids=b["ids"], topk_w=b["w"], out=b["out"], ws=b["dws"],
-                             stream=stream)
+                             stream=stream, active=active)
             return b["out"]
-        moe_route_topk(logits, self.k, self.gate_mode, b["ids"], b["w"], stream=stream)
+        moe_route_topk(logits, self.k, self.gate_mode, b["ids"], b["w"], stream=stream,
+                       active=active)
         fused = self.fuse_rows
-        scatter = self._scatter_out(gate_in_gemm)
+        scatter = self._scatter_out(gate_in_gemm, active is not None)
         R = T * self.k
         moe_permute(b["ids"], b["w"], x, self.E,
                     out=(b["perm"], b["inv"], b["off"], None if fused else b["xp"], b["wp"]),
@@ -208,7 +213,7 @@ class DeviceLayer:
 
     # ------------------------------------------------------------------ cached launch plan
     def plan(self, ws: Workspace, x, logits, weights=None, gate_in_gemm: bool = True,
-             stream=None) -> "LayerPlan":
+             stream=None, active=None) -> "LayerPlan":
         """Pre-marshal every C call of one forward() for fixed buffers, so that a step is
         just the C calls (no per-call Python argument checks).  `weights` = (w1, w2) device
         tensors in the packed layout (defaults to this layer's own)."""
@@ -226,10 +231,10 @@ class DeviceLayer:
         wsp, wsn = _ptr(b["ws"]), b["ws"].numel()
         wt, ac = WTYPES[self.wtype], ACTS[self.act]
         fused = self.fuse_rows
-        scatter = self._scatter_out(gate_in_gemm)
+        scatter = self._scatter_out(gate_in_gemm, active is not None)
         R = T * self.k
         rs = _ptr(b["wp"]) if gate_in_gemm else None
-        keep = (opts, x, logits, w1, w2, self.s1, self.s2, self.shared, ws)
+        keep = (opts, x, logits, w1, w2, self.s1, self.s2, self.shared, ws, active)
         if self.uses_decode(T, gate_in_gemm):
             calls = []
             addend = None
@@ -237,14 +242,16 @@ class DeviceLayer:
                 calls = [(n, fn, args[:-1] + (st,)) for n, fn, args in self._shared_calls(b, x, T)]
                 addend = b["sh_y"]
             calls.append(("decode", L.moe_decode_layer,
-                          (_ptr(logits), _ptr(x), T, self.E, self.k, GATES[self.gate_mode],
-                           self.d, self.inter, ac, _ptr(w1), _ptr(self.s1), _ptr(w2),
-                           _ptr(self.s2), wt, self.group, _ptr(addend), _ptr(b["ids"]),
-                           _ptr(b["w"]), _ptr(b["out"]), _ptr(b["dws"]), b["dws"].numel(), st)))
+                          (_ptr(logits), _ptr(active), _ptr(x), T, self.E, self.k,
+                           GATES[self.gate_mode], self.d, self.inter, ac, _ptr(w1),
+                           _ptr(self.s1), _ptr(w2), _ptr(self.s2), wt, self.group, _ptr(addend),
+                           _ptr(b["ids"]), _ptr(b["w"]), _ptr(b["out"]), _ptr(b["dws"]),
+                           b["dws"].numel(), st)))
             return LayerPlan(calls, b["out"], keep=keep)
         calls = [
-            ("route", L.moe_route_topk, (_ptr(logits), T, self.E, self.k, GATES[self.gate_mode],
-                                         _ptr(b["ids"]), _ptr(b["w"]), st)),
+            ("route", L.moe_route_topk_active, (_ptr(logits), _ptr(active), T, self.E, self.k,
+                                                GATES[self.gate_mode], _ptr(b["ids"]),
+                                                _ptr(b["w"]), st)),
             ("permute", L.moe_permute, (_ptr(b["ids"]), _ptr(b["w"]), _ptr(x), T, self.k, self.E,
                                         self.d, _ptr(b["perm"]), _ptr(b["inv"]), _ptr(b["off"]),
                                         None if fused else _ptr(b["xp"]), _ptr(b["wp"]), None, 0,
@@ -265,8 +272,7 @@ class DeviceLayer:
                           (_ptr(b["h"]), R, None, 1, _ptr(b["off"]), R, self.E, self.inter, self.d,
                            _ptr(w2), _ptr(self.s2), wt, self.group, 0, rs, _ptr(b["out"]), T,
                            _ptr(b["perm"]), ob, wsp, wsn, st)))
-            return LayerPlan(calls, b["out"], keep=(opts, x, logits, w1, w2, self.s1, self.s2,
-                                                    self.shared, ws))
+            return LayerPlan(calls, b["out"], keep=keep)
         calls.append(("gemm2", L.moe_grouped_gemm_wq,
                       (_ptr(b["h"]), _ptr(b["off"]), R, self.E, self.inter, self.d, _ptr(w2),
                        _ptr(self.s2), wt, self.group, 0, rs, _ptr(b["y"]), ob, wsp, wsn, st)))
@@ -288,8 +294,7 @@ class DeviceLayer:
                        _ptr(addend), T, self.k, self.d, _ptr(b["out"]), st)))
         # the plan holds raw device pointers: keep every tensor they point into alive for as
         # long as the plan exists (the layer itself may be dropped by the caller)
-        return LayerPlan(calls, b["out"], keep=(opts, x, logits, w1, w2, self.s1, self.s2,
-                                                self.shared, ws))
+        return LayerPlan(calls, b["out"], keep=keep)
 
 
 class LayerPlan:

@@ -132,6 +132,18 @@ FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced on t
 MIS = ctypes.c_void_p(0x10002)        # misaligned
 
 
+def test_route_topk_active_validation():
+    L = q.lib()
+    f = L.moe_route_topk_active
+    assert f(FAKE, FAKE, 4, 8, 9, 0, FAKE, FAKE, None) == q.MOE_ERR_INVALID     # k > E
+    assert f(FAKE, FAKE, 4, 8, 2, 7, FAKE, FAKE, None) == q.MOE_ERR_INVALID     # gate mode
+    assert f(None, FAKE, 4, 8, 2, 0, FAKE, FAKE, None) == q.MOE_ERR_INVALID
+    assert f(None, None, 0, 8, 2, 0, None, None, None) == q.MOE_OK              # T = 0
+    if not gpu_available():
+        assert f(FAKE, None, 4, 8, 2, 0, FAKE, FAKE, None) == q.MOE_ERR_NO_DEVICE
+        assert f(FAKE, MIS, 4, 8, 2, 0, FAKE, FAKE, None) == q.MOE_ERR_NO_DEVICE   # bytes
+
+
 def test_route_topk_validation():
     L = q.lib()
     assert L.moe_route_topk(FAKE, 4, 8, 9, 0, FAKE, FAKE, None) == q.MOE_ERR_INVALID   # k > E
@@ -270,13 +282,13 @@ def test_decode_layer_validation():
     assert ws_need > 0
 
     def args(**kw):
-        d = dict(logits=FAKE, x=FAKE, T=4, E=8, k=2, gate=0, d=256, inter=512, act=2, w1=FAKE,
-                 s1=FAKE, w2=FAKE, s2=FAKE, wt=0, g=128, add=None, ids=FAKE, w=FAKE, out=FAKE,
-                 ws=FAKE, wsb=ws_need, stream=None)
+        d = dict(logits=FAKE, active=None, x=FAKE, T=4, E=8, k=2, gate=0, d=256, inter=512,
+                 act=2, w1=FAKE, s1=FAKE, w2=FAKE, s2=FAKE, wt=0, g=128, add=None, ids=FAKE,
+                 w=FAKE, out=FAKE, ws=FAKE, wsb=ws_need, stream=None)
         d.update(kw)
-        return [d[n] for n in ("logits", "x", "T", "E", "k", "gate", "d", "inter", "act", "w1",
-                               "s1", "w2", "s2", "wt", "g", "add", "ids", "w", "out", "ws", "wsb",
-                               "stream")]
+        return [d[n] for n in ("logits", "active", "x", "T", "E", "k", "gate", "d", "inter",
+                               "act", "w1", "s1", "w2", "s2", "wt", "g", "add", "ids", "w", "out",
+                               "ws", "wsb", "stream")]
 
     assert f(*args(k=9)) == q.MOE_ERR_INVALID
     assert f(*args(k=9, E=8)) == q.MOE_ERR_INVALID
