@@ -229,3 +229,32 @@ def moe_layer_tokens(inp, tokens, gate_mode=None, act=None, active=None):
 def moe_layer(inp, gate_mode=None, act=None, active=None):
     """Layer output (fp64) for all T tokens (active: batch pruning, as above)."""
     return moe_layer_tokens(inp, np.arange(inp.T), gate_mode=gate_mode, act=act, active=active)
+
+
+# ---------------------------------------------------------------- expert lookahead buffer
+def elb_accumulate(counts: np.ndarray, step_ids: np.ndarray, E: int) -> np.ndarray:
+    """One draft step of the expert lookahead buffer ("Specter" summary, Method steps, step 2:
+    ELB_cnt[j, e] = sum over draft steps i of [e in ELB_route[i, j]]).
+
+    counts int [L, E]; step_ids int [L, T, k] = the step's routing in each of L layers (T draft
+    tokens, k experts each).  Membership: an expert used by several tokens of the step counts
+    once.  Ids outside [0, E) (a finished token's -1) are not routing.  Returns new counts."""
+    out = np.array(counts, dtype=np.int64, copy=True)
+    ids = np.asarray(step_ids)
+    for j in range(ids.shape[0]):
+        lay = ids[j].ravel()
+        used = np.unique(lay[(lay >= 0) & (lay < E)])
+        out[j, used] += 1
+    return out
+
+
+def elb_top_m(counts: np.ndarray, M: int):
+    """The planner's snapshot ("Specter" summary, Method steps, step 3): per layer, the M experts
+    with the largest counts, ties to the smaller expert index.  Returns (experts [L, M],
+    their counts [L, M])."""
+    counts = np.asarray(counts)
+    L, E = counts.shape
+    experts = np.empty((L, M), dtype=np.int64)
+    for j in range(L):
+        experts[j] = np.lexsort((np.arange(E), -counts[j]))[:M]
+    return experts, np.take_along_axis(counts, experts, axis=1)

@@ -425,3 +425,47 @@ def test_fp16_expert_inputs_are_seeded_normals():
     assert abs(sd - 0.02) < 1e-3
     again = synth.make_inputs(synth.get_config("mt_encoder"), 8, wtype="fp16", active=2)
     assert np.array_equal(again.codes2[5], inp.codes2[5])
+
+
+# ---------------------------------------------------------------- expert lookahead buffer pins
+def _elb_golden(golden_dir):
+    g = {}
+    for line in open(os.path.join(golden_dir, "elb_worked_example.txt")):
+        line = line.split("#")[0].split()
+        if line:
+            g[line[0]] = np.array([int(v) for v in line[1:]])
+    return g
+
+
+def test_elb_worked_example(golden_dir):
+    g = _elb_golden(golden_dir)
+    counts = np.zeros((2, 5), dtype=np.int64)
+    counts = oracle.elb_accumulate(counts, g["step1"].reshape(2, 2, 2), 5)
+    counts = oracle.elb_accumulate(counts, g["step2"].reshape(2, 2, 2), 5)
+    assert np.array_equal(counts.ravel(), g["counts"])
+    ex, cn = oracle.elb_top_m(counts, 3)
+    assert np.array_equal(ex.ravel(), g["top3_experts"])
+    assert np.array_equal(cn.ravel(), g["top3_counts"])
+
+
+def test_elb_matches_the_counting_rule_brute_force():
+    """The definition written out with Python sets and loops, on random small inputs."""
+    rng = np.random.default_rng(11)
+    for trial in range(20):
+        L, T, k, E, steps = (int(rng.integers(1, 4)), int(rng.integers(1, 4)),
+                             int(rng.integers(1, 4)), int(rng.integers(1, 7)),
+                             int(rng.integers(1, 5)))
+        all_ids = rng.integers(-1, E, size=(steps, L, T, k))
+        counts = np.zeros((L, E), dtype=np.int64)
+        for i in range(steps):
+            counts = oracle.elb_accumulate(counts, all_ids[i], E)
+        for j in range(L):
+            for e in range(E):
+                want = sum(1 for i in range(steps)
+                           if e in {int(v) for v in all_ids[i, j].ravel()})
+                assert counts[j, e] == want
+        M = int(rng.integers(1, E + 1))
+        ex, cn = oracle.elb_top_m(counts, M)
+        for j in range(L):
+            ranked = sorted(range(E), key=lambda e: (-counts[j, e], e))[:M]
+            assert list(ex[j]) == ranked and list(cn[j]) == [counts[j, e] for e in ranked]
