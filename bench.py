@@ -70,6 +70,13 @@ def parse():
                          "take no expert); seeded, whole sentences of --sentence-len tokens")
     ap.add_argument("--sentence-len", type=int, default=40,
                     help="tokens per sentence for --finished (40: the MT workload's sentences)")
+    ap.add_argument("--workload", default="layer", choices=["layer", "elb"],
+                    help="layer: the MoE layer step (default); elb: the expert lookahead buffer "
+                         "of a speculative draft (--elb-layers layers, --elb-steps draft steps, "
+                         "--T tokens per step, --elb-m experts per layer in the plan)")
+    ap.add_argument("--elb-layers", type=int, default=24)
+    ap.add_argument("--elb-steps", type=int, default=16)
+    ap.add_argument("--elb-m", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-graph", action="store_true",
@@ -136,6 +143,61 @@ def cpu_baseline(inp, budget_s):
                       f"(dequantization of the experts those tokens use included), {dt:.2f} s"}
 
 
+def bench_elb(args, q, torch, np, synth):
+    """Expert lookahead buffer ("Specter" summary, Method steps, steps 2 and 3): device time of
+    one draft step's count update over all layers, and of the planner's top-M snapshot."""
+    import oracle
+    cfg = synth.get_config(args.config)
+    T = args.T or 1
+    L, K, M = args.elb_layers, args.elb_steps, min(args.elb_m, cfg.E)
+    dev = torch.device("cuda:0")
+    inp = synth.make_inputs(cfg, K * L * T, with_weights=False)
+    ids, _ = q.moe_route_topk(torch.from_numpy(inp.logits).to(dev), cfg.k, cfg.gate_mode)
+    ids = ids.reshape(K, L, T, cfg.k).contiguous()
+    steps = [ids[i].contiguous() for i in range(K)]
+    counts = torch.zeros((L, cfg.E), dtype=torch.int32, device=dev)
+    ex = torch.empty((L, M), dtype=torch.int32, device=dev)
+    cn = torch.empty((L, M), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for r in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    acc_us = timed(lambda: q.moe_elb_accumulate(steps[0], cfg.E, counts), args.steps)
+    top_us = timed(lambda: q.moe_elb_top_m(counts, M, experts=ex, top_counts=cn), args.steps)
+    # working set per layer after k draft steps (experts with a nonzero count), checked
+    # against the oracle's counts
+    counts.zero_()
+    want = np.zeros((L, cfg.E), dtype=np.int64)
+    ids_h = ids.cpu().numpy()
+    work = {}
+    for i in range(K):
+        q.moe_elb_accumulate(steps[i], cfg.E, counts)
+        want = oracle.elb_accumulate(want, ids_h[i], cfg.E)
+        if (i + 1) & i == 0 or i + 1 == K:
+            work[i + 1] = float((want > 0).sum(axis=1).mean())
+    if not np.array_equal(counts.cpu().numpy(), want):
+        raise RuntimeError("ELB counts differ from the oracle")
+    print(json.dumps({
+        "metric": "expert lookahead buffer: device us per draft step (count update, all layers)",
+        "value": acc_us, "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "top_m_us": top_us,
+        "working_set_per_layer": work,
+        "config": {"workload": f"elb_{cfg.name}_L{L}_K{K}_T{T}_M{M}", "layers": L,
+                   "draft_steps": K, "tokens_per_step": T, "experts": cfg.E, "top_k": cfg.k,
+                   "plan_m": M}}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -150,6 +212,10 @@ def main():
     import quantized_expert_layer_amd as q
     import synth
 
+    if args.workload == "elb":
+        torch.cuda.set_device(torch.device("cuda:0"))
+        bench_elb(args, q, torch, np, synth)
+        return
     cfg = synth.get_config(args.config)
     T = args.T or cfg.T_list[0]
     inp = synth.make_inputs(cfg, T, wtype=args.wtype, active=args.active)

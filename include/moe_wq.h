@@ -10,6 +10,7 @@
  *   and moe_dequant          the standalone per-expert dequantization (Algorithm 1);
  *   moe_decode_layer         steps 1-4 for the few tokens of a decode / verify step, in three
  *                            launches
+ *   moe_elb_accumulate / moe_elb_top_m   the expert lookahead buffer of a speculative draft
  *
  * Sources (page, section):
  *   [W] "Who Says Elephants Can't Run: Bringing Large Scale MoE Models into Cloud Scale
@@ -282,6 +283,33 @@ int32_t moe_probe_mfma(int32_t iters, float* out, int32_t blocks, void* stream);
 int32_t moe_unpermute_combine(const uint16_t* y_perm, const int32_t* inv_perm,
                               const float* topk_w, const uint16_t* addend,
                               int32_t T, int32_t k, int32_t d, uint16_t* out, void* stream);
+
+/*
+ * Expert lookahead buffer.  [S] Method steps, step 2: while the draft advances, the analyzer
+ * counts per MoE layer j and expert e the draft steps whose routing used e in layer j,
+ * ELB_cnt[j, e] = sum over steps i of [e in ELB_route[i, j]]; step 3: at a chunk boundary the
+ * planner takes each layer's top-M experts as the prefetch plan.
+ *
+ * moe_elb_accumulate -- one draft step.
+ *   ids     int32 [L, T, k]  the step's routing in each of L layers (T draft tokens, k experts
+ *                            each, e.g. moe_route_topk's output per layer); ids outside [0, E)
+ *                            route nowhere and are ignored
+ *   counts  int32 [L, E]     in/out: counts[j][e] += 1 if e appears among layer j's ids
+ *                            (once per step, however many tokens chose it)
+ *   Requires 1 <= E <= 256, k >= 1.  L == 0 enqueues nothing; T == 0 adds nothing.
+ *
+ * moe_elb_top_m -- the planner's snapshot.
+ *   counts      int32 [L, E]
+ *   experts     int32 [L, M] out: per layer the M experts with the largest counts, in that
+ *                            order, ties to the smaller expert index (experts with count 0
+ *                            fill the tail when fewer than M were used)
+ *   top_counts  int32 [L, M] out (nullable): their counts
+ *   Requires 1 <= M <= E <= 256.
+ */
+int32_t moe_elb_accumulate(const int32_t* ids, int32_t L, int32_t T, int32_t k, int32_t E,
+                           int32_t* counts, void* stream);
+int32_t moe_elb_top_m(const int32_t* counts, int32_t L, int32_t E, int32_t M, int32_t* experts,
+                      int32_t* top_counts, void* stream);
 
 /*
  * moe_dequant -- Algorithm 1 of [W] section 3:

@@ -27,7 +27,7 @@ __all__ = [
     "moe_dequant", "moe_pack_wq", "moe_packed_bytes", "moe_gemm_workspace_size",
     "moe_permute_workspace_size", "GemmOpts", "EXPORTED_SYMBOLS", "new_output",
     "moe_probe_read", "moe_probe_mfma", "moe_decode_layer", "moe_decode_workspace_size",
-    "MOE_DECODE_MAX_TOKENS", "MOE_DECODE_MAX_ROWS",
+    "MOE_DECODE_MAX_TOKENS", "MOE_DECODE_MAX_ROWS", "moe_elb_accumulate", "moe_elb_top_m",
 ]
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE = 0, -1, -2, -3
@@ -52,6 +52,7 @@ EXPORTED_SYMBOLS = (
     "moe_grouped_gemm_wq_rows", "moe_gemm_workspace_size", "moe_unpermute_combine", "moe_dequant", "moe_packed_bytes",
     "moe_pack_wq", "moe_status_str", "moe_version", "moe_probe_read", "moe_probe_mfma",
     "moe_decode_layer", "moe_decode_workspace_size", "moe_route_topk_active",
+    "moe_elb_accumulate", "moe_elb_top_m",
 )
 
 
@@ -115,6 +116,8 @@ def lib():
         "moe_decode_layer": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I,
                                   _I, _P, _P, _P, _P, _P, _SZ, _P]),
         "moe_route_topk_active": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
+        "moe_elb_accumulate": (_I, [_P, _I, _I, _I, _I, _P, _P]),
+        "moe_elb_top_m": (_I, [_P, _I, _I, _I, _P, _P, _P]),
         "moe_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     }
     for name, (res, args) in sig.items():
@@ -383,6 +386,33 @@ def moe_decode_layer(logits, x, k, gate_mode, inter, act, w1, s1, w2, s2, wtype,
         _ptr(addend), _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
     return out, topk_ids, topk_w
+
+
+def moe_elb_accumulate(ids, E, counts, stream=None):
+    """One draft step: ids int32 [L, T, k] (device), counts int32 [L, E] updated in place."""
+    torch = _torch()
+    L, T, k = ids.shape
+    _need(ids, torch.int32, "ids")
+    _need(counts, torch.int32, "counts", L * E)
+    _check("moe_elb_accumulate", lib().moe_elb_accumulate(_ptr(ids), L, T, k, E, _ptr(counts),
+                                                          _stream(stream)))
+    return counts
+
+
+def moe_elb_top_m(counts, M, experts=None, top_counts=None, stream=None):
+    """Per layer the M most-counted experts: returns (experts int32 [L, M], counts [L, M])."""
+    torch = _torch()
+    L, E = counts.shape
+    if experts is None:
+        experts = new_output((L, M), torch.int32, counts.device)
+    if top_counts is None:
+        top_counts = new_output((L, M), torch.int32, counts.device)
+    _need(counts, torch.int32, "counts", L * E)
+    _need(experts, torch.int32, "experts", L * M)
+    _need(top_counts, torch.int32, "top_counts", L * M)
+    _check("moe_elb_top_m", lib().moe_elb_top_m(_ptr(counts), L, E, int(M), _ptr(experts),
+                                                _ptr(top_counts), _stream(stream)))
+    return experts, top_counts
 
 
 def moe_unpermute_combine(y_perm, inv_perm, topk_w, addend, T, k, out=None, stream=None):

@@ -321,6 +321,31 @@ int32_t moe_unpermute_combine(const uint16_t* y_perm, const int32_t* inv_perm, c
                                           (hipStream_t)stream));
 }
 
+int32_t moe_elb_accumulate(const int32_t* ids, int32_t L, int32_t T, int32_t k, int32_t E,
+                           int32_t* counts, void* stream) {
+    if (L < 0 || T < 0 || k < 1 || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_INVALID;
+    if ((int64_t)L * T * k >= (int64_t)1 << 31 || (int64_t)L * E >= (int64_t)1 << 31)
+        return MOE_ERR_UNSUPPORTED;
+    if (L == 0) return MOE_OK;
+    if (!counts || (T > 0 && !ids)) return MOE_ERR_INVALID;
+    if (!aligned(counts, 4) || (ids && !aligned(ids, 4))) return MOE_ERR_INVALID;
+    if (int32_t st = check_device()) return st;
+    return hip_status(moe::launch_elb_accumulate(ids, L, T * k, E, counts, (hipStream_t)stream));
+}
+
+int32_t moe_elb_top_m(const int32_t* counts, int32_t L, int32_t E, int32_t M, int32_t* experts,
+                      int32_t* top_counts, void* stream) {
+    if (L < 0 || E < 1 || E > MOE_MAX_EXPERTS || M < 1 || M > E) return MOE_ERR_INVALID;
+    if ((int64_t)L * E >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+    if (L == 0) return MOE_OK;
+    if (!counts || !experts) return MOE_ERR_INVALID;
+    if (!aligned(counts, 4) || !aligned(experts, 4) || (top_counts && !aligned(top_counts, 4)))
+        return MOE_ERR_INVALID;
+    if (int32_t st = check_device()) return st;
+    return hip_status(moe::launch_elb_top_m(counts, L, E, M, experts, top_counts,
+                                            (hipStream_t)stream));
+}
+
 int32_t moe_dequant(const void* w_packed, const uint16_t* scales, int32_t wtype, int32_t group_size,
                     int32_t E, int32_t K, int32_t N, uint16_t* w_out, void* stream) {
     if (E < 1 || E > MOE_MAX_EXPERTS || K <= 0 || N <= 0) return MOE_ERR_INVALID;

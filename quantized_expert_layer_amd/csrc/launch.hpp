@@ -23,6 +23,11 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* inv_perm, const floa
                           const uint16_t* addend, int T, int k, int d, uint16_t* out,
                           hipStream_t stream);
 
+hipError_t launch_elb_accumulate(const int32_t* ids, int L, int n, int E, int32_t* counts,
+                                 hipStream_t stream);
+hipError_t launch_elb_top_m(const int32_t* counts, int L, int E, int M, int32_t* experts,
+                            int32_t* top_counts, hipStream_t stream);
+
 hipError_t launch_dequant(const void* w, const uint16_t* scales, int wtype, int group,
                           int E, int K, int N, uint16_t* out, hipStream_t stream);
 

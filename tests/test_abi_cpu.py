@@ -329,3 +329,23 @@ def test_decode_workspace_size():
     assert need >= 4 * (3 * R + E + 1) + 4 * (d // 16) + 2 * R * inter
     # and it grows with the tokens
     assert L.moe_decode_workspace_size(T + 1, k, E, d, inter, 0) > need
+
+
+def test_elb_validation():
+    L = q.lib()
+    acc, top = L.moe_elb_accumulate, L.moe_elb_top_m
+    assert acc(FAKE, 2, 1, 0, 8, FAKE, None) == q.MOE_ERR_INVALID          # k = 0
+    assert acc(FAKE, 2, 1, 2, 257, FAKE, None) == q.MOE_ERR_INVALID        # E > 256
+    assert acc(FAKE, -1, 1, 2, 8, FAKE, None) == q.MOE_ERR_INVALID
+    assert acc(FAKE, 2, 1, 2, 8, None, None) == q.MOE_ERR_INVALID          # no counts
+    assert acc(MIS, 2, 1, 2, 8, FAKE, None) == q.MOE_ERR_INVALID
+    assert acc(None, 0, 1, 2, 8, None, None) == q.MOE_OK                   # L = 0
+    assert top(FAKE, 2, 8, 0, FAKE, None, None) == q.MOE_ERR_INVALID       # M = 0
+    assert top(FAKE, 2, 8, 9, FAKE, None, None) == q.MOE_ERR_INVALID       # M > E
+    assert top(FAKE, 2, 8, 3, None, None, None) == q.MOE_ERR_INVALID
+    assert top(FAKE, 2, 8, 3, FAKE, MIS, None) == q.MOE_ERR_INVALID
+    assert top(None, 0, 8, 3, None, None, None) == q.MOE_OK
+    if not gpu_available():
+        assert acc(FAKE, 2, 1, 2, 8, FAKE, None) == q.MOE_ERR_NO_DEVICE
+        assert acc(None, 2, 0, 2, 8, FAKE, None) == q.MOE_ERR_NO_DEVICE    # T = 0: no ids needed
+        assert top(FAKE, 2, 8, 3, FAKE, None, None) == q.MOE_ERR_NO_DEVICE
