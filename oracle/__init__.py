@@ -12,5 +12,5 @@ from .oracle import (  # noqa: F401
     GATE_ALL, GATE_TOPK,
     topk_route, stable_expert_sort, permute_rows, dequant_algorithm1, dense_weights,
     expert_ffn, grouped_gemm, unpermute_combine, shared_ffn, moe_layer, moe_layer_tokens,
-    elb_accumulate, elb_top_m,
+    elb_accumulate, elb_top_m, bf16_decompose, bf16_recombine,
 )

@@ -258,3 +258,25 @@ def elb_top_m(counts: np.ndarray, M: int):
     for j in range(L):
         experts[j] = np.lexsort((np.arange(E), -counts[j]))[:M]
     return experts, np.take_along_axis(counts, experts, axis=1)
+
+
+# ---------------------------------------------------------------- BF16 bit-field recombination
+# "ZipMoE" note, key design "BF16 bit-field lossless compression": a BF16 value is split into
+# its exponent bits (which are compressed) and its sign and mantissa bits (packed byte-aligned);
+# recovery merges the decompressed exponents with the sign-mantissa bytes.  Reading of the
+# byte layout: one exponent byte per value (the 8 exponent bits), and one sign-mantissa byte
+# per value holding the sign in bit 7 and the 7 mantissa bits in bits 6..0 (the BF16 bit order
+# with the exponent field taken out).
+def bf16_decompose(bits: np.ndarray):
+    """BF16 bit patterns (uint16) -> (exponent bytes, sign-mantissa bytes), both uint8."""
+    v = np.asarray(bits, dtype=np.uint16).astype(np.uint32)
+    exponent = (v >> 7) & 0xFF
+    sign_mantissa = ((v >> 8) & 0x80) | (v & 0x7F)
+    return exponent.astype(np.uint8), sign_mantissa.astype(np.uint8)
+
+
+def bf16_recombine(exponent: np.ndarray, sign_mantissa: np.ndarray) -> np.ndarray:
+    """(exponent bytes, sign-mantissa bytes) -> BF16 bit patterns (uint16)."""
+    e = np.asarray(exponent, dtype=np.uint8).astype(np.uint32)
+    sm = np.asarray(sign_mantissa, dtype=np.uint8).astype(np.uint32)
+    return (((sm & 0x80) << 8) | (e << 7) | (sm & 0x7F)).astype(np.uint16)

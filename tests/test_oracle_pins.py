@@ -469,3 +469,29 @@ def test_elb_matches_the_counting_rule_brute_force():
         for j in range(L):
             ranked = sorted(range(E), key=lambda e: (-counts[j, e], e))[:M]
             assert list(ex[j]) == ranked and list(cn[j]) == [counts[j, e] for e in ranked]
+
+
+# ---------------------------------------------------------------- BF16 bit-field pins
+def test_bf16_fields_hand_worked(golden_dir):
+    import torch
+    for line in open(os.path.join(golden_dir, "bf16_fields.txt")):
+        line = line.split("#")[0].split()
+        if not line:
+            continue
+        name, bits, e, sm = line[0], int(line[1], 16), int(line[2], 16), int(line[3], 16)
+        ge, gsm = oracle.bf16_decompose(np.array([bits], np.uint16))
+        assert (int(ge[0]), int(gsm[0])) == (e, sm), name
+        assert int(oracle.bf16_recombine(ge, gsm)[0]) == bits, name
+        # the bit pattern is the value the row names (torch's own bf16 encoding)
+        if name not in ("nan", "2^-133"):
+            want = torch.tensor([float(name)], dtype=torch.bfloat16).view(torch.int16).item() & 0xFFFF
+            assert want == bits, name
+    assert torch.tensor([2.0 ** -133], dtype=torch.bfloat16).view(torch.int16).item() == 1
+
+
+def test_bf16_round_trip_is_lossless_for_every_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    e, sm = oracle.bf16_decompose(bits)
+    assert np.array_equal(oracle.bf16_recombine(e, sm), bits)
+    # each field takes every value: 256 exponents, 256 sign-mantissa bytes
+    assert np.unique(e).size == 256 and np.unique(sm).size == 256
