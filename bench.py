@@ -70,10 +70,12 @@ def parse():
                          "take no expert); seeded, whole sentences of --sentence-len tokens")
     ap.add_argument("--sentence-len", type=int, default=40,
                     help="tokens per sentence for --finished (40: the MT workload's sentences)")
-    ap.add_argument("--workload", default="layer", choices=["layer", "elb"],
+    ap.add_argument("--workload", default="layer", choices=["layer", "elb", "bf16"],
                     help="layer: the MoE layer step (default); elb: the expert lookahead buffer "
                          "of a speculative draft (--elb-layers layers, --elb-steps draft steps, "
-                         "--T tokens per step, --elb-m experts per layer in the plan)")
+                         "--T tokens per step, --elb-m experts per layer in the plan); bf16: "
+                         "BF16 recovery from exponent / sign-mantissa bytes of one expert's "
+                         "three matrices (--config's shape)")
     ap.add_argument("--elb-layers", type=int, default=24)
     ap.add_argument("--elb-steps", type=int, default=16)
     ap.add_argument("--elb-m", type=int, default=16)
@@ -198,6 +200,53 @@ def bench_elb(args, q, torch, np, synth):
                    "plan_m": M}}), flush=True)
 
 
+def bench_bf16(args, q, torch, np, synth):
+    """BF16 bit-field recombination ("ZipMoE" note): one expert's gate, up and down matrices
+    (3 * d * I values) recovered from exponent and sign-mantissa bytes; HBM-bound."""
+    import oracle
+    cfg = synth.get_config(args.config)
+    n = 3 * cfg.d * cfg.inter
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(20261202)
+    # expert-like values, bf16: N(0, 0.02^2)
+    w = torch.from_numpy(rng.standard_normal(n, dtype=np.float32) * np.float32(0.02))
+    bits = w.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    e_h, sm_h = oracle.bf16_decompose(bits)
+    # enough copies to read past the 256 MB cache on every call
+    n_copies = max(1, int(np.ceil(1e9 / (4.0 * n))))
+    bufs = [(torch.from_numpy(e_h).to(dev), torch.from_numpy(sm_h).to(dev),
+             torch.empty(n, dtype=torch.bfloat16, device=dev)) for _ in range(n_copies)]
+    for b in bufs:
+        q.moe_bf16_recombine(b[0], b[1], out=b[2])
+    torch.cuda.synchronize()
+    if not np.array_equal(bufs[0][2].view(torch.int16).cpu().numpy().view(np.uint16), bits):
+        raise RuntimeError("BF16 recovery differs from the original bits")
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        b = bufs[i % n_copies]
+        q.moe_bf16_recombine(b[0], b[1], out=b[2])
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        b = bufs[i % n_copies]
+        evs[i][0].record(stream)
+        q.moe_bf16_recombine(b[0], b[1], out=b[2])
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(z) for a, z in evs]) * 1e3)
+    gbs = 4.0 * n / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "BF16 recovery from bit fields: HBM GB/s (2 bytes read + 2 written per value)",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "vs_baseline": None, "dtype": "u8->bf16", "data": "synthetic",
+        "us_per_call": us,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "config": {"workload": f"bf16_recombine_{cfg.name}_expert", "values": n,
+                   "copies_rotated": n_copies}}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -212,9 +261,9 @@ def main():
     import quantized_expert_layer_amd as q
     import synth
 
-    if args.workload == "elb":
+    if args.workload in ("elb", "bf16"):
         torch.cuda.set_device(torch.device("cuda:0"))
-        bench_elb(args, q, torch, np, synth)
+        (bench_elb if args.workload == "elb" else bench_bf16)(args, q, torch, np, synth)
         return
     cfg = synth.get_config(args.config)
     T = args.T or cfg.T_list[0]

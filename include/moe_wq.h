@@ -11,6 +11,7 @@
  *   moe_decode_layer         steps 1-4 for the few tokens of a decode / verify step, in three
  *                            launches
  *   moe_elb_accumulate / moe_elb_top_m   the expert lookahead buffer of a speculative draft
+ *   moe_bf16_recombine       BF16 values from separately stored exponent / sign-mantissa bytes
  *
  * Sources (page, section):
  *   [W] "Who Says Elephants Can't Run: Bringing Large Scale MoE Models into Cloud Scale
@@ -22,6 +23,7 @@
  *   [S] "Specter" summary: Background / MoE (top-k routing), Background / GPTQ INT4
  *       (symmetric, group size 128), Method steps, step 5 (tokens grouped by expert into
  *       one GEMM per expert, then scattered back).
+ *   [Z] "ZipMoE" note: key design, BF16 bit-field lossless compression.
  *
  * Conventions for every call:
  *   - Pointers are device pointers owned by the caller unless marked [host].  fp16 values
@@ -310,6 +312,19 @@ int32_t moe_elb_accumulate(const int32_t* ids, int32_t L, int32_t T, int32_t k, 
                            int32_t* counts, void* stream);
 int32_t moe_elb_top_m(const int32_t* counts, int32_t L, int32_t E, int32_t M, int32_t* experts,
                       int32_t* top_counts, void* stream);
+
+/*
+ * moe_bf16_recombine -- [Z] "ZipMoE" note, key design (BF16 bit-field lossless compression):
+ * an expert tensor is kept as its exponent bits (compressed, then decompressed before use) and
+ * its sign and mantissa bits (byte-aligned); recovery merges them into the original BF16.
+ *   exponents      uint8 [n]   the 8 exponent bits of each value
+ *   sign_mantissa  uint8 [n]   sign in bit 7, the 7 mantissa bits in bits 6..0
+ *   out            uint16 [n]  BF16 bits: (sm & 0x80) << 8 | e << 7 | (sm & 0x7F)
+ *   All three pointers 16-byte aligned; any n (a tail of n % 16 values is handled apart).
+ *   Exact: recombining the fields of any BF16 value gives its bits back.
+ */
+int32_t moe_bf16_recombine(const uint8_t* exponents, const uint8_t* sign_mantissa, size_t n,
+                           uint16_t* out, void* stream);
 
 /*
  * moe_dequant -- Algorithm 1 of [W] section 3:

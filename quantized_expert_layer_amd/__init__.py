@@ -28,6 +28,7 @@ __all__ = [
     "moe_permute_workspace_size", "GemmOpts", "EXPORTED_SYMBOLS", "new_output",
     "moe_probe_read", "moe_probe_mfma", "moe_decode_layer", "moe_decode_workspace_size",
     "MOE_DECODE_MAX_TOKENS", "MOE_DECODE_MAX_ROWS", "moe_elb_accumulate", "moe_elb_top_m",
+    "moe_bf16_recombine",
 ]
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE = 0, -1, -2, -3
@@ -52,7 +53,7 @@ EXPORTED_SYMBOLS = (
     "moe_grouped_gemm_wq_rows", "moe_gemm_workspace_size", "moe_unpermute_combine", "moe_dequant", "moe_packed_bytes",
     "moe_pack_wq", "moe_status_str", "moe_version", "moe_probe_read", "moe_probe_mfma",
     "moe_decode_layer", "moe_decode_workspace_size", "moe_route_topk_active",
-    "moe_elb_accumulate", "moe_elb_top_m",
+    "moe_elb_accumulate", "moe_elb_top_m", "moe_bf16_recombine",
 )
 
 
@@ -118,6 +119,7 @@ def lib():
         "moe_route_topk_active": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
         "moe_elb_accumulate": (_I, [_P, _I, _I, _I, _I, _P, _P]),
         "moe_elb_top_m": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+        "moe_bf16_recombine": (_I, [_P, _P, _SZ, _P, _P]),
         "moe_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     }
     for name, (res, args) in sig.items():
@@ -413,6 +415,20 @@ def moe_elb_top_m(counts, M, experts=None, top_counts=None, stream=None):
     _check("moe_elb_top_m", lib().moe_elb_top_m(_ptr(counts), L, E, int(M), _ptr(experts),
                                                 _ptr(top_counts), _stream(stream)))
     return experts, top_counts
+
+
+def moe_bf16_recombine(exponents, sign_mantissa, out=None, stream=None):
+    """BF16 tensor [n] from uint8 exponent bytes [n] and sign-mantissa bytes [n] (device)."""
+    torch = _torch()
+    n = exponents.numel()
+    if out is None:
+        out = new_output(n, torch.bfloat16, exponents.device)
+    _need(exponents, torch.uint8, "exponents", n)
+    _need(sign_mantissa, torch.uint8, "sign_mantissa", n)
+    _need(out, torch.bfloat16, "out", n)
+    _check("moe_bf16_recombine", lib().moe_bf16_recombine(_ptr(exponents), _ptr(sign_mantissa),
+                                                          n, _ptr(out), _stream(stream)))
+    return out
 
 
 def moe_unpermute_combine(y_perm, inv_perm, topk_w, addend, T, k, out=None, stream=None):

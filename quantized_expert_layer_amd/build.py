@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_wq.so")
 
 HIP_SOURCES = ["api.hip", "route_topk.hip", "permute.hip", "gemm.hip", "combine.hip", "dequant.hip",
-               "probe.hip", "decode.hip", "elb.hip"]
+               "probe.hip", "decode.hip", "elb.hip", "bf16.hip"]
 CXX_SOURCES = ["pack.cpp"]
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -346,6 +346,18 @@ int32_t moe_elb_top_m(const int32_t* counts, int32_t L, int32_t E, int32_t M, in
                                             (hipStream_t)stream));
 }
 
+int32_t moe_bf16_recombine(const uint8_t* exponents, const uint8_t* sign_mantissa, size_t n,
+                           uint16_t* out, void* stream) {
+    if (n == 0) return MOE_OK;
+    if (n >= (size_t)1 << 40) return MOE_ERR_UNSUPPORTED;
+    if (!exponents || !sign_mantissa || !out) return MOE_ERR_INVALID;
+    if (!aligned(exponents, 16) || !aligned(sign_mantissa, 16) || !aligned(out, 16))
+        return MOE_ERR_INVALID;
+    if (int32_t st = check_device()) return st;
+    return hip_status(moe::launch_bf16_recombine(exponents, sign_mantissa, n, out,
+                                                 (hipStream_t)stream));
+}
+
 int32_t moe_dequant(const void* w_packed, const uint16_t* scales, int32_t wtype, int32_t group_size,
                     int32_t E, int32_t K, int32_t N, uint16_t* w_out, void* stream) {
     if (E < 1 || E > MOE_MAX_EXPERTS || K <= 0 || N <= 0) return MOE_ERR_INVALID;

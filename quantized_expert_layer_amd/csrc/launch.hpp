@@ -28,6 +28,9 @@ hipError_t launch_elb_accumulate(const int32_t* ids, int L, int n, int E, int32_
 hipError_t launch_elb_top_m(const int32_t* counts, int L, int E, int M, int32_t* experts,
                             int32_t* top_counts, hipStream_t stream);
 
+hipError_t launch_bf16_recombine(const uint8_t* e, const uint8_t* sm, size_t n, uint16_t* out,
+                                 hipStream_t stream);
+
 hipError_t launch_dequant(const void* w, const uint16_t* scales, int wtype, int group,
                           int E, int K, int N, uint16_t* out, hipStream_t stream);
 

@@ -349,3 +349,15 @@ def test_elb_validation():
         assert acc(FAKE, 2, 1, 2, 8, FAKE, None) == q.MOE_ERR_NO_DEVICE
         assert acc(None, 2, 0, 2, 8, FAKE, None) == q.MOE_ERR_NO_DEVICE    # T = 0: no ids needed
         assert top(FAKE, 2, 8, 3, FAKE, None, None) == q.MOE_ERR_NO_DEVICE
+
+
+def test_bf16_recombine_validation():
+    L = q.lib()
+    f = L.moe_bf16_recombine
+    assert f(None, None, 0, None, None) == q.MOE_OK                        # nothing to do
+    assert f(None, FAKE, 16, FAKE, None) == q.MOE_ERR_INVALID
+    assert f(FAKE, FAKE, 16, None, None) == q.MOE_ERR_INVALID
+    assert f(MIS, FAKE, 16, FAKE, None) == q.MOE_ERR_INVALID               # 16-byte aligned
+    assert f(FAKE, FAKE, 1 << 41, FAKE, None) == q.MOE_ERR_UNSUPPORTED
+    if not gpu_available():
+        assert f(FAKE, FAKE, 17, FAKE, None) == q.MOE_ERR_NO_DEVICE
