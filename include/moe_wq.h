@@ -230,6 +230,9 @@ int32_t moe_grouped_gemm_wq_rows(const uint16_t* a, int32_t a_nrows, const int32
  *             their scales (NULL for MOE_W_FP16), as for moe_grouped_gemm_wq
  *   w2, s2    second-GEMM weights for (wtype, E, inter, d) and scales
  *   addend    fp16 [T, d] or NULL: added with weight 1 (e.g. shared experts)
+ *   addend_ready  hipEvent_t (as void*) or NULL: the call makes `stream` wait for this event
+ *             just before its last launch, the first to read addend, so the caller may compute
+ *             the addend on another stream while the gating, sort and first GEMM run
  *   topk_ids, topk_w  int32 / fp32 [T, k]  out: exactly what moe_route_topk returns
  *   out       fp16 [T, d]  out: out[t] = fp16( sum_j topk_w[t,j] * FFN_{topk_ids[t,j]}(x[t])
  *             + addend[t] ).  The hidden activations are rounded to fp16 as in
@@ -247,8 +250,9 @@ int32_t moe_decode_layer(const float* logits, const uint8_t* active, const uint1
                          int32_t inter, int32_t act,
                          const void* w1, const uint16_t* s1, const void* w2,
                          const uint16_t* s2, int32_t wtype, int32_t group_size,
-                         const uint16_t* addend, int32_t* topk_ids, float* topk_w,
-                         uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+                         const uint16_t* addend, void* addend_ready, int32_t* topk_ids,
+                         float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                         void* stream);
 /* Workspace bytes of moe_decode_layer (0 for arguments it does not accept). */
 size_t moe_decode_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int32_t inter,
                                  int32_t wtype);

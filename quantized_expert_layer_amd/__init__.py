@@ -115,7 +115,7 @@ def lib():
         "moe_probe_read": (_I, [_P, _SZ, _P, _I, _P]),
         "moe_probe_mfma": (_I, [_I, _P, _I, _P]),
         "moe_decode_layer": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I,
-                                  _I, _P, _P, _P, _P, _P, _SZ, _P]),
+                                  _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
         "moe_route_topk_active": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
         "moe_elb_accumulate": (_I, [_P, _I, _I, _I, _I, _P, _P]),
         "moe_elb_top_m": (_I, [_P, _I, _I, _I, _P, _P, _P]),
@@ -353,9 +353,10 @@ def moe_decode_workspace_size(T, k, E, d, inter, wtype):
 
 def moe_decode_layer(logits, x, k, gate_mode, inter, act, w1, s1, w2, s2, wtype, group_size,
                      addend=None, topk_ids=None, topk_w=None, out=None, ws=None, stream=None,
-                     active=None):
+                     active=None, addend_ready=None):
     """The routed layer for a decode / verify step (T <= MOE_DECODE_MAX_TOKENS tokens).
-    Returns (out fp16 [T, d], topk_ids int32 [T, k], topk_w fp32 [T, k])."""
+    Returns (out fp16 [T, d], topk_ids int32 [T, k], topk_w fp32 [T, k]).  addend_ready: a
+    recorded torch.cuda.Event the call waits for before it first reads addend."""
     torch = _torch()
     T, E = logits.shape
     d = x.shape[1]
@@ -385,7 +386,8 @@ def moe_decode_layer(logits, x, k, gate_mode, inter, act, w1, s1, w2, s2, wtype,
     _check("moe_decode_layer", lib().moe_decode_layer(
         _ptr(logits), _ptr(active), _ptr(x), T, E, k, GATES.get(gate_mode, gate_mode), d, int(inter),
         ACTS.get(act, act), _ptr(w1), _ptr(s1), _ptr(w2), _ptr(s2), wt, int(group_size),
-        _ptr(addend), _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(ws),
+        _ptr(addend), None if addend_ready is None else addend_ready.cuda_event,
+        _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
     return out, topk_ids, topk_w
 

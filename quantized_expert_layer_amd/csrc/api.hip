@@ -265,8 +265,9 @@ int32_t moe_decode_layer(const float* logits, const uint8_t* active, const uint1
                          int32_t inter, int32_t act,
                          const void* w1, const uint16_t* s1, const void* w2,
                          const uint16_t* s2, int32_t wtype, int32_t group_size,
-                         const uint16_t* addend, int32_t* topk_ids, float* topk_w,
-                         uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+                         const uint16_t* addend, void* addend_ready, int32_t* topk_ids,
+                         float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                         void* stream) {
     if (int32_t st = validate_decode(T, E, k, gate_mode, d, inter, act, wtype, group_size))
         return st;
     if (T == 0) return MOE_OK;
@@ -298,6 +299,7 @@ int32_t moe_decode_layer(const float* logits, const uint8_t* active, const uint1
     a.wtype = wtype;
     a.group = group_size;
     a.addend = addend;
+    a.addend_ready = addend_ready;
     a.ids = topk_ids;
     a.wts = topk_w;
     a.out = out;

@@ -350,6 +350,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     c.N = a.d;
     c.T = a.T;
     c.k = a.k;
+    // the addend (e.g. shared experts computed on another stream) is first read here
+    if (a.addend_ready) {
+        err = hipStreamWaitEvent(stream, (hipEvent_t)a.addend_ready, 0);
+        if (err != hipSuccess) return err;
+    }
     const bool grouped = a.group != 0;
     switch (a.wtype * 2 + (grouped ? 1 : 0)) {
         case MOE_W_INT4 * 2 + 0: return combine_launch<MOE_W_INT4, false>(c, stream);

@@ -92,6 +92,7 @@ struct DecodeArgs {
     const uint16_t* s2;
     int wtype, group;
     const uint16_t* addend;
+    void* addend_ready;      // hipEvent_t or NULL: waited for before the launch that adds addend
     int32_t* ids;
     float* wts;
     uint16_t* out;

@@ -162,8 +162,7 @@ class DeviceLayer:
             addend = None
             if self.shared is not None:
                 for name, fn, args in self._shared_calls(b, x, T):
-                    args = args[:-1] + (_stream(stream),)
-                    st = fn(*args)
+                    st = fn(*(args[:-1] + (_stream(stream),)))
                     if st != 0:
                         raise MoEError(name, st)
                 addend = b["sh_y"]
@@ -239,13 +238,13 @@ class DeviceLayer:
             calls = []
             addend = None
             if self.shared is not None:
-                calls = [(n, fn, args[:-1] + (st,)) for n, fn, args in self._shared_calls(b, x, T)]
                 addend = b["sh_y"]
+                calls = [(n, fn, args[:-1] + (st,)) for n, fn, args in self._shared_calls(b, x, T)]
             calls.append(("decode", L.moe_decode_layer,
                           (_ptr(logits), _ptr(active), _ptr(x), T, self.E, self.k,
                            GATES[self.gate_mode], self.d, self.inter, ac, _ptr(w1),
                            _ptr(self.s1), _ptr(w2), _ptr(self.s2), wt, self.group, _ptr(addend),
-                           _ptr(b["ids"]), _ptr(b["w"]), _ptr(b["out"]), _ptr(b["dws"]),
+                           None, _ptr(b["ids"]), _ptr(b["w"]), _ptr(b["out"]), _ptr(b["dws"]),
                            b["dws"].numel(), st)))
             return LayerPlan(calls, b["out"], keep=keep)
         calls = [

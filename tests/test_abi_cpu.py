@@ -283,12 +283,12 @@ def test_decode_layer_validation():
 
     def args(**kw):
         d = dict(logits=FAKE, active=None, x=FAKE, T=4, E=8, k=2, gate=0, d=256, inter=512,
-                 act=2, w1=FAKE, s1=FAKE, w2=FAKE, s2=FAKE, wt=0, g=128, add=None, ids=FAKE,
-                 w=FAKE, out=FAKE, ws=FAKE, wsb=ws_need, stream=None)
+                 act=2, w1=FAKE, s1=FAKE, w2=FAKE, s2=FAKE, wt=0, g=128, add=None, ready=None,
+                 ids=FAKE, w=FAKE, out=FAKE, ws=FAKE, wsb=ws_need, stream=None)
         d.update(kw)
         return [d[n] for n in ("logits", "active", "x", "T", "E", "k", "gate", "d", "inter",
-                               "act", "w1", "s1", "w2", "s2", "wt", "g", "add", "ids", "w", "out",
-                               "ws", "wsb", "stream")]
+                               "act", "w1", "s1", "w2", "s2", "wt", "g", "add", "ready", "ids",
+                               "w", "out", "ws", "wsb", "stream")]
 
     assert f(*args(k=9)) == q.MOE_ERR_INVALID
     assert f(*args(k=9, E=8)) == q.MOE_ERR_INVALID

@@ -184,3 +184,35 @@ def test_decode_sort_matches_moe_permute(name, T):
     assert np.array_equal(inv, host(i2))
     assert np.array_equal(off, host(off2))
     assert np.array_equal(wp.view(np.uint32), host(w2).view(np.uint32))
+
+
+def test_decode_waits_for_an_addend_made_on_another_stream():
+    """addend_ready: the addend is produced on a second stream (behind a slow fill, so it is
+    late); the decode call waits for the event before its last launch and adds it exactly as
+    an addend ready beforehand."""
+    import torch
+
+    name, T = "qwen15_moe", 17
+    inp, layer = _layer(name, T)
+    x, L = dev(inp.x), dev(inp.logits)
+    add_h = np.random.default_rng(2).standard_normal((T, inp.cfg.d)).astype(np.float16)
+    want_addend = dev(add_h)
+    kw = dict(k=inp.cfg.k, gate_mode=inp.cfg.gate_mode, inter=inp.cfg.inter, act=inp.cfg.act,
+              w1=layer.w1, s1=layer.s1, w2=layer.w2, s2=layer.s2, wtype=inp.wtype,
+              group_size=inp.cfg.group)
+    case("decode addend_ready")
+    want = host(q.moe_decode_layer(L, x, addend=want_addend, **kw)[0]).copy()
+    side = torch.cuda.Stream()
+    late = torch.zeros_like(want_addend)
+    big = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
+    main = torch.cuda.current_stream()
+    ready = torch.cuda.Event()
+    with torch.cuda.stream(side):
+        side.wait_stream(main)
+        for _ in range(20):
+            big.fill_(1.0)                          # delay the side stream
+        late.copy_(want_addend)
+        ready.record(side)
+    got = host(q.moe_decode_layer(L, x, addend=late, addend_ready=ready, **kw)[0])
+    torch.cuda.synchronize()
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
