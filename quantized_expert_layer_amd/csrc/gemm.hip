@@ -318,7 +318,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
     // larger, keep the register-staged path below, which measured faster for them.
     constexpr bool DMA_A = WT != MOE_W_FP16;
     constexpr int AD = tile_a_stages<WT>();
-    constexpr int NAB = (ATOT > 256 ? ATOT : 256) / kWave;   // wave-wide loads per stage
+    constexpr int NAB = DMA_A ? (ATOT > 256 ? ATOT : 256) / kWave : 4;  // wave-wide loads / stage
     constexpr int NA = NAB / 4;
     static_assert(NAB % 4 == 0 && LDS_BUF * 2 >= NAB * 1024, "DMA stage layout");
     const char* adma[NA];
@@ -588,13 +588,18 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmParams p, int ncb
     int mt, e, row0, rows;
     if (!lookup_m_tile<BM>(p.offsets, p.E, p.R, logical_mt, mt, e, row0, rows)) return;
     const int cbg = a_major ? L % ncbg : L / mtiles;
-    // body specialised for the tile's number of 16-row subtiles (rounded up to 1, 2, 4, 6, 8)
+    // body specialised for the tile's number of 16-row subtiles (1, 2, 3, 4; 5-6 as 6; MS)
+    static_assert(MS >= 3, "the subtile cases below assume tiles of at least 48 rows");
     switch ((rows + 15) / 16) {
         case 1: tile_body<WT, ACT, GROUPED, 1, NS, BM>(p, lds, e, row0, rows, cbg); break;
         case 2: tile_body<WT, ACT, GROUPED, 2, NS, BM>(p, lds, e, row0, rows, cbg); break;
-        case 3: case 4: tile_body<WT, ACT, GROUPED, 4, NS, BM>(p, lds, e, row0, rows, cbg); break;
+        case 3: tile_body<WT, ACT, GROUPED, 3, NS, BM>(p, lds, e, row0, rows, cbg); break;
+        case 4:
+            tile_body<WT, ACT, GROUPED, (MS >= 4 ? 4 : MS), NS, BM>(p, lds, e, row0, rows, cbg);
+            break;
         case 5: case 6:
-            tile_body<WT, ACT, GROUPED, (MS >= 6 ? 6 : 4), NS, BM>(p, lds, e, row0, rows, cbg); break;
+            tile_body<WT, ACT, GROUPED, (MS >= 6 ? 6 : MS), NS, BM>(p, lds, e, row0, rows, cbg);
+            break;
         default: tile_body<WT, ACT, GROUPED, MS, NS, BM>(p, lds, e, row0, rows, cbg); break;
     }
 }
@@ -678,7 +683,7 @@ static hipError_t tile_launch(const GemmParams& p, hipStream_t stream) {
 // holds 64 KB of LDS per block and reads twice the A fragments per MFMA), so it is only
 // used when asked for.
 int gemm_choose_tile(int R, int E, int N, int act, int forced) {
-    if (forced >= MOE_TILE_64x256 && forced <= MOE_TILE_128x128) return forced;
+    if (forced >= MOE_TILE_64x256 && forced <= MOE_TILE_48x256) return forced;
     const int active = R < E ? R : E;
     const int nbo = (act == MOE_ACT_SWIGLU) ? N / 32 : N / 16;
     const int opw = (act == MOE_ACT_SWIGLU) ? 2 : 4;
@@ -691,6 +696,7 @@ static hipError_t tile_dispatch(const GemmParams& p, hipStream_t stream) {
     switch (gemm_choose_tile(p.R, p.E, p.N, ACT, p.tile)) {
         case MOE_TILE_64x256: return tile_launch<WT, ACT, GROUPED, 4, 4>(p, stream);
         case MOE_TILE_128x128: return tile_launch<WT, ACT, GROUPED, 8, 2>(p, stream);
+        case MOE_TILE_48x256: return tile_launch<WT, ACT, GROUPED, 3, 4>(p, stream);
         default: return tile_launch<WT, ACT, GROUPED, 4, 2>(p, stream);
     }
 }

@@ -83,7 +83,37 @@ GEMM_CASES = [
 
 
 PATHS = [(q.PATH_STREAM, q.TILE_AUTO), (q.PATH_TILE, q.TILE_64x256),
-         (q.PATH_TILE, q.TILE_64x128), (q.PATH_TILE, q.TILE_128x128)]
+         (q.PATH_TILE, q.TILE_64x128), (q.PATH_TILE, q.TILE_128x128),
+         (q.PATH_TILE, q.TILE_48x256)]
+
+# expert row counts hitting every specialised body of the tile kernel (1, 2, 3, 4, 6 and all
+# 16-row subtiles, as whole tiles and as the ragged last tile of a larger expert), an empty
+# expert and a full 128-row tile
+SUBTILE_COUNTS = [1, 16, 17, 32, 33, 40, 47, 48, 49, 64, 0, 65, 97, 110, 128, 150, 176, 129]
+
+
+@pytest.mark.parametrize("path,tile", PATHS[1:])
+@pytest.mark.parametrize("wtype,group,act", [("int4", 128, "swiglu"), ("int8", 0, "relu"),
+                                             ("fp16", 0, "none")])
+def test_tile_bodies_for_every_subtile_count(wtype, group, act, path, tile):
+    E, K, N = len(SUBTILE_COUNTS), 256, 128
+    counts = np.array(SUBTILE_COUNTS)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(off[-1])
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal((R, K)).astype(np.float16)
+    if wtype == "fp16":
+        codes = (rng.standard_normal((E, K, N)) * 0.05).astype(np.float16)
+        scales, wdq = None, codes
+    else:
+        codes, scales = synth.gen.make_expert_weights(E, K, N, wtype, group, seed=9)
+        wdq = oracle.dequant_algorithm1(codes, scales, group)
+    case(f"gemm subtile counts {wtype} g={group} {act} tile={tile}")
+    out = q.moe_grouped_gemm_wq(dev(a), dev(off), E, K, N, dev(q.moe_pack_wq(codes, wtype)),
+                                None if scales is None else dev(scales), wtype, group, act,
+                                path=path, tile=tile)
+    ref = oracle.grouped_gemm(a, off, wdq if wtype != "fp16" else wdq.astype(np.float64), act)
+    assert_layer_close(host(out), ref, "subtile counts")
 
 
 @pytest.mark.parametrize("path,tile", PATHS)
