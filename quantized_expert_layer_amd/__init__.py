@@ -224,9 +224,10 @@ def moe_route_topk(logits, k, gate_mode, topk_ids=None, topk_w=None, stream=None
 
 
 def moe_permute(topk_ids, topk_w, x, E, want_w_perm=True, out=None, stream=None,
-                want_x_perm=True):
+                want_x_perm=True, ws=None):
     """Returns (perm, inv_perm, expert_offsets, x_perm or None, w_perm or None).
-    want_x_perm=False skips the row copy (the first GEMM then reads x through perm)."""
+    want_x_perm=False skips the row copy (the first GEMM then reads x through perm).
+    ws: uint8 device workspace of moe_permute_workspace_size bytes (allocated if None)."""
     torch = _torch()
     T, k = topk_ids.shape
     d = x.shape[1]
@@ -248,9 +249,14 @@ def moe_permute(topk_ids, topk_w, x, E, want_w_perm=True, out=None, stream=None,
     _need(offsets, torch.int32, "expert_offsets", E + 1)
     _need(x_perm, torch.float16, "x_perm", R * d)
     _need(w_perm, torch.float32, "w_perm", R)
+    need = lib().moe_permute_workspace_size(T, k, E)
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(ws, torch.uint8, "ws")
     _check("moe_permute", lib().moe_permute(
         _ptr(topk_ids), _ptr(topk_w), _ptr(x), T, k, E, d, _ptr(perm), _ptr(inv_perm),
-        _ptr(offsets), _ptr(x_perm), _ptr(w_perm), None, 0, _stream(stream)))
+        _ptr(offsets), _ptr(x_perm), _ptr(w_perm), _ptr(ws), 0 if ws is None else ws.numel(),
+        _stream(stream)))
     return perm, inv_perm, offsets, x_perm, w_perm
 
 

@@ -126,15 +126,15 @@ int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int
 }
 
 size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E) {
-    (void)T; (void)k; (void)E;
-    return 0;
+    if (T <= 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS) return 0;
+    if ((int64_t)T * k >= (int64_t)1 << 31) return 0;
+    return moe::sort_workspace_bytes(T * k, E);
 }
 
 int32_t moe_permute(const int32_t* topk_ids, const float* topk_w, const uint16_t* x, int32_t T,
                     int32_t k, int32_t E, int32_t d, int32_t* perm, int32_t* inv_perm,
                     int32_t* expert_offsets, uint16_t* x_perm, float* w_perm, void* ws,
                     size_t ws_bytes, void* stream) {
-    (void)ws; (void)ws_bytes;
     if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS || d <= 0)
         return MOE_ERR_INVALID;
     if (d % 8 != 0) return MOE_ERR_UNSUPPORTED;
@@ -148,10 +148,12 @@ int32_t moe_permute(const int32_t* topk_ids, const float* topk_w, const uint16_t
         !aligned(perm, 4) || !aligned(inv_perm, 4) || !aligned(expert_offsets, 4))
         return MOE_ERR_INVALID;
     if ((topk_w && !aligned(topk_w, 4)) || (w_perm && !aligned(w_perm, 4))) return MOE_ERR_INVALID;
+    const size_t need = moe::sort_workspace_bytes((int)R, E);
+    if (need && (!ws || ws_bytes < need || !aligned(ws, 4))) return MOE_ERR_WORKSPACE;
     if (int32_t st = check_device()) return st;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = moe::launch_sort(topk_ids, topk_w, (int)R, E, perm, inv_perm, expert_offsets,
-                                    w_perm, s);
+                                    w_perm, ws, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (!x_perm) return MOE_OK;               // the caller gathers inside the first GEMM
     return hip_status(moe::launch_gather(x, perm, (int)R, k, d, x_perm, s));

@@ -12,9 +12,11 @@ int32_t device_status();
 hipError_t launch_route_topk(const float* logits, const uint8_t* active, int T, int E, int k,
                              int gate_all, int32_t* ids, float* wts, hipStream_t stream);
 
+// ws: sort_workspace_bytes(R, E) bytes (none up to 1024 slots)
+size_t sort_workspace_bytes(int R, int E);
 hipError_t launch_sort(const int32_t* ids, const float* wts, int R, int E,
                        int32_t* perm, int32_t* inv_perm, int32_t* offsets, float* w_perm,
-                       hipStream_t stream);
+                       void* ws, hipStream_t stream);
 
 hipError_t launch_gather(const uint16_t* x, const int32_t* perm, int R, int k, int d,
                          uint16_t* x_perm, hipStream_t stream);

@@ -2,7 +2,11 @@
 // ("Who Says Elephants Can't Run", section 3 workflow: the row index is attached to the
 // gating output, the tuples are sorted by expert_idx, the activations are permuted).
 //
-// The sort itself is sort_block (one workgroup of 16 waves, ballot-matched counting sort).
+// Up to 1024 slots the sort is sort_block (one workgroup of 16 waves, ballot-matched counting
+// sort).  Beyond that one workgroup is bound by its CU's VALU (the per-bit ballot matching of
+// every 64-slot chunk), so the slots are split into 1024-slot blocks over two launches: the
+// first counts each block's keys per expert into a small workspace; the second has each block
+// turn all the counts into its own per-expert bases and place its slots.  Same result, stable.
 #include "common.hpp"
 #include "launch.hpp"
 #include "sort.hpp"
@@ -10,6 +14,7 @@
 namespace moe {
 
 constexpr int kSortLdsKeys = 16384;     // keys staged in LDS when R fits (64 KB)
+constexpr int kSortBlockSlots = kSortWaves * kWave;   // slots per block of the multi-block sort
 
 // KEYS_IN_LDS: all R keys are first copied to LDS with one coalesced pass, so the two walks
 // of the sort read LDS instead of issuing one dependent global load per 64-key chunk.
@@ -48,8 +53,130 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x
     }
 }
 
+// Multi-block sort, launch 1: block b counts the keys of slots [1024 b, 1024 (b + 1)) per
+// expert (one 64-slot chunk per wave; one LDS add per distinct key per wave).
+__global__ __launch_bounds__(1024) void sort_hist_kernel(const int32_t* __restrict__ ids, int R,
+                                                         int E, int32_t* __restrict__ hist) {
+    __shared__ int cnt[MOE_MAX_EXPERTS];
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    const int nbits = (E <= 1) ? 0 : 32 - __clz(E - 1);
+    const int f = blockIdx.x * kSortBlockSlots + threadIdx.x;
+    const int kf = f < R ? ids[f] : -1;
+    const bool valid = (unsigned)kf < (unsigned)E;
+    const Match m = wave_match(kf, valid, nbits, lane);
+    if (valid && m.rank == m.total - 1) atomicAdd(&cnt[kf], m.total);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Multi-block sort, launch 2: block b reads every block's counts, takes the global offsets of
+// the experts (exclusive scan of the totals) plus the counts of blocks before it as its bases,
+// ranks its own slots as sort_block does (wave order, then rank among equal keys of a chunk)
+// and writes perm / inv_perm / w_perm.  Block 0 also writes offsets and fills the positions
+// left empty by slots routed nowhere.
+__global__ __launch_bounds__(1024) void sort_scatter_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ wts, int R, int E,
+    const int32_t* __restrict__ hist, int nblk, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv_perm, int32_t* __restrict__ offsets, float* __restrict__ w_perm) {
+    __shared__ int cnt[kSortWaves][MOE_MAX_EXPERTS];
+    __shared__ int base[MOE_MAX_EXPERTS];
+    __shared__ int wave_sum[4];
+    __shared__ int n_valid;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int f = blockIdx.x * kSortBlockSlots + threadIdx.x;
+    const int kf = f < R ? ids[f] : -1;
+    const float wf = (w_perm && f < R) ? wts[f] : 0.0f;
+    for (int i = threadIdx.x; i < kSortWaves * MOE_MAX_EXPERTS; i += blockDim.x)
+        (&cnt[0][0])[i] = 0;
+
+    int tot = 0, pre = 0, incl = 0;
+    if (threadIdx.x < 256) {                   // waves 0..3, one expert per thread
+        const int e = threadIdx.x;
+        if (e < E) {
+            for (int b = 0; b < nblk; ++b) {
+                const int h = hist[(size_t)b * E + e];
+                tot += h;
+                if (b < (int)blockIdx.x) pre += h;
+            }
+        }
+        incl = tot;
+        for (int s = 1; s < kWave; s <<= 1) {
+            const int v = __shfl_up(incl, s, kWave);
+            if (lane >= s) incl += v;
+        }
+        if (lane == kWave - 1) wave_sum[wave] = incl;
+    }
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        const int e = threadIdx.x;
+        int before = 0;
+        for (int w = 0; w < wave; ++w) before += wave_sum[w];
+        const int start = before + incl - tot;
+        if (e < E) {
+            base[e] = start + pre;
+            if (blockIdx.x == 0) offsets[e] = start;
+            if (e == E - 1) {
+                if (blockIdx.x == 0) offsets[E] = start + tot;
+                n_valid = start + tot;
+            }
+        }
+    }
+    // pass 1: per-wave counts of this block's slots (one chunk per wave)
+    const int nbits = (E <= 1) ? 0 : 32 - __clz(E - 1);
+    const bool valid = (unsigned)kf < (unsigned)E;
+    const Match m = wave_match(kf, valid, nbits, lane);
+    if (valid && m.rank == m.total - 1) cnt[wave][kf] = m.total;
+    __syncthreads();
+    // per-(wave, expert) bases in wave order
+    if (threadIdx.x < E) {
+        const int e = threadIdx.x;
+        int run = base[e];
+        for (int w = 0; w < kSortWaves; ++w) {
+            const int c = cnt[w][e];
+            cnt[w][e] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    // pass 2: scatter
+    if (valid) {
+        const int pos = cnt[wave][kf] + m.rank;
+        perm[pos] = f;
+        inv_perm[f] = pos;
+        if (w_perm) w_perm[pos] = wf;
+    } else if (f < R) {
+        inv_perm[f] = -1;
+    }
+    if (blockIdx.x == 0) {
+        for (int p = n_valid + threadIdx.x; p < R; p += blockDim.x) {
+            perm[p] = -1;
+            if (w_perm) w_perm[p] = 0.0f;
+        }
+    }
+}
+
+size_t sort_workspace_bytes(int R, int E) {
+    if (R <= kSortBlockSlots) return 0;
+    const size_t nblk = ((size_t)R + kSortBlockSlots - 1) / kSortBlockSlots;
+    return nblk * (size_t)E * sizeof(int32_t);
+}
+
 hipError_t launch_sort(const int32_t* ids, const float* wts, int R, int E, int32_t* perm,
-                       int32_t* inv_perm, int32_t* offsets, float* w_perm, hipStream_t stream) {
+                       int32_t* inv_perm, int32_t* offsets, float* w_perm, void* ws,
+                       hipStream_t stream) {
+    if (R > kSortBlockSlots) {
+        const int nblk = (R + kSortBlockSlots - 1) / kSortBlockSlots;
+        int32_t* hist = (int32_t*)ws;
+        sort_hist_kernel<<<nblk, kSortBlockSlots, 0, stream>>>(ids, R, E, hist);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        sort_scatter_kernel<<<nblk, kSortBlockSlots, 0, stream>>>(ids, wts, R, E, hist, nblk, perm,
+                                                                  inv_perm, offsets, w_perm);
+        return hipGetLastError();
+    }
     if (R <= kSortLdsKeys)
         sort_kernel<true><<<1, kSortWaves * kWave, 0, stream>>>(ids, wts, R, E, perm, inv_perm,
                                                                 offsets, w_perm);

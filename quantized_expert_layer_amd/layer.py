@@ -19,7 +19,8 @@ import ctypes
 from . import (ACTS, GATES, MOE_DECODE_MAX_ROWS, MOE_DECODE_MAX_TOKENS, WTYPES, MoEError, _ptr,
                _stream, lib, moe_decode_layer, moe_decode_workspace_size,
                moe_gemm_workspace_size, moe_grouped_gemm_wq, moe_grouped_gemm_wq_rows,
-               moe_pack_wq, moe_permute, moe_route_topk, moe_unpermute_combine, new_output)
+               moe_pack_wq, moe_permute, moe_permute_workspace_size, moe_route_topk,
+               moe_unpermute_combine, new_output)
 
 
 def _dev(a, device):
@@ -128,6 +129,8 @@ class DeviceLayer:
                       moe_gemm_workspace_size(T, 1, self.shared_inter, d, "fp16", "none",
                                               self.gemm_path))
         b["ws"] = new_output(max(wsz, 16), torch.uint8, dev)
+        b["pws"] = new_output(max(moe_permute_workspace_size(T, self.k, self.E), 16),
+                              torch.uint8, dev)
         dws = moe_decode_workspace_size(T, self.k, self.E, d, self.inter, self.wtype)
         if dws:
             b["dws"] = new_output(dws, torch.uint8, dev)
@@ -178,7 +181,7 @@ class DeviceLayer:
         R = T * self.k
         moe_permute(b["ids"], b["w"], x, self.E,
                     out=(b["perm"], b["inv"], b["off"], None if fused else b["xp"], b["wp"]),
-                    stream=stream)
+                    stream=stream, ws=b["pws"])
         if fused:
             moe_grouped_gemm_wq_rows(x, b["perm"], self.k, b["off"], R, self.E, self.d, self.n1,
                                      self.w1, self.s1, self.wtype, self.group, self.act,
@@ -253,8 +256,8 @@ class DeviceLayer:
                                                 _ptr(b["w"]), st)),
             ("permute", L.moe_permute, (_ptr(b["ids"]), _ptr(b["w"]), _ptr(x), T, self.k, self.E,
                                         self.d, _ptr(b["perm"]), _ptr(b["inv"]), _ptr(b["off"]),
-                                        None if fused else _ptr(b["xp"]), _ptr(b["wp"]), None, 0,
-                                        st)),
+                                        None if fused else _ptr(b["xp"]), _ptr(b["wp"]),
+                                        _ptr(b["pws"]), b["pws"].numel(), st)),
         ]
         if fused:
             calls.append(("gemm1", L.moe_grouped_gemm_wq_rows,

@@ -67,6 +67,36 @@ def test_permute_matches_oracle(T, k, E, d, skew):
     assert np.array_equal(host(wp), w.ravel()[r_perm])
 
 
+@pytest.mark.parametrize("T,k,E", [(600, 2, 8), (3000, 2, 40), (9000, 2, 256)])
+def test_permute_multi_block_with_dropped_slots(T, k, E):
+    """Above 1024 slots the sort runs over several blocks: ids -1 (finished tokens) and out of
+    range, a skewed key mix, and block boundaries inside runs of equal keys."""
+    rng = np.random.default_rng(T)
+    ids = synth.gen.random_ids(T, k, E, seed=T, skew=True)
+    drop = rng.random((T, k)) < 0.1
+    ids[drop] = -1
+    ids[rng.random((T, k)) < 0.01] = E + 3
+    w = rng.random((T, k), dtype=np.float32)
+    x = rng.standard_normal((T, 8)).astype(np.float16)
+    case(f"permute multi-block T={T} k={k} E={E}")
+    perm, inv, off, xp, wp = q.moe_permute(dev(ids), dev(w), dev(x), E)
+    valid = (ids >= 0) & (ids < E)
+    keys = np.where(valid, ids, E).ravel()               # dropped slots sort after every expert
+    order = np.argsort(keys, kind="stable")
+    n_valid = int(valid.sum())
+    r_perm = np.full(T * k, -1, np.int64)
+    r_perm[:n_valid] = order[:n_valid]
+    r_inv = np.full(T * k, -1, np.int64)
+    r_inv[order[:n_valid]] = np.arange(n_valid)
+    r_off = np.concatenate([[0], np.cumsum(np.bincount(ids[valid], minlength=E))])
+    assert np.array_equal(host(perm), r_perm)
+    assert np.array_equal(host(inv), r_inv)
+    assert np.array_equal(host(off), r_off)
+    r_wp = np.zeros(T * k, np.float32)
+    r_wp[:n_valid] = w.ravel()[order[:n_valid]]
+    assert np.array_equal(host(wp), r_wp)
+
+
 def test_permute_drops_ids_out_of_range():
     case("permute out-of-range ids")
     ids = np.array([[0, 3], [7, 1], [2, -1]], np.int32)       # 7 and -1 are outside [0, 4)
