@@ -143,59 +143,73 @@ __device__ __forceinline__ u32x4 load_weights16(const u32x4* p) {
     return __builtin_nontemporal_load(p);
 }
 
-// ------------------------------------------------------------------------------------
-// Tile lookup: m-tile `mt` of the grouped GEMM -> (expert, first row, rows).
-// Experts are visited in order; expert e contributes ceil(c_e / BM) m-tiles where c_e is
-// its row count taken from the offsets, clamped into [0, R] so that any offsets array
-// yields in-bounds rows.  Executed by a whole wave; returns false when mt is past the end.
+// Inclusive prefix sum over the 64 lanes of a wave.  Row shifts by 1, 2, 4 and 8 lanes give the
+// sums within each row of 16 lanes; broadcasting lane 15 into rows 1 and 3, then lane 31 into rows
+// 2 and 3, adds the totals of the rows before.  A lane that a shift or broadcast does not reach
+// adds 0 (the `old` operand).  Six DPP additions instead of a chain of cross-lane permutes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return v;
+}
+
 // ------------------------------------------------------------------------------------
 // Tile lookup in one pass over the offsets: the total number of m-tiles (sum over experts of
 // ceil(c_e / BM)) and, for logical tile index `want` (a function of that total), the expert,
-// first row and row count.  Row counts come from the offsets clamped into [0, R], so any
+// first row and row count.  Experts are visited in order, 64 per lane chunk; only the chunks
+// that hold experts are scanned.  Row counts come from the offsets clamped into [0, R], so any
 // offsets array yields in-bounds rows.  Executed by a whole wave; results are wave-uniform.
 // Returns false when `want` maps past the last tile.
+// ------------------------------------------------------------------------------------
 template <int BM, typename F>
 __device__ __forceinline__ bool lookup_m_tile(const int32_t* __restrict__ offsets, int E, int R,
                                               F want_of_total, int& mt_out, int& e_out,
                                               int& row0, int& rows) {
     const int lane = threadIdx.x & (kWave - 1);
     constexpr int MAXC = (MOE_MAX_EXPERTS + kWave - 1) / kWave;
+    const int nc = (E + kWave - 1) / kWave;          // chunks holding experts (wave-uniform)
     int lo[MAXC], hi[MAXC], tl[MAXC], incl[MAXC];
-    int total = 0;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
         const int e = c * kWave + lane;
         lo[c] = hi[c] = 0;
-        if (e < E) {
+        if (c < nc && e < E) {
             lo[c] = min(max(offsets[e], 0), R);
             hi[c] = min(max(offsets[e + 1], 0), R);
         }
-        tl[c] = (max(hi[c] - lo[c], 0) + BM - 1) / BM;
-        int v = tl[c];
+    }
+    int total = 0;
 #pragma unroll
-        for (int s = 1; s < kWave; s <<= 1) {
-            const int u = __shfl_up(v, s, kWave);
-            if (lane >= s) v += u;
+    for (int c = 0; c < MAXC; ++c) {
+        tl[c] = (max(hi[c] - lo[c], 0) + BM - 1) / BM;
+        incl[c] = total;
+        if (c < nc) {
+            const int v = wave_incl_scan(tl[c]);
+            incl[c] = total + v;
+            total += __builtin_amdgcn_readlane(v, kWave - 1);
         }
-        incl[c] = total + v;
-        total += __shfl(v, kWave - 1, kWave);
     }
     total = __builtin_amdgcn_readfirstlane(total);
     const int mt = want_of_total(total);
     if (mt < 0 || mt >= total) return false;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
+        if (c >= nc) break;
         const int excl = incl[c] - tl[c];
         const unsigned long long hit = __ballot(tl[c] > 0 && mt >= excl && mt < incl[c]);
         if (hit) {
-            const int src = __builtin_ctzll(hit);
+            const int src = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
             const int my_row0 = lo[c] + (mt - excl) * BM;
             const int my_rows = min(BM, hi[c] - my_row0);
             mt_out = mt;
-            e_out = __builtin_amdgcn_readfirstlane(__shfl(c * kWave + lane, src, kWave));
-            row0 = __builtin_amdgcn_readfirstlane(__shfl(my_row0, src, kWave));
-            rows = __builtin_amdgcn_readfirstlane(__shfl(my_rows, src, kWave));
-            return true;
+            e_out = c * kWave + src;
+            row0 = __builtin_amdgcn_readlane(my_row0, src);
+            rows = __builtin_amdgcn_readlane(my_rows, src);
+            return rows > 0 && row0 >= 0 && row0 + rows <= R;
         }
     }
     return false;

@@ -264,6 +264,25 @@ template <int WT, int ACT, int MS, int NS> constexpr int tile_lds_halves() {
     return stages > epi ? stages : epi;
 }
 
+// Weight loads of the tile path while LDS-DMA loads are in flight.  The compiler counts
+// outstanding vector loads exactly only while every pending load fills registers: with LDS-DMA
+// loads pending it waits for all of them (vmcnt 0) before a register load's first use, which
+// would drain the A stages loaded two ahead at every stage.  These weight loads are therefore
+// issued as instructions of their own; the per-stage wait counts them (vector memory loads
+// complete in order), and tie_to_wait() makes every later use of a register depend on an
+// instruction placed after that wait.  Between the load and the wait nothing reads or moves the
+// destination registers (the test suite checks the generated code for this).
+__device__ __forceinline__ void issue_load16(u32x4& dst, const void* ptr) {
+    asm volatile("global_load_dwordx4 %0, %1, off ; weight load" : "=&v"(dst) : "v"(ptr) : "memory");
+}
+__device__ __forceinline__ void issue_load_u16(uint32_t& dst, const void* ptr) {
+    asm volatile("global_load_ushort %0, %1, off ; weight load" : "=&v"(dst) : "v"(ptr) : "memory");
+}
+template <typename T>
+__device__ __forceinline__ void tie_to_wait(T& v) {
+    asm volatile("; weights ready %0" : "+v"(v));
+}
+
 template <int WT, int ACT, bool GROUPED, int MA, int NS, int BM>
 __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__ lds, int e,
                                           int row0, int rows, int cbg) {
@@ -363,8 +382,11 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
 
     // group scales: one per (column block, super-block) -- a super-block never spans groups
     constexpr int SCS = GROUPED ? SBPS : 1;
-    u32x4 bcur[NS][SBPS], bnext[NS][SBPS];
-    uint32_t scur[NS][SCS] = {}, snext[NS][SCS] = {};
+    // Two weight buffers that alternate statically (the stage loops below run two stages per
+    // iteration): copying a buffer whose loads are in flight would make the compiler wait for
+    // every outstanding load, the A stages two ahead included, at the top of each stage.
+    u32x4 bbuf[2][NS][SBPS];
+    uint32_t sbuf[2][NS][SCS] = {};
     auto load_b = [&](u32x4 (&b)[NS][SBPS], uint32_t (&sc)[NS][SCS], int st) {
 #pragma unroll
         for (int c = 0; c < NS; ++c) {
@@ -373,6 +395,28 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
                 b[c][q] = wp[c][(size_t)(st * SBPS + q) * kWave];
                 if constexpr (GROUPED)
                     sc[c][q] = (uint32_t)sp[(size_t)((st * KC + q * KSB) >> 7) * N + ncol[c]];
+            }
+        }
+    };
+    // the same loads issued by hand (DMA path), and the ties that follow their wait
+    auto issue_b = [&](u32x4 (&b)[NS][SBPS], uint32_t (&sc)[NS][SCS], int st) {
+#pragma unroll
+        for (int c = 0; c < NS; ++c) {
+#pragma unroll
+            for (int q = 0; q < SBPS; ++q) {
+                issue_load16(b[c][q], wp[c] + (size_t)(st * SBPS + q) * kWave);
+                if constexpr (GROUPED)
+                    issue_load_u16(sc[c][q], sp + (size_t)((st * KC + q * KSB) >> 7) * N + ncol[c]);
+            }
+        }
+    };
+    auto tie_b = [&](u32x4 (&b)[NS][SBPS], uint32_t (&sc)[NS][SCS]) {
+#pragma unroll
+        for (int c = 0; c < NS; ++c) {
+#pragma unroll
+            for (int q = 0; q < SBPS; ++q) {
+                tie_to_wait(b[c][q]);
+                if constexpr (GROUPED) tie_to_wait(sc[c][q]);
             }
         }
     };
@@ -387,7 +431,8 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
     const int nstage = K / KC;
     const int lrow = lane & 15;
     // one stage's MFMAs from the A stage in abuf and the weights in bcur / scur
-    auto compute_stage = [&](const f16* abuf) {
+    auto compute_stage = [&](const f16* abuf, const u32x4 (&bcur)[NS][SBPS],
+                             const uint32_t (&scur)[NS][SCS]) {
         // the weight fragments of K-step ks+1 are expanded while the MFMAs of ks issue
         auto expand = [&](f16x8 (&bq)[NS], int ks) {
 #pragma unroll
@@ -417,48 +462,48 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
             }
         }
     };
-    auto advance_b = [&] {
-#pragma unroll
-        for (int c = 0; c < NS; ++c) {
-#pragma unroll
-            for (int q = 0; q < SBPS; ++q) bcur[c][q] = bnext[c][q];
-#pragma unroll
-            for (int q = 0; q < SCS; ++q) scur[c][q] = snext[c][q];
-        }
-    };
 
     if constexpr (DMA_A) {
-        // prologue: A stages 0 .. AD-2, then the weights of stage 0
+        // prologue: A stage 0, the weights of stage 0, then A stages 1 .. AD-2
+        dma_a(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_b(bbuf[0], sbuf[0], 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s0 = 0; s0 < AD - 1; ++s0) dma_a(min(s0, nstage - 1), s0);
-        load_b(bcur, scur, 0);
+        for (int s0 = 1; s0 < AD - 1; ++s0) dma_a(min(s0, nstage - 1), s0);
 
-        // Waits.  Per stage a wave issues, in this order, NB weight / scale loads (stage
-        // st + 1) and NA A loads (stage st + AD - 1); vector memory loads complete in order, so
-        // once at most (AD - 2) * NA + NB loads are outstanding, this wave's A loads of stage
-        // st are done.  The barrier after the wait makes every wave's A loads of stage st
-        // visible and frees the buffer stage st - 1 used, which the stage's new A loads
-        // overwrite.  (The barrier is issued bare: the compiler's fence before a block barrier
-        // would wait for all A loads in flight.)  The count holds for the first stages too,
-        // whose prologue order is the A stages 0 .. AD - 2, then the weights of stage 0.
-        constexpr int NB = NS * SBPS * (GROUPED ? 2 : 1);
-        constexpr int NWAIT = (AD - 2) * NA + NB;
+        // Waits.  Per stage a wave issues, in this order, the weight / scale loads of stage
+        // st + 1 and NA A loads (stage st + AD - 1); vector memory loads complete in order, so
+        // once at most (AD - 2) * NA loads are outstanding, the weights of stage st (issued
+        // before the A loads of stage st + AD - 2) and this wave's A loads of stage st (issued
+        // before those) are done.  The barrier after the wait makes every wave's A loads of
+        // stage st visible and frees the buffer stage st - 1 used, which the stage's new A
+        // loads overwrite.  (The barrier is issued bare: the compiler's fence before a block
+        // barrier would wait for all A loads in flight.)  The count holds for the first stages
+        // too, whose prologue order is A stage 0, the weights of stage 0, A stages 1 .. AD - 2.
+        constexpr int NWAIT = (AD - 2) * NA;
         static_assert(NWAIT < 64, "vmcnt field");
         constexpr int WAITCNT = (NWAIT & 15) | ((NWAIT >> 4) << 14) | (7 << 4) | (15 << 8);
 
-        for (int st = 0; st < nstage; ++st) {
+        auto stage = [&](int st, u32x4 (&bc)[NS][SBPS], uint32_t (&sc)[NS][SCS],
+                         u32x4 (&bn)[NS][SBPS], uint32_t (&sn)[NS][SCS]) {
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_waitcnt(WAITCNT);
+            __builtin_amdgcn_sched_barrier(0);
+            tie_b(bc, sc);
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            const int nxt = min(st + 1, nstage - 1);
-            load_b(bnext, snext, nxt);
+            issue_b(bn, sn, min(st + 1, nstage - 1));
+            __builtin_amdgcn_sched_barrier(0);
             dma_a(min(st + AD - 1, nstage - 1), (st + AD - 1) % AD);
             // keep the prefetch at the top: the scheduler would otherwise sink the loads next
             // to their first use at the end of the stage and expose their full latency
             __builtin_amdgcn_sched_barrier(0);
-            compute_stage(lds + (st % AD) * LDS_BUF);
-            advance_b();
+            compute_stage(lds + (st % AD) * LDS_BUF, bc, sc);
+        };
+        for (int st = 0; st < nstage; st += 2) {
+            stage(st, bbuf[0], sbuf[0], bbuf[1], sbuf[1]);
+            if (st + 1 < nstage) stage(st + 1, bbuf[1], sbuf[1], bbuf[0], sbuf[0]);
         }
         // the last stages loaded repeats of the last one; they must land before the epilogue
         // reuses the LDS
@@ -466,7 +511,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         __syncthreads();
     } else {
         load_a(0, 0);
-        load_b(bcur, scur, 0);
+        load_b(bbuf[0], sbuf[0], 0);
         load_a(1, min(1, nstage - 1));
         store_a(0, 0);
         __syncthreads();
@@ -474,21 +519,23 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         // The stage body is branch-free: the last stages prefetch (and store to the idle LDS
         // buffer) copies of the last one, so the compiler can count outstanding loads exactly
         // and keep the following stages' loads in flight across the whole compute of this one.
-        // The loop runs two stages per iteration so the A register sets alternate statically.
-        auto stage = [&](int st, int set_new, int set_old) {
+        // The loop runs two stages per iteration so the A register sets and the weight buffers
+        // alternate statically.
+        auto stage = [&](int st, int set_new, int set_old, const u32x4 (&bc)[NS][SBPS],
+                         const uint32_t (&sc)[NS][SCS], u32x4 (&bn)[NS][SBPS],
+                         uint32_t (&sn)[NS][SCS]) {
             const int nxt = min(st + 1, nstage - 1);
             load_a(set_new, min(st + 2, nstage - 1));
-            load_b(bnext, snext, nxt);
+            load_b(bn, sn, nxt);
             // keep the prefetch at the top (see above)
             __builtin_amdgcn_sched_barrier(0);
-            compute_stage(lds + (st & 1) * LDS_BUF);
+            compute_stage(lds + (st & 1) * LDS_BUF, bc, sc);
             store_a(set_old, (st + 1) & 1);
             __syncthreads();
-            advance_b();
         };
         for (int st = 0; st < nstage; st += 2) {
-            stage(st, 0, 1);
-            if (st + 1 < nstage) stage(st + 1, 1, 0);
+            stage(st, 0, 1, bbuf[0], sbuf[0], bbuf[1], sbuf[1]);
+            if (st + 1 < nstage) stage(st + 1, 1, 0, bbuf[1], sbuf[1], bbuf[0], sbuf[0]);
         }
 #pragma unroll
         for (int set = 0; set < 2; ++set)
@@ -500,9 +547,9 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
 #pragma unroll
     for (int c = 0; c < NS; ++c) {
 #pragma unroll
-        for (int q = 0; q < SBPS; ++q) consume(bnext[c][q]);
+        for (int q = 0; q < SBPS; ++q) { consume(bbuf[0][c][q]); consume(bbuf[1][c][q]); }
 #pragma unroll
-        for (int q = 0; q < SCS; ++q) consume(snext[c][q]);
+        for (int q = 0; q < SCS; ++q) { consume(sbuf[0][c][q]); consume(sbuf[1][c][q]); }
     }
 
     // epilogue: lane holds row (lane & 15) of each subtile, 4 consecutive columns per block
