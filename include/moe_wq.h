@@ -69,7 +69,8 @@ enum moe_tile  { MOE_TILE_AUTO = 0,           /* chosen from R, E, K, N         
                  MOE_TILE_64x256 = 1,         /* tile path: 64 rows x 256 weight columns */
                  MOE_TILE_64x128 = 2,         /*            64 rows x 128 weight columns */
                  MOE_TILE_128x128 = 3,        /*           128 rows x 128 weight columns */
-                 MOE_TILE_48x256 = 4 };       /*            48 rows x 256 weight columns */
+                 MOE_TILE_48x256 = 4,         /*            48 rows x 256 weight columns */
+                 MOE_TILE_48x128 = 5 };       /*            48 rows x 128 weight columns */
 
 typedef struct moe_gemm_opts {
     int32_t path;      /* enum moe_path                                              */

@@ -19,7 +19,7 @@ __all__ = [
     "MOE_ERR_NO_DEVICE", "MOE_ERR_HIP",
     "GATE_TOPK", "GATE_ALL", "W_INT4", "W_INT8", "W_FP16", "ACT_NONE", "ACT_RELU",
     "ACT_SWIGLU", "PATH_AUTO", "PATH_STREAM", "PATH_TILE", "TILE_AUTO", "TILE_64x256",
-    "TILE_64x128", "TILE_128x128", "TILE_48x256", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SPLIT_K",
+    "TILE_64x128", "TILE_128x128", "TILE_48x256", "TILE_48x128", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SPLIT_K",
     "MoEError", "MoELibraryError", "lib", "lib_path", "status_str", "version",
     "moe_route_topk", "moe_route_topk_active", "moe_permute", "moe_grouped_gemm_wq",
     "moe_grouped_gemm_wq_rows",
@@ -37,7 +37,7 @@ GATE_TOPK, GATE_ALL = 0, 1
 W_INT4, W_INT8, W_FP16 = 0, 1, 2
 ACT_NONE, ACT_RELU, ACT_SWIGLU = 0, 1, 2
 PATH_AUTO, PATH_STREAM, PATH_TILE = 0, 1, 2
-TILE_AUTO, TILE_64x256, TILE_64x128, TILE_128x128, TILE_48x256 = 0, 1, 2, 3, 4
+TILE_AUTO, TILE_64x256, TILE_64x128, TILE_128x128, TILE_48x256, TILE_48x128 = 0, 1, 2, 3, 4, 5
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_SPLIT_K = 256, 8, 8
 MOE_DECODE_MAX_TOKENS, MOE_DECODE_MAX_ROWS = 64, 512
 

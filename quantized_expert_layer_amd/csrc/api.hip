@@ -69,7 +69,7 @@ int32_t validate_gemm(const uint16_t* a, const int32_t* offsets, int32_t R, int3
     if (opts) {
         if (opts->path < MOE_PATH_AUTO || opts->path > MOE_PATH_TILE) return MOE_ERR_INVALID;
         if (opts->split_k < 0 || opts->split_k > MOE_MAX_SPLIT_K) return MOE_ERR_INVALID;
-        if (opts->tile < MOE_TILE_AUTO || opts->tile > MOE_TILE_48x256) return MOE_ERR_INVALID;
+        if (opts->tile < MOE_TILE_AUTO || opts->tile > MOE_TILE_48x128) return MOE_ERR_INVALID;
     }
     if ((int64_t)R * K >= (int64_t)1 << 40) return MOE_ERR_UNSUPPORTED;
     if (R == 0) return MOE_OK;

@@ -80,8 +80,22 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmP
     // first and the surplus of the upper-bound grid exits last
     const int cbo = blockIdx.x % nbo;
     const int mt = blockIdx.x / nbo;
-    int e, row0, rows;
-    if (!find_m_tile<16>(p.offsets, p.E, p.R, mt, e, row0, rows)) return;   // block-uniform
+    // one wave looks the tile up and hands it to the others (fewer requests on the offsets)
+    __shared__ int tile_info[3];
+    if (threadIdx.x < kWave) {
+        int e0, r0, nr;
+        const bool ok = find_m_tile<16>(p.offsets, p.E, p.R, mt, e0, r0, nr);
+        if (threadIdx.x == 0) {
+            tile_info[0] = ok ? e0 : -1;
+            tile_info[1] = r0;
+            tile_info[2] = nr;
+        }
+    }
+    __syncthreads();
+    const int e = __builtin_amdgcn_readfirstlane(tile_info[0]);
+    if (e < 0) return;                                                          // block-uniform
+    const int row0 = __builtin_amdgcn_readfirstlane(tile_info[1]);
+    const int rows = __builtin_amdgcn_readfirstlane(tile_info[2]);
 
     const int K = p.K, N = p.N;
     const int nSB = K / KSB;
@@ -614,7 +628,11 @@ template <int WT, int ACT, bool GROUPED, int MS, int NS>
 __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmParams p, int ncbg, int mt_ub,
                                                            int grid_real, int a_major) {
     constexpr int BM = 16 * MS;
-    __shared__ __attribute__((aligned(16))) f16 lds[tile_lds_halves<WT, ACT, MS, NS>()];
+    // the A ring starts the block's LDS (its DMA writes stay aligned); 16 bytes after the body's
+    // LDS carry the tile from the wave that looks it up to the others
+    constexpr int kBodyHalves = tile_lds_halves<WT, ACT, MS, NS>();
+    __shared__ __attribute__((aligned(1024))) f16 lds[kBodyHalves + 8];
+    int* const tile_info = (int*)(lds + kBodyHalves);
 
     // XCD-aware order: hardware block b runs on XCD b % 8.  The real tiles (counted from the
     // offsets, not the host's upper bound) are split into 8 equal contiguous ranges, one per
@@ -632,9 +650,24 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmParams p, int ncb
         if (j >= G8 || L >= real) return -1;
         return a_major ? L / ncbg : L % total;
     };
-    int mt, e, row0, rows;
-    if (!lookup_m_tile<BM>(p.offsets, p.E, p.R, logical_mt, mt, e, row0, rows)) return;
-    const int cbg = a_major ? L % ncbg : L / mtiles;
+    // one wave looks the tile up and hands it to the others: every block reads the same few
+    // offsets at launch, so four waves per block would quadruple the requests on one L2 channel
+    if (threadIdx.x < kWave) {
+        int mt, e0, r0, nr;
+        const bool ok = lookup_m_tile<BM>(p.offsets, p.E, p.R, logical_mt, mt, e0, r0, nr);
+        if (threadIdx.x == 0) {
+            tile_info[0] = ok ? e0 : -1;
+            tile_info[1] = r0;
+            tile_info[2] = nr;
+            tile_info[3] = ok ? (a_major ? L % ncbg : L / mtiles) : 0;
+        }
+    }
+    __syncthreads();
+    const int e = __builtin_amdgcn_readfirstlane(tile_info[0]);
+    if (e < 0) return;
+    const int row0 = __builtin_amdgcn_readfirstlane(tile_info[1]);
+    const int rows = __builtin_amdgcn_readfirstlane(tile_info[2]);
+    const int cbg = __builtin_amdgcn_readfirstlane(tile_info[3]);
     // body specialised for the tile's number of 16-row subtiles (1, 2, 3, 4; 5-6 as 6; MS)
     static_assert(MS >= 3, "the subtile cases below assume tiles of at least 48 rows");
     switch ((rows + 15) / 16) {
@@ -724,26 +757,40 @@ static hipError_t tile_launch(const GemmParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Block tile of the tile path.  64x256 (4 subtiles x 4 column blocks per wave) expands each
-// weight fragment for 4 MFMAs; 64x128 gives twice the blocks when N is small; 128x128
-// (8 x 2) expands each fragment for 8 MFMAs but measured slower at every shape here (it
-// holds 64 KB of LDS per block and reads twice the A fragments per MFMA), so it is only
-// used when asked for.
-int gemm_choose_tile(int R, int E, int N, int act, int forced) {
-    if (forced >= MOE_TILE_64x256 && forced <= MOE_TILE_48x256) return forced;
+// Block tile of the tile path.  Measured on the layer shapes here (rotated weights, one GEMM per
+// call): with integer codes, 48-row tiles beat 64-row ones wherever experts hold few rows (fewer
+// padded rows in each expert's last tile, and about two full rounds of blocks instead of one and a
+// half) and for per-channel scales at every size; 64x256 stays ahead for group scales once an
+// expert holds about 96 rows or more.  8-bit codes keep to 128-column tiles (their 256-column
+// bodies hold too many registers for three waves per SIMD).  fp16 weights: 64x256 when there are
+// blocks for four per CU, else 64x128.  128x128 is only used when asked for.
+int gemm_choose_tile(int R, int E, int N, int act, int wtype, bool grouped, int forced) {
+    if (forced >= MOE_TILE_64x256 && forced <= MOE_TILE_48x128) return forced;
     const int active = R < E ? R : E;
     const int nbo = (act == MOE_ACT_SWIGLU) ? N / 32 : N / 16;
-    const int opw = (act == MOE_ACT_SWIGLU) ? 2 : 4;
-    const long blocks_wide = (long)cdiv(nbo, 4 * opw) * (cdiv(R, 64) + active / 2);
-    return blocks_wide >= 4L * 256 ? MOE_TILE_64x256 : MOE_TILE_64x128;
+    const int opw = (act == MOE_ACT_SWIGLU) ? 2 : 4;           // output blocks per wave, 256 wide
+    const long groups_wide = cdiv(nbo, 4 * opw);
+    if (wtype == MOE_W_FP16) {
+        const long blocks_wide = groups_wide * (cdiv(R, 64) + active / 2);
+        return blocks_wide >= 4L * 256 ? MOE_TILE_64x256 : MOE_TILE_64x128;
+    }
+    const double rows_per_expert = active > 0 ? (double)R / active : 0.0;
+    if (wtype == MOE_W_INT8) {
+        const long blocks_wide = groups_wide * (cdiv(R, 64) + active / 2);
+        return blocks_wide >= 4L * 256 ? MOE_TILE_48x128 : MOE_TILE_64x128;
+    }
+    if (grouped && rows_per_expert >= 96.0) return MOE_TILE_64x256;
+    const long blocks_48 = groups_wide * (cdiv(R, 48) + active / 2);
+    return blocks_48 >= 256 ? MOE_TILE_48x256 : MOE_TILE_48x128;
 }
 
 template <int WT, int ACT, bool GROUPED>
 static hipError_t tile_dispatch(const GemmParams& p, hipStream_t stream) {
-    switch (gemm_choose_tile(p.R, p.E, p.N, ACT, p.tile)) {
+    switch (gemm_choose_tile(p.R, p.E, p.N, ACT, WT, GROUPED, p.tile)) {
         case MOE_TILE_64x256: return tile_launch<WT, ACT, GROUPED, 4, 4>(p, stream);
         case MOE_TILE_128x128: return tile_launch<WT, ACT, GROUPED, 8, 2>(p, stream);
         case MOE_TILE_48x256: return tile_launch<WT, ACT, GROUPED, 3, 4>(p, stream);
+        case MOE_TILE_48x128: return tile_launch<WT, ACT, GROUPED, 3, 2>(p, stream);
         default: return tile_launch<WT, ACT, GROUPED, 4, 2>(p, stream);
     }
 }

@@ -56,7 +56,7 @@ struct GemmParams {
 // Path/split decisions (host-only, deterministic in the arguments).
 int gemm_choose_path(int R, int E, int K, int N, int wtype, int act, int forced);
 int gemm_choose_split(int R, int E, int K, int N, int wtype, int act, int forced);
-int gemm_choose_tile(int R, int E, int N, int act, int forced);
+int gemm_choose_tile(int R, int E, int N, int act, int wtype, bool grouped, int forced);
 
 hipError_t launch_gemm_stream(const GemmParams& p, hipStream_t stream);
 hipError_t launch_gemm_tile(const GemmParams& p, hipStream_t stream);

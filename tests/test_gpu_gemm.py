@@ -84,7 +84,7 @@ GEMM_CASES = [
 
 PATHS = [(q.PATH_STREAM, q.TILE_AUTO), (q.PATH_TILE, q.TILE_64x256),
          (q.PATH_TILE, q.TILE_64x128), (q.PATH_TILE, q.TILE_128x128),
-         (q.PATH_TILE, q.TILE_48x256)]
+         (q.PATH_TILE, q.TILE_48x256), (q.PATH_TILE, q.TILE_48x128)]
 
 # expert row counts hitting every specialised body of the tile kernel (1, 2, 3, 4, 6 and all
 # 16-row subtiles, as whole tiles and as the ragged last tile of a larger expert), an empty
