@@ -30,10 +30,11 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict
     if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
-// Each wave runs 16 independent chains of v_mfma_f32_16x16x32_f16 on all-ones operands (the
-// form needs about 16 accumulators in flight per wave to issue at full rate; 8 reach about
-// 60% of it), so every MFMA adds exactly 32 to each accumulator element; out[thread] = sum
-// over the chains of element 0 = 16 * 32 * iters (exact in fp32 for iters < 2^15).
+// Each wave runs 16 independent chains of v_mfma_f32_16x16x32_f16 on all-ones operands (with 8
+// the compiler moves every accumulator through other registers each iteration, and the loop
+// reaches about 60% of this one), so every MFMA adds exactly 32 to each accumulator element;
+// out[thread] = sum over the chains of element 0 = 16 * 32 * iters (exact in fp32 for
+// iters < 2^15).
 constexpr int kProbeChains = 16;
 __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* __restrict__ out) {
     f16x8 a, b;
