@@ -12,6 +12,36 @@ __device__ __forceinline__ bool route_before(float va, int ia, float vb, int ib)
     return va > vb || (va == vb && ia < ib);
 }
 
+// Wave-wide reductions by DPP: row shifts by 1, 2, 4 and 8 lanes, then broadcasts of lanes 15
+// and 31 into the rows after them, leave the reduction of all 64 lanes in lane 63, which every
+// lane then reads.  Lanes a shift or broadcast does not reach combine with `ident`.  Max and min
+// are exact in any order; the sum has this one fixed order, the same on every lane.
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_bits(int v, int ident, Op op) {
+    v = op(v, __builtin_amdgcn_update_dpp(ident, v, 0x111, 0xF, 0xF, false));   // row_shr:1
+    v = op(v, __builtin_amdgcn_update_dpp(ident, v, 0x112, 0xF, 0xF, false));   // row_shr:2
+    v = op(v, __builtin_amdgcn_update_dpp(ident, v, 0x114, 0xF, 0xF, false));   // row_shr:4
+    v = op(v, __builtin_amdgcn_update_dpp(ident, v, 0x118, 0xF, 0xF, false));   // row_shr:8
+    v = op(v, __builtin_amdgcn_update_dpp(ident, v, 0x142, 0xA, 0xF, false));   // row_bcast:15
+    v = op(v, __builtin_amdgcn_update_dpp(ident, v, 0x143, 0xC, 0xF, false));   // row_bcast:31
+    return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+    return __builtin_bit_cast(float, wave_reduce_bits(
+        __builtin_bit_cast(int, v), __builtin_bit_cast(int, -__builtin_inff()), [](int a, int b) {
+            return __builtin_bit_cast(int, fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)));
+        }));
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+    return wave_reduce_bits(v, 0x7fffffff, [](int a, int b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    return __builtin_bit_cast(float, wave_reduce_bits(
+        __builtin_bit_cast(int, v), 0, [](int a, int b) {
+            return __builtin_bit_cast(int, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+        }));
+}
+
 // One wave, row = the token's E logits.  Lane j < k receives choice j: its expert (out_e) and
 // gate weight (out_w).  Softmax over the k chosen logits, or over all E (gate_all) keeping the
 // k chosen entries; fp32, exp(l - m) / sum with m the largest logit.  NaN orders as -inf.
@@ -42,13 +72,11 @@ __device__ __forceinline__ void topk_token(const float* row, int E, int k, int g
             const int e = lane + i * kWave;
             if (!taken[i] && route_before(v[i], e, bv, be)) { bv = v[i]; be = e; }
         }
-        // wave arg-best (butterfly: every lane ends with the same winner)
-#pragma unroll
-        for (int s = 1; s < kWave; s <<= 1) {
-            const float ov = __shfl_xor(bv, s, kWave);
-            const int oe = __shfl_xor(be, s, kWave);
-            if (route_before(ov, oe, bv, be)) { bv = ov; be = oe; }
-        }
+        // wave arg-best: the largest value, then the smallest index holding it (every lane
+        // ends with the same winner)
+        const float wm = wave_max_f32(bv);
+        be = wave_min_i32(bv == wm ? be : 0x7fffffff);
+        bv = wm;
         sel_v[j] = bv;
         sel_e[j] = be;
 #pragma unroll
@@ -63,9 +91,7 @@ __device__ __forceinline__ void topk_token(const float* row, int E, int k, int g
 #pragma unroll
         for (int i = 0; i < PER_LANE; ++i)
             if (lane + i * kWave < E) part += expf(v[i] - m);
-#pragma unroll
-        for (int s = 1; s < kWave; s <<= 1) part += __shfl_xor(part, s, kWave);
-        denom = part;
+        denom = wave_sum_f32(part);
     } else {
 #pragma unroll
         for (int j = 0; j < MOE_MAX_TOPK; ++j)
