@@ -112,19 +112,14 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_combine_kernel(Comb
             }
             const int cnt = max(hi - lo, 0);
             const int nt = (cnt + 15) / 16;
-            int incl = nt;
-#pragma unroll
-            for (int s = 1; s < kWave; s <<= 1) {
-                const int v = __shfl_up(incl, s, kWave);
-                if (lane >= s) incl += v;
-            }
+            const int incl = wave_incl_scan(nt);
             const int b0 = base + incl - nt;
             for (int i = 0; i < nt && b0 + i < kCombineMaxTiles; ++i) {
                 tile_e[b0 + i] = e;
                 tile_r0[b0 + i] = lo + 16 * i;
                 tile_n[b0 + i] = min(16, cnt - 16 * i);
             }
-            base += __shfl(incl, kWave - 1, kWave);
+            base += __builtin_amdgcn_readlane(incl, kWave - 1);
         }
         if (lane == 0) n_tiles = min(base, kCombineMaxTiles);
     }

@@ -102,11 +102,7 @@ __global__ __launch_bounds__(1024) void sort_scatter_kernel(
                 if (b < (int)blockIdx.x) pre += h;
             }
         }
-        incl = tot;
-        for (int s = 1; s < kWave; s <<= 1) {
-            const int v = __shfl_up(incl, s, kWave);
-            if (lane >= s) incl += v;
-        }
+        incl = wave_incl_scan(tot);
         if (lane == kWave - 1) wave_sum[wave] = incl;
     }
     __syncthreads();

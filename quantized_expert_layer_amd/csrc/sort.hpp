@@ -80,11 +80,7 @@ __device__ __forceinline__ void sort_block(int R, int E, KeyOf key_of, WOf w_of,
         const int e = threadIdx.x;
         if (e < E)
             for (int w = 0; w < kSortWaves; ++w) tot += cnt[w][e];
-        incl = tot;
-        for (int s = 1; s < kWave; s <<= 1) {
-            const int v = __shfl_up(incl, s, kWave);
-            if (lane >= s) incl += v;
-        }
+        incl = wave_incl_scan(tot);
         if (lane == kWave - 1) wave_sum[wave] = incl;
     }
     __syncthreads();
@@ -164,17 +160,12 @@ __device__ __forceinline__ void sort_wave(int R, int E, KeyOf key_of, WOf w_of, 
     for (int c0 = 0; c0 < E; c0 += kWave) {
         const int e = c0 + lane;
         const int v = e < E ? cnt[e] : 0;
-        int incl = v;
-#pragma unroll
-        for (int s = 1; s < kWave; s <<= 1) {
-            const int u = __shfl_up(incl, s, kWave);
-            if (lane >= s) incl += u;
-        }
+        const int incl = wave_incl_scan(v);
         if (e < E) {
             offsets[e] = run + incl - v;
             cnt[e] = run + incl - v;
         }
-        run += __shfl(incl, kWave - 1, kWave);
+        run += __builtin_amdgcn_readlane(incl, kWave - 1);
     }
     if (lane == 0) offsets[E] = run;
     phase();
