@@ -80,22 +80,8 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmP
     // first and the surplus of the upper-bound grid exits last
     const int cbo = blockIdx.x % nbo;
     const int mt = blockIdx.x / nbo;
-    // one wave looks the tile up and hands it to the others (fewer requests on the offsets)
-    __shared__ int tile_info[3];
-    if (threadIdx.x < kWave) {
-        int e0, r0, nr;
-        const bool ok = find_m_tile<16>(p.offsets, p.E, p.R, mt, e0, r0, nr);
-        if (threadIdx.x == 0) {
-            tile_info[0] = ok ? e0 : -1;
-            tile_info[1] = r0;
-            tile_info[2] = nr;
-        }
-    }
-    __syncthreads();
-    const int e = __builtin_amdgcn_readfirstlane(tile_info[0]);
-    if (e < 0) return;                                                          // block-uniform
-    const int row0 = __builtin_amdgcn_readfirstlane(tile_info[1]);
-    const int rows = __builtin_amdgcn_readfirstlane(tile_info[2]);
+    int e, row0, rows;
+    if (!find_m_tile<16>(p.offsets, p.E, p.R, mt, e, row0, rows)) return;   // block-uniform
 
     const int K = p.K, N = p.N;
     const int nSB = K / KSB;
@@ -271,11 +257,14 @@ template <int WT> constexpr int tile_a_stages() { return WT == MOE_W_FP16 ? 2 : 
 template <int ACT, int NS> constexpr int tile_epi_stride() {
     return (ACT == MOE_ACT_SWIGLU ? NS / 2 : NS) * 16 + 8;
 }
-// LDS of one block: the double-buffered A stages, or the 4 waves' epilogue regions if larger.
-template <int WT, int ACT, int MS, int NS> constexpr int tile_lds_halves() {
-    const int stages = tile_a_stages<WT>() * 16 * MS * tile_kc<WT>();
+// LDS of one block: the A stages of its KG groups, the fp32 partial tiles of groups 1..KG-1,
+// or the 4 waves' epilogue regions, whichever is largest.
+template <int WT, int ACT, int MS, int NS, int KG = 1> constexpr int tile_lds_halves() {
+    const int stages = KG * tile_a_stages<WT>() * 16 * MS * tile_kc<WT>();
+    const int partial = (KG - 1) * 4 * MS * NS * kWave * 4 * 2;
     const int epi = 4 * 16 * MS * tile_epi_stride<ACT, NS>();
-    return stages > epi ? stages : epi;
+    const int m = stages > epi ? stages : epi;
+    return m > partial ? m : partial;
 }
 
 // Weight loads of the tile path while LDS-DMA loads are in flight.  The compiler counts
@@ -297,7 +286,10 @@ __device__ __forceinline__ void tie_to_wait(T& v) {
     asm volatile("; weights ready %0" : "+v"(v));
 }
 
-template <int WT, int ACT, bool GROUPED, int MA, int NS, int BM>
+// KG > 1 (fp16 weights only): the block holds KG groups of 4 waves; group g runs the K stages
+// [g * n, (g + 1) * n) of the tile with its own A buffers, and groups 1..KG-1 hand their fp32
+// partial tiles to group 0 through LDS, which adds them in group order and writes the tile.
+template <int WT, int ACT, bool GROUPED, int MA, int NS, int BM, int KG = 1>
 __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__ lds, int e,
                                           int row0, int rows, int cbg) {
     constexpr int KSB = WTraits<WT>::KSB;
@@ -316,7 +308,9 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
     constexpr int NO = SWI ? NS / 2 : NS;            // output column blocks per wave
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = (threadIdx.x / kWave) & 3;      // column wave within the group
+    const int kg = threadIdx.x / 256;                // K group
+    const int tid = threadIdx.x & 255;
     const int K = p.K, N = p.N;
     const int nSB = K / KSB;
     const int ncbw = N / 16;
@@ -350,6 +344,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
     // wave-wide loads per stage.  fp16 weights, whose per-stage weight loads are four times
     // larger, keep the register-staged path below, which measured faster for them.
     constexpr bool DMA_A = WT != MOE_W_FP16;
+    static_assert(KG == 1 || !DMA_A, "K groups are built for the register-staged A path only");
     constexpr int AD = tile_a_stages<WT>();
     constexpr int NAB = DMA_A ? (ATOT > 256 ? ATOT : 256) / kWave : 4;  // wave-wide loads / stage
     constexpr int NA = NAB / 4;
@@ -370,12 +365,14 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
                 (__attribute__((address_space(3))) void*)(lds + buf * LDS_BUF + (wave * NA + i) * 512),
                 16, 0, 0);
     };
-    // register-staged A: chunk q = threadIdx.x + 256 i -> row q / CPR, chunk q % CPR
+    // register-staged A: chunk q = tid + 256 i -> row q / CPR, chunk q % CPR, into the group's
+    // two LDS buffers
+    f16* const lds_a = lds + (KG > 1 ? kg * 2 * LDS_BUF : 0);
     const u32x4* asrc[ACH];
     int adst[ACH];
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
-        const int q = min((int)threadIdx.x + 256 * i, ATOT - 1);
+        const int q = min(tid + 256 * i, ATOT - 1);
         const int r = q / CPR, c = q % CPR;
         asrc[i] = (const u32x4*)(p.a + (size_t)a_source_row(p, row0 + min(r, rows - 1)) * K) + c;
         adst[i] = r * KC + ((c ^ (r & (CPR - 1))) * 8);
@@ -385,13 +382,13 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
     auto load_a = [&](int set, int st) {
 #pragma unroll
         for (int i = 0; i < ACH; ++i)
-            if (ATOT % 256 == 0 || (int)threadIdx.x + 256 * i < ATOT) areg[set][i] = asrc[i][st * CPR];
+            if (ATOT % 256 == 0 || tid + 256 * i < ATOT) areg[set][i] = asrc[i][st * CPR];
     };
     auto store_a = [&](int set, int buf) {
 #pragma unroll
         for (int i = 0; i < ACH; ++i)
-            if (ATOT % 256 == 0 || (int)threadIdx.x + 256 * i < ATOT)
-                *(u32x4*)(lds + buf * LDS_BUF + adst[i]) = areg[set][i];
+            if (ATOT % 256 == 0 || tid + 256 * i < ATOT)
+                *(u32x4*)(lds_a + buf * LDS_BUF + adst[i]) = areg[set][i];
     };
 
     // group scales: one per (column block, super-block) -- a super-block never spans groups
@@ -524,9 +521,12 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));
         __syncthreads();
     } else {
-        load_a(0, 0);
-        load_b(bbuf[0], sbuf[0], 0);
-        load_a(1, min(1, nstage - 1));
+        // this group's stages: [s0, s0 + ns)
+        const int ns = nstage / KG;
+        const int s0 = kg * ns;
+        load_a(0, s0);
+        load_b(bbuf[0], sbuf[0], s0);
+        load_a(1, s0 + min(1, ns - 1));
         store_a(0, 0);
         __syncthreads();
 
@@ -538,23 +538,44 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         auto stage = [&](int st, int set_new, int set_old, const u32x4 (&bc)[NS][SBPS],
                          const uint32_t (&sc)[NS][SCS], u32x4 (&bn)[NS][SBPS],
                          uint32_t (&sn)[NS][SCS]) {
-            const int nxt = min(st + 1, nstage - 1);
-            load_a(set_new, min(st + 2, nstage - 1));
+            const int nxt = s0 + min(st + 1, ns - 1);
+            load_a(set_new, s0 + min(st + 2, ns - 1));
             load_b(bn, sn, nxt);
             // keep the prefetch at the top (see above)
             __builtin_amdgcn_sched_barrier(0);
-            compute_stage(lds + (st & 1) * LDS_BUF, bc, sc);
+            compute_stage(lds_a + (st & 1) * LDS_BUF, bc, sc);
             store_a(set_old, (st + 1) & 1);
             __syncthreads();
         };
-        for (int st = 0; st < nstage; st += 2) {
+        for (int st = 0; st < ns; st += 2) {
             stage(st, 0, 1, bbuf[0], sbuf[0], bbuf[1], sbuf[1]);
-            if (st + 1 < nstage) stage(st + 1, 1, 0, bbuf[1], sbuf[1], bbuf[0], sbuf[0]);
+            if (st + 1 < ns) stage(st + 1, 1, 0, bbuf[1], sbuf[1], bbuf[0], sbuf[0]);
         }
 #pragma unroll
         for (int set = 0; set < 2; ++set)
 #pragma unroll
             for (int i = 0; i < ACH; ++i) consume(areg[set][i]);
+        if constexpr (KG > 1) {
+            // groups 1..KG-1 hand their partial tiles to group 0, which adds them in group
+            // order (the A buffers are free once the last stage's barrier has passed)
+            f32x4* part = (f32x4*)lds;
+            auto slot = [&](int g, int m, int c) { return (((g - 1) * 4 + wave) * MA + m) * NS + c; };
+            if (kg > 0) {
+#pragma unroll
+                for (int m = 0; m < MA; ++m)
+#pragma unroll
+                    for (int c = 0; c < NS; ++c) part[slot(kg, m, c) * kWave + lane] = acc[m][c];
+            }
+            __syncthreads();
+            if (kg == 0) {
+                for (int g = 1; g < KG; ++g)
+#pragma unroll
+                    for (int m = 0; m < MA; ++m)
+#pragma unroll
+                        for (int c = 0; c < NS; ++c) acc[m][c] += part[slot(g, m, c) * kWave + lane];
+            }
+            __syncthreads();
+        }
     }
 
     // the last stage prefetched a repeat of itself, which nothing reads
@@ -564,6 +585,10 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         for (int q = 0; q < SBPS; ++q) { consume(bbuf[0][c][q]); consume(bbuf[1][c][q]); }
 #pragma unroll
         for (int q = 0; q < SCS; ++q) { consume(sbuf[0][c][q]); consume(sbuf[1][c][q]); }
+    }
+
+    if constexpr (KG > 1) {
+        if (kg > 0) return;                      // group 0 writes the tile
     }
 
     // epilogue: lane holds row (lane & 15) of each subtile, 4 consecutive columns per block
@@ -624,13 +649,13 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
     }
 }
 
-template <int WT, int ACT, bool GROUPED, int MS, int NS>
-__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmParams p, int ncbg, int mt_ub,
+template <int WT, int ACT, bool GROUPED, int MS, int NS, int KG>
+__global__ __launch_bounds__(256 * KG, KG == 1 ? 2 : 1) void gemm_tile_kernel(GemmParams p, int ncbg, int mt_ub,
                                                            int grid_real, int a_major) {
     constexpr int BM = 16 * MS;
     // the A ring starts the block's LDS (its DMA writes stay aligned); 16 bytes after the body's
     // LDS carry the tile from the wave that looks it up to the others
-    constexpr int kBodyHalves = tile_lds_halves<WT, ACT, MS, NS>();
+    constexpr int kBodyHalves = tile_lds_halves<WT, ACT, MS, NS, KG>();
     __shared__ __attribute__((aligned(1024))) f16 lds[kBodyHalves + 8];
     int* const tile_info = (int*)(lds + kBodyHalves);
 
@@ -671,16 +696,16 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmParams p, int ncb
     // body specialised for the tile's number of 16-row subtiles (1, 2, 3, 4; 5-6 as 6; MS)
     static_assert(MS >= 3, "the subtile cases below assume tiles of at least 48 rows");
     switch ((rows + 15) / 16) {
-        case 1: tile_body<WT, ACT, GROUPED, 1, NS, BM>(p, lds, e, row0, rows, cbg); break;
-        case 2: tile_body<WT, ACT, GROUPED, 2, NS, BM>(p, lds, e, row0, rows, cbg); break;
-        case 3: tile_body<WT, ACT, GROUPED, 3, NS, BM>(p, lds, e, row0, rows, cbg); break;
+        case 1: tile_body<WT, ACT, GROUPED, 1, NS, BM, KG>(p, lds, e, row0, rows, cbg); break;
+        case 2: tile_body<WT, ACT, GROUPED, 2, NS, BM, KG>(p, lds, e, row0, rows, cbg); break;
+        case 3: tile_body<WT, ACT, GROUPED, 3, NS, BM, KG>(p, lds, e, row0, rows, cbg); break;
         case 4:
-            tile_body<WT, ACT, GROUPED, (MS >= 4 ? 4 : MS), NS, BM>(p, lds, e, row0, rows, cbg);
+            tile_body<WT, ACT, GROUPED, (MS >= 4 ? 4 : MS), NS, BM, KG>(p, lds, e, row0, rows, cbg);
             break;
         case 5: case 6:
-            tile_body<WT, ACT, GROUPED, (MS >= 6 ? 6 : MS), NS, BM>(p, lds, e, row0, rows, cbg);
+            tile_body<WT, ACT, GROUPED, (MS >= 6 ? 6 : MS), NS, BM, KG>(p, lds, e, row0, rows, cbg);
             break;
-        default: tile_body<WT, ACT, GROUPED, MS, NS, BM>(p, lds, e, row0, rows, cbg); break;
+        default: tile_body<WT, ACT, GROUPED, MS, NS, BM, KG>(p, lds, e, row0, rows, cbg); break;
     }
 }
 
@@ -752,8 +777,33 @@ static hipError_t tile_launch(const GemmParams& p, hipStream_t stream) {
     const double a_bytes = 2.0 * p.R * p.K;
     const double w_bytes = (double)active * p.K * p.N * wbits / 8.0;
     const int a_major = a_bytes * (ncbg - 1) > w_bytes ? 1 : 0;
-    gemm_tile_kernel<WT, ACT, GROUPED, MS, NS><<<(unsigned)grid, 256, 0, stream>>>(
-        p, ncbg, mt_ub, (int)real, a_major);
+    // fp16 weights on a grid smaller than the machine: split each tile's K stages over 2 or 4
+    // groups of 4 waves in the block (the register-staged A path takes any split that divides
+    // the stages; integer codes keep one group)
+    // (only splits whose LDS fits a workgroup: the partial tiles grow with the tile)
+    constexpr int kLdsMax = 160 * 1024 - 64;
+    // four groups put four waves of the block on each SIMD: 128 registers, which only the
+    // tiles with at most 8 accumulator fragments per wave fit without spilling
+    constexpr bool kFit4 = MS * NS <= 8 && 2 * tile_lds_halves<WT, ACT, MS, NS, 4>() <= kLdsMax;
+    constexpr bool kFit2 = 2 * tile_lds_halves<WT, ACT, MS, NS, 2>() <= kLdsMax;
+    int kg = 1;
+    if constexpr (WT == MOE_W_FP16) {
+        const int nstage = p.K / tile_kc<WT>();
+        if (kFit4 && real <= 192 && nstage % 4 == 0) kg = 4;
+        else if (kFit2 && real <= 384 && nstage % 2 == 0) kg = 2;
+    }
+    if (kg == 4) {
+        if constexpr (WT == MOE_W_FP16 && kFit4)
+            gemm_tile_kernel<WT, ACT, GROUPED, MS, NS, 4><<<(unsigned)grid, 1024, 0, stream>>>(
+                p, ncbg, mt_ub, (int)real, a_major);
+    } else if (kg == 2) {
+        if constexpr (WT == MOE_W_FP16 && kFit2)
+            gemm_tile_kernel<WT, ACT, GROUPED, MS, NS, 2><<<(unsigned)grid, 512, 0, stream>>>(
+                p, ncbg, mt_ub, (int)real, a_major);
+    } else {
+        gemm_tile_kernel<WT, ACT, GROUPED, MS, NS, 1><<<(unsigned)grid, 256, 0, stream>>>(
+            p, ncbg, mt_ub, (int)real, a_major);
+    }
     return hipGetLastError();
 }
 

@@ -94,8 +94,10 @@ SUBTILE_COUNTS = [1, 16, 17, 32, 33, 40, 47, 48, 49, 64, 0, 65, 97, 110, 128, 15
 
 @pytest.mark.parametrize("path,tile", PATHS[1:])
 @pytest.mark.parametrize("wtype,group,act", [("int4", 128, "swiglu"), ("int8", 0, "relu"),
-                                             ("fp16", 0, "none")])
+                                             ("fp16", 0, "none"), ("fp16", 0, "swiglu")])
 def test_tile_bodies_for_every_subtile_count(wtype, group, act, path, tile):
+    # (the grid here is small, so fp16 weights run with the K stages split over 2 or 4 wave
+    # groups of the block)
     E, K, N = len(SUBTILE_COUNTS), 256, 128
     counts = np.array(SUBTILE_COUNTS)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
