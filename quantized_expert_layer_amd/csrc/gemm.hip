@@ -231,16 +231,19 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmP
 //                 column blocks for all the tile's rows, so each weight byte of the tile is
 //                 loaded and expanded by one wave only.  SwiGLU: NS/2 gate blocks + the
 //                 matching NS/2 up blocks.
-//   K stage     = 128 rows of K (64 for fp16 weights).  The A stage (rows x KC fp16) is
-//                 loaded to registers two stages ahead (two register sets) and written to
-//                 LDS one stage ahead (double buffered); the weights are loaded one stage
-//                 ahead.  The activation rows are usually not in L2 (a previous kernel's
-//                 output, or x read through perm), so their latency is the longer one.
-//                 LDS rows are not padded: 16-byte chunk c of row r sits at chunk position
-//                 c ^ (r & 15), so the 16 lanes of an A-fragment read (16 rows, one chunk)
-//                 and of a row write hit distinct 4-bank groups.
+//   K stage     = 128 rows of K (64 for fp16 weights).  Integer codes: the A stage (rows x KC
+//                 fp16) goes from memory straight into a ring of three LDS buffers, two
+//                 stages ahead; fp16 weights: it is loaded to registers two stages ahead and
+//                 written to LDS one stage ahead (double buffered).  The weights are loaded
+//                 one stage ahead into two register buffers that alternate.  The activation
+//                 rows are usually not in L2 (a previous kernel's output, or x read through
+//                 perm), so their latency is the longer one.  LDS rows are not padded:
+//                 16-byte chunk c of row r sits at chunk position c ^ (r & 15), so the 16
+//                 lanes of an A-fragment read (16 rows, one chunk) hit distinct 4-bank groups.
 //   partial     = a tile with fewer valid rows runs the body specialised for its number of
 //                 16-row subtiles (1..MS), so it neither loads nor multiplies absent rows.
+//   K groups    = fp16 weights on a small grid: 2 or 4 groups of 4 waves split the K stages
+//                 and add their fp32 partial tiles through LDS (see tile_body).
 //   occupancy   = 2+ blocks per CU, so each SIMD interleaves at least two waves.
 // ------------------------------------------------------------------------------------
 // K per stage: 128 rows for int4/int8 codes (one 128-group), 64 for fp16 weights (whose
