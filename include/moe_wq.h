@@ -62,7 +62,7 @@ enum moe_wtype { MOE_W_INT4 = 0, MOE_W_INT8 = 1, MOE_W_FP16 = 2 };
 enum moe_act   { MOE_ACT_NONE = 0, MOE_ACT_RELU = 1, MOE_ACT_SWIGLU = 2 };
 enum moe_path  { MOE_PATH_AUTO = 0,           /* chosen from R, E, K, N                  */
                  MOE_PATH_STREAM = 1,         /* weight-streaming path, 16-row tiles     */
-                 MOE_PATH_TILE = 2 };         /* LDS-staged MFMA tile path, 64-row tiles  */
+                 MOE_PATH_TILE = 2 };         /* LDS-staged MFMA tile path, 48/64-row tiles */
 
 /* Optional per-call GEMM settings.  Pass NULL for the defaults (all fields 0). */
 enum moe_tile  { MOE_TILE_AUTO = 0,           /* chosen from R, E, K, N                  */
@@ -75,8 +75,12 @@ enum moe_tile  { MOE_TILE_AUTO = 0,           /* chosen from R, E, K, N         
 typedef struct moe_gemm_opts {
     int32_t path;      /* enum moe_path                                              */
     int32_t split_k;   /* 0 = automatic; 1..MOE_MAX_SPLIT_K forces the number of  */
-                       /* waves that split K per stream-path block                 */
-    int32_t tile;      /* enum moe_tile: block tile of the tile path                 */
+                       /* waves that split K per stream-path block (the tile path  */
+                       /* ignores it)                                              */
+    int32_t tile;      /* enum moe_tile: block tile of the tile path (automatic:   */
+                       /* 48-row tiles for per-channel scales and for experts with */
+                       /* under ~96 rows, 64x256 for group scales beyond that,     */
+                       /* 128-column tiles for 8-bit codes)                        */
     int32_t reserved[5];
 } moe_gemm_opts;
 
