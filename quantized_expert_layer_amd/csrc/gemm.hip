@@ -653,7 +653,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
 }
 
 template <int WT, int ACT, bool GROUPED, int MS, int NS, int KG>
-__global__ __launch_bounds__(256 * KG, KG == 1 ? 2 : 1) void gemm_tile_kernel(GemmParams p, int ncbg, int mt_ub,
+__global__ __launch_bounds__(256 * KG, (KG == 1 && MS < 8) ? 2 : 1) void gemm_tile_kernel(GemmParams p, int ncbg, int mt_ub,
                                                            int grid_real, int a_major) {
     constexpr int BM = 16 * MS;
     // the A ring starts the block's LDS (its DMA writes stay aligned); 16 bytes after the body's
