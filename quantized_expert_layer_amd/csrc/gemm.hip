@@ -487,15 +487,16 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         for (int s0 = 1; s0 < AD - 1; ++s0) dma_a(min(s0, nstage - 1), s0);
 
         // Waits.  Per stage a wave issues, in this order, the weight / scale loads of stage
-        // st + 1 and NA A loads (stage st + AD - 1); vector memory loads complete in order, so
-        // once at most (AD - 2) * NA loads are outstanding, the weights of stage st (issued
-        // before the A loads of stage st + AD - 2) and this wave's A loads of stage st (issued
-        // before those) are done.  The barrier after the wait makes every wave's A loads of
-        // stage st visible and frees the buffer stage st - 1 used, which the stage's new A
-        // loads overwrite.  (The barrier is issued bare: the compiler's fence before a block
-        // barrier would wait for all A loads in flight.)  The count holds for the first stages
-        // too, whose prologue order is A stage 0, the weights of stage 0, A stages 1 .. AD - 2.
-        constexpr int NWAIT = (AD - 2) * NA;
+        // st + 1 and NA A loads (stage st + AD - 1); vector memory loads complete in order.  At
+        // the top of stage st only the NA A loads issued after the weights of stage st (those
+        // of stage st + AD - 2) may still be outstanding: once at most NA are, the weights of
+        // stage st and this wave's A loads of stage st (issued earlier still) are done.  The
+        // barrier after the wait makes every wave's A loads of stage st visible and frees the
+        // buffer stage st - 1 used, which the stage's new A loads overwrite.  (The barrier is
+        // issued bare: the compiler's fence before a block barrier would wait for all A loads
+        // in flight.)  The count holds for the first stages too, whose prologue order is A
+        // stage 0, the weights of stage 0, A stages 1 .. AD - 2.
+        constexpr int NWAIT = NA;
         static_assert(NWAIT < 64, "vmcnt field");
         constexpr int WAITCNT = (NWAIT & 15) | ((NWAIT >> 4) << 14) | (7 << 4) | (15 << 8);
 
