@@ -128,3 +128,33 @@ def test_plan_outlives_its_layer(name, T):
     got = host(plan.out)
     del junk
     np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("name,T", [("mt_encoder", 3840), ("qwen15_moe", 544)])
+def test_layer_replays_from_a_graph(name, T):
+    """The step the bench times: the layer plan captured once in a HIP graph and replayed with
+    eager work in between.  Every replay gives the eager output bit for bit, and sampled tokens
+    of the replayed output match the fp64 oracle."""
+    import torch
+
+    inp, layer = _layer(name, T, None, 0)
+    x, L = dev(inp.x), dev(inp.logits)
+    ws = layer.workspace(T)
+    case(f"layer graph {name} T={T}")
+    want = host(layer.forward(x, L, ws=ws)).copy()
+    s = torch.cuda.Stream()
+    plan = layer.plan(ws, x, L, stream=s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        plan.run()
+    for i in range(3):
+        ws.bufs["out"].fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        got = host(ws.bufs["out"])
+        assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), i
+        # eager work on other inputs between the replays
+        layer.forward(dev(inp.x[::-1].copy()), dev(inp.logits[::-1].copy()), ws=ws)
+        torch.cuda.synchronize()
+    toks = _tokens(T, 64)
+    assert_layer_close(got[toks], oracle.moe_layer_tokens(inp, toks), f"graph {name} T={T}")
