@@ -173,15 +173,19 @@ def test_one_hot_rows_reproduce_dequantized_weight_rows(wtype, group, path, tile
     assert np.array_equal(out.view(np.uint16), ref.view(np.uint16))
 
 
+@pytest.mark.parametrize("K", [256, 128, 384])
 @pytest.mark.parametrize("path,tile", PATHS)
-def test_fp16_weights_and_zero_row_experts(path, tile):
-    E, K, N, T = 6, 256, 128, 40
+def test_fp16_weights_and_zero_row_experts(path, tile, K):
+    # fp16 stages are 64 rows of K: 256 gives 4 stages, which the small grid splits over 4 wave
+    # groups (2 for the larger tiles); 128 (2 stages) and 384 (6) do not divide by 4 and fall
+    # back to 2 groups
+    E, N, T = 6, 128, 40
     rng = np.random.default_rng(8)
     w = (rng.standard_normal((E, K, N)) * 0.05).astype(np.float16)
     off = np.array([0, 0, 17, 17, 17, 40, 40], np.int32)      # experts 0, 2, 3, 5 have no rows
     a = rng.standard_normal((T, K)).astype(np.float16)
     for act in ("none", "swiglu"):
-        case(f"fp16 weights act={act} path={path}")
+        case(f"fp16 weights act={act} path={path} tile={tile} K={K}")
         out = q.moe_grouped_gemm_wq(dev(a), dev(off), E, K, N, dev(q.moe_pack_wq(w, "fp16")), None,
                                     "fp16", 0, act, path=path, tile=tile)
         ref = oracle.grouped_gemm(a, off, w.astype(np.float64), act)
