@@ -139,7 +139,7 @@ int32_t moe_route_topk_active(const float* logits, const uint8_t* active, int32_
  *                                 through perm itself)
  *   w_perm          fp32  [T*k]   out (optional): w_perm[p] = topk_w.flat[perm[p]]
  *   ws, ws_bytes    workspace of at least moe_permute_workspace_size(T, k, E) bytes: 0 up
- *                   to 1024 slots (NULL allowed), else 4 * E * ceil(T*k / 1024) (per-block
+ *                   to 8192 slots (NULL allowed), else 4 * E * ceil(T*k / 1024) (per-block
  *                   expert counts of the two-launch sort); MOE_ERR_WORKSPACE if short
  *   Requires 1 <= E <= 256, 1 <= k <= 8, d % 8 == 0.  A slot whose id is outside [0, E)
  *   (-1 from moe_route_topk_active for a finished token) is not routed: it gets no sorted

@@ -4,9 +4,12 @@
 //
 // Up to 1024 slots the sort is sort_block (one workgroup of 16 waves, ballot-matched counting
 // sort).  Beyond that one workgroup is bound by its CU's VALU (the per-bit ballot matching of
-// every 64-slot chunk), so the slots are split into 1024-slot blocks over two launches: the
-// first counts each block's keys per expert into a small workspace; the second has each block
-// turn all the counts into its own per-expert bases and place its slots.  Same result, stable.
+// every 64-slot chunk), so the slots are split into 1024-slot blocks, each of which turns the
+// per-expert counts of all slots into its own per-expert bases and places its slots.  Up to
+// kSortCountBlocks blocks every block counts all R keys itself (one launch; the keys are at
+// most 32 KiB and sit in L2; counting costs about 0.3 us per 1000 keys, less than a second
+// launch up to about 12000); beyond that a first launch counts each block's keys into a small
+// workspace and the second reads those counts.  Same result either way, stable.
 #include "common.hpp"
 #include "launch.hpp"
 #include "sort.hpp"
@@ -15,6 +18,7 @@ namespace moe {
 
 constexpr int kSortLdsKeys = 16384;     // keys staged in LDS when R fits (64 KB)
 constexpr int kSortBlockSlots = kSortWaves * kWave;   // slots per block of the multi-block sort
+constexpr int kSortCountBlocks = 8;   // up to this many blocks each block counts all keys itself
 
 // KEYS_IN_LDS: all R keys are first copied to LDS with one coalesced pass, so the two walks
 // of the sort read LDS instead of issuing one dependent global load per 64-key chunk.
@@ -71,17 +75,21 @@ __global__ __launch_bounds__(1024) void sort_hist_kernel(const int32_t* __restri
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// Multi-block sort, launch 2: block b reads every block's counts, takes the global offsets of
-// the experts (exclusive scan of the totals) plus the counts of blocks before it as its bases,
-// ranks its own slots as sort_block does (wave order, then rank among equal keys of a chunk)
-// and writes perm / inv_perm / w_perm.  Block 0 also writes offsets and fills the positions
-// left empty by slots routed nowhere.
+// Multi-block sort, scatter: block b takes the per-expert counts of all slots (COUNT: by
+// counting every key itself; else from the counts launch 1 left in hist), the global offsets
+// of the experts (exclusive scan of the totals) plus the counts of the slots before its own as
+// its bases, ranks its own slots as sort_block does (wave order, then rank among equal keys of
+// a chunk) and writes perm / inv_perm / w_perm.  Block 0 also writes offsets and fills the
+// positions left empty by slots routed nowhere.
+template <bool COUNT>
 __global__ __launch_bounds__(1024) void sort_scatter_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ wts, int R, int E,
     const int32_t* __restrict__ hist, int nblk, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv_perm, int32_t* __restrict__ offsets, float* __restrict__ w_perm) {
     __shared__ int cnt[kSortWaves][MOE_MAX_EXPERTS];
     __shared__ int base[MOE_MAX_EXPERTS];
+    __shared__ int all_cnt[COUNT ? MOE_MAX_EXPERTS : 1];    // keys of all slots, per expert
+    __shared__ int pre_cnt[COUNT ? MOE_MAX_EXPERTS : 1];    // keys of the slots before block b
     __shared__ int wave_sum[4];
     __shared__ int n_valid;
     const int lane = threadIdx.x & (kWave - 1);
@@ -89,17 +97,55 @@ __global__ __launch_bounds__(1024) void sort_scatter_kernel(
     const int f = blockIdx.x * kSortBlockSlots + threadIdx.x;
     const int kf = f < R ? ids[f] : -1;
     const float wf = (w_perm && f < R) ? wts[f] : 0.0f;
+    const int nbits = (E <= 1) ? 0 : 32 - __clz(E - 1);
     for (int i = threadIdx.x; i < kSortWaves * MOE_MAX_EXPERTS; i += blockDim.x)
         (&cnt[0][0])[i] = 0;
+
+    if constexpr (COUNT) {
+        // every block counts all R keys: wave w takes 64-slot chunks w, w + 16, ...; four
+        // chunks' loads are issued before the first is matched.  The chunks before this
+        // block's first (16 b) are its predecessors' slots.
+        for (int e = threadIdx.x; e < MOE_MAX_EXPERTS; e += blockDim.x) {
+            all_cnt[e] = 0;
+            pre_cnt[e] = 0;
+        }
+        __syncthreads();
+        const int nchunks = (R + kWave - 1) / kWave;
+        const int first_own = blockIdx.x * kSortWaves;
+        constexpr int U = 4;
+        for (int c0 = wave; c0 < nchunks; c0 += U * kSortWaves) {
+            int key[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int g = (c0 + u * kSortWaves) * kWave + lane;
+                key[u] = g < R ? ids[g] : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool ok = (unsigned)key[u] < (unsigned)E;
+                const Match mu = wave_match(key[u], ok, nbits, lane);
+                if (ok && mu.rank == mu.total - 1) {
+                    atomicAdd(&all_cnt[key[u]], mu.total);
+                    if (c0 + u * kSortWaves < first_own) atomicAdd(&pre_cnt[key[u]], mu.total);
+                }
+            }
+        }
+        __syncthreads();
+    }
 
     int tot = 0, pre = 0, incl = 0;
     if (threadIdx.x < 256) {                   // waves 0..3, one expert per thread
         const int e = threadIdx.x;
         if (e < E) {
-            for (int b = 0; b < nblk; ++b) {
-                const int h = hist[(size_t)b * E + e];
-                tot += h;
-                if (b < (int)blockIdx.x) pre += h;
+            if constexpr (COUNT) {
+                tot = all_cnt[e];
+                pre = pre_cnt[e];
+            } else {
+                for (int b = 0; b < nblk; ++b) {
+                    const int h = hist[(size_t)b * E + e];
+                    tot += h;
+                    if (b < (int)blockIdx.x) pre += h;
+                }
             }
         }
         incl = wave_incl_scan(tot);
@@ -121,7 +167,6 @@ __global__ __launch_bounds__(1024) void sort_scatter_kernel(
         }
     }
     // pass 1: per-wave counts of this block's slots (one chunk per wave)
-    const int nbits = (E <= 1) ? 0 : 32 - __clz(E - 1);
     const bool valid = (unsigned)kf < (unsigned)E;
     const Match m = wave_match(kf, valid, nbits, lane);
     if (valid && m.rank == m.total - 1) cnt[wave][kf] = m.total;
@@ -155,8 +200,8 @@ __global__ __launch_bounds__(1024) void sort_scatter_kernel(
 }
 
 size_t sort_workspace_bytes(int R, int E) {
-    if (R <= kSortBlockSlots) return 0;
     const size_t nblk = ((size_t)R + kSortBlockSlots - 1) / kSortBlockSlots;
+    if (nblk <= (size_t)kSortCountBlocks) return 0;
     return nblk * (size_t)E * sizeof(int32_t);
 }
 
@@ -165,12 +210,17 @@ hipError_t launch_sort(const int32_t* ids, const float* wts, int R, int E, int32
                        hipStream_t stream) {
     if (R > kSortBlockSlots) {
         const int nblk = (R + kSortBlockSlots - 1) / kSortBlockSlots;
+        if (nblk <= kSortCountBlocks) {
+            sort_scatter_kernel<true><<<nblk, kSortBlockSlots, 0, stream>>>(
+                ids, wts, R, E, nullptr, nblk, perm, inv_perm, offsets, w_perm);
+            return hipGetLastError();
+        }
         int32_t* hist = (int32_t*)ws;
         sort_hist_kernel<<<nblk, kSortBlockSlots, 0, stream>>>(ids, R, E, hist);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
-        sort_scatter_kernel<<<nblk, kSortBlockSlots, 0, stream>>>(ids, wts, R, E, hist, nblk, perm,
-                                                                  inv_perm, offsets, w_perm);
+        sort_scatter_kernel<false><<<nblk, kSortBlockSlots, 0, stream>>>(
+            ids, wts, R, E, hist, nblk, perm, inv_perm, offsets, w_perm);
         return hipGetLastError();
     }
     if (R <= kSortLdsKeys)

@@ -158,8 +158,9 @@ def test_route_topk_validation():
 def test_permute_workspace_size():
     L = q.lib()
     assert L.moe_permute_workspace_size(512, 2, 8) == 0               # one workgroup sorts
-    assert L.moe_permute_workspace_size(513, 2, 8) == 2 * 8 * 4        # 1026 slots: 2 blocks
-    assert L.moe_permute_workspace_size(8192, 2, 16) == 16 * 16 * 4
+    assert L.moe_permute_workspace_size(513, 2, 8) == 0                # 2 blocks, one launch
+    assert L.moe_permute_workspace_size(4096, 2, 16) == 0              # 8 blocks, one launch
+    assert L.moe_permute_workspace_size(4097, 2, 16) == 9 * 16 * 4     # 9 blocks: two launches
     assert L.moe_permute_workspace_size(0, 2, 8) == 0
 
 
@@ -177,9 +178,9 @@ def test_permute_validation():
     assert L.moe_permute(*args(T=0, ids=None, x=None)) == q.MOE_OK
     assert L.moe_permute(*args(x=None)) == q.MOE_ERR_INVALID          # x_perm needs x
     assert L.moe_permute(*args(x=None, xp=None, T=0)) == q.MOE_OK      # x may go with x_perm
-    # more than 1024 slots need the workspace of the two-launch sort
-    assert L.moe_permute(*args(T=600, ws=None, wsb=0)) == q.MOE_ERR_WORKSPACE
-    assert L.moe_permute(*args(T=600, ws=FAKE, wsb=2 * 8 * 4 - 1)) == q.MOE_ERR_WORKSPACE
+    # more than 8192 slots need the workspace of the two-launch sort (k = 2: 9 blocks)
+    assert L.moe_permute(*args(T=4097, ws=None, wsb=0)) == q.MOE_ERR_WORKSPACE
+    assert L.moe_permute(*args(T=4097, ws=FAKE, wsb=9 * 8 * 4 - 1)) == q.MOE_ERR_WORKSPACE
 
 
 def _gemm_args(**kw):

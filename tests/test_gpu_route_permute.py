@@ -67,10 +67,13 @@ def test_permute_matches_oracle(T, k, E, d, skew):
     assert np.array_equal(host(wp), w.ravel()[r_perm])
 
 
-@pytest.mark.parametrize("T,k,E", [(600, 2, 8), (3000, 2, 40), (9000, 2, 256)])
+@pytest.mark.parametrize("T,k,E", [(600, 2, 8), (3000, 2, 40), (4096, 2, 16), (4097, 2, 16),
+                                   (9000, 2, 256), (5000, 7, 8)])
 def test_permute_multi_block_with_dropped_slots(T, k, E):
     """Above 1024 slots the sort runs over several blocks: ids -1 (finished tokens) and out of
-    range, a skewed key mix, and block boundaries inside runs of equal keys."""
+    range, a skewed key mix, and block boundaries inside runs of equal keys.  Up to 8 blocks
+    (8192 slots) each block counts all keys itself; 8194 slots and more take the two-launch
+    form."""
     rng = np.random.default_rng(T)
     ids = synth.gen.random_ids(T, k, E, seed=T, skew=True)
     drop = rng.random((T, k)) < 0.1
