@@ -82,6 +82,13 @@ def test_permute_multi_block_with_dropped_slots(T, k, E):
     w = rng.random((T, k), dtype=np.float32)
     x = rng.standard_normal((T, 8)).astype(np.float16)
     case(f"permute multi-block T={T} k={k} E={E}")
+    _check_sort_with_drops(ids, w, x, E)
+
+
+def _check_sort_with_drops(ids, w, x, E):
+    """moe_permute against a stable argsort in which slots outside [0, E) sort last and are
+    dropped."""
+    T, k = ids.shape
     perm, inv, off, xp, wp = q.moe_permute(dev(ids), dev(w), dev(x), E)
     valid = (ids >= 0) & (ids < E)
     keys = np.where(valid, ids, E).ravel()               # dropped slots sort after every expert
@@ -98,6 +105,27 @@ def test_permute_multi_block_with_dropped_slots(T, k, E):
     r_wp = np.zeros(T * k, np.float32)
     r_wp[:n_valid] = w.ravel()[order[:n_valid]]
     assert np.array_equal(host(wp), r_wp)
+    r_xp = np.zeros((T * k, x.shape[1]), np.float16)     # rows routed nowhere are zero-filled
+    r_xp[:n_valid] = x[order[:n_valid] // k]
+    assert np.array_equal(host(xp).view(np.uint16), r_xp.view(np.uint16))
+
+
+@pytest.mark.parametrize("T,k,E,fill", [(3000, 1, 1, None), (1000, 8, 256, None),
+                                        (1024, 8, 256, None), (2000, 2, 16, -1),
+                                        (3000, 2, 40, 40)])
+def test_permute_multi_block_edge_cases(T, k, E, fill):
+    """The multi-block sort at its corners: one expert (no key bits to match), 256 experts at
+    and just below the 8192-slot edge of the one-launch form, and every slot dropped (-1, or
+    ids equal to E)."""
+    case(f"permute multi-block edge T={T} k={k} E={E} fill={fill}")
+    if fill is None:
+        ids = synth.gen.random_ids(T, k, E, seed=T + 7, skew=True)
+    else:
+        ids = np.full((T, k), fill, np.int32)
+    rng = np.random.default_rng(T + k)
+    w = rng.random((T, k), dtype=np.float32)
+    x = rng.standard_normal((T, 8)).astype(np.float16)
+    _check_sort_with_drops(ids, w, x, E)
 
 
 def test_permute_drops_ids_out_of_range():
