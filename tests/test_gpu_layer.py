@@ -130,8 +130,9 @@ def test_plan_outlives_its_layer(name, T):
     np.testing.assert_array_equal(got, want)
 
 
-@pytest.mark.parametrize("name,T", [("mt_encoder", 3840), ("qwen15_moe", 544)])
-def test_layer_replays_from_a_graph(name, T):
+@pytest.mark.parametrize("name,T,n_check", [("mt_encoder", 3840, 64), ("qwen15_moe", 544, 64),
+                                            ("dsv2_lite", 288, 64), ("phi35_moe", 8192, 16)])
+def test_layer_replays_from_a_graph(name, T, n_check):
     """The step the bench times: the layer plan captured once in a HIP graph and replayed with
     eager work in between.  Every replay gives the eager output bit for bit, and sampled tokens
     of the replayed output match the fp64 oracle."""
@@ -156,5 +157,5 @@ def test_layer_replays_from_a_graph(name, T):
         # eager work on other inputs between the replays
         layer.forward(dev(inp.x[::-1].copy()), dev(inp.logits[::-1].copy()), ws=ws)
         torch.cuda.synchronize()
-    toks = _tokens(T, 64)
+    toks = _tokens(T, n_check)
     assert_layer_close(got[toks], oracle.moe_layer_tokens(inp, toks), f"graph {name} T={T}")
