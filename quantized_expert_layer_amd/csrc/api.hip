@@ -207,6 +207,7 @@ static int32_t grouped_gemm(const uint16_t* a, int32_t a_nrows, const int32_t* a
     p.act = act;
     p.split = pl.split;
     p.tile = opts ? opts->tile : MOE_TILE_AUTO;
+    p.tiles16 = nullptr;
     hipStream_t s = (hipStream_t)stream;
     return hip_status(pl.path == MOE_PATH_TILE ? moe::launch_gemm_tile(p, s)
                                                : moe::launch_gemm_stream(p, s));
@@ -369,7 +370,7 @@ int32_t moe_dequant(const void* w_packed, const uint16_t* scales, int32_t wtype,
     if (group_size != 0 && group_size != 128) return MOE_ERR_UNSUPPORTED;
     if (K % 128 != 0 || N % 16 != 0) return MOE_ERR_UNSUPPORTED;
     if (!w_packed || !scales || !w_out) return MOE_ERR_INVALID;
-    if (!aligned(w_packed, 16) || !aligned(scales, 2) || !aligned(w_out, 2)) return MOE_ERR_INVALID;
+    if (!aligned(w_packed, 16) || !aligned(scales, 16) || !aligned(w_out, 16)) return MOE_ERR_INVALID;
     if (int32_t st = check_device()) return st;
     return hip_status(moe::launch_dequant(w_packed, scales, wtype, group_size, E, K, N, w_out,
                                           (hipStream_t)stream));

@@ -129,6 +129,37 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
     return (float)__builtin_bit_cast(f16, b);
 }
 
+// Four fp16 values (8-byte aligned) to fp32, and four fp32 values to fp16 (round to nearest
+// even) in one 8-byte store.
+__device__ __forceinline__ f32x4 load4_f16(const uint16_t* src) {
+    const uint2 v = *(const uint2*)src;
+    const f16x2 lo = __builtin_bit_cast(f16x2, v.x), hi = __builtin_bit_cast(f16x2, v.y);
+    return f32x4{(float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]};
+}
+__device__ __forceinline__ void store4_f16_bits(uint16_t* dst, f32x4 v) {
+    const f16x2 lo = {(f16)v[0], (f16)v[1]}, hi = {(f16)v[2], (f16)v[3]};
+    uint2 o;
+    o.x = __builtin_bit_cast(uint32_t, lo);
+    o.y = __builtin_bit_cast(uint32_t, hi);
+    *(uint2*)dst = o;
+}
+
+// Block barrier that orders LDS accesses only.  __syncthreads() also waits for every global
+// store the wave has in flight (vmcnt 0), which costs a memory round trip where the other waves
+// only need LDS data.  Callers use it where no wave reads global memory written by another
+// wave of the block before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// The same ordering for the LDS accesses of one wave (no barrier: a wave's LDS accesses take
+// effect in program order; this keeps the compiler from moving them across the point).
+__device__ __forceinline__ void lds_wave_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Marks a register value as read here, so its load has completed and its registers are not
 // handed to other values before this point.  Used where a prefetch ring ends: the ring's last
 // (repeated) loads are never consumed otherwise, and a register that still awaits one must not
@@ -213,6 +244,24 @@ __device__ __forceinline__ bool lookup_m_tile(const int32_t* __restrict__ offset
         }
     }
     return false;
+}
+
+// ------------------------------------------------------------------------------------
+// Tile table of a decode step: the gating + sort launch lists every 16-row m-tile of the
+// sorted rows (expert e, first row r0, rows n in 1..16), so a later launch finds its tile with
+// one load instead of a scan over the offsets.  Entry 0 holds the number of tiles; tile i is
+// entry 1 + i, packed as e | r0 << 9 | (n - 1) << 19 (e < 512, r0 < 1024).
+// ------------------------------------------------------------------------------------
+constexpr int kDecodeMaxTiles = MOE_DECODE_MAX_ROWS / 16 + MOE_MAX_EXPERTS;
+static_assert(MOE_MAX_EXPERTS <= 512 && MOE_DECODE_MAX_ROWS <= 1024, "tile packing");
+
+__device__ __forceinline__ int tile16_pack(int e, int r0, int n) {
+    return e | (r0 << 9) | ((n - 1) << 19);
+}
+__device__ __forceinline__ void tile16_unpack(int v, int& e, int& r0, int& n) {
+    e = v & 511;
+    r0 = (v >> 9) & 1023;
+    n = ((v >> 19) & 15) + 1;
 }
 
 template <int BM>

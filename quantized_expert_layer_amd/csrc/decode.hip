@@ -1,13 +1,18 @@
-// The routed layer for the few tokens of a decode or verify step, in three launches:
+// The routed layer for the few tokens of a decode or verify step:
 //
-//   1. decode_route_sort_kernel  top-k gating of every token and the stable sort of the T*k
-//                                slots by expert, in one workgroup (the keys stay in LDS).
+//   1. decode_route_sort_kernel  top-k gating of every token, the stable sort of the T*k
+//                                slots by expert, and the table of 16-row m-tiles of the
+//                                sorted rows, in one workgroup (the keys stay in LDS).
 //   2. gemm_stream_kernel        grouped GEMM 1 (gate/up or W1) over all active experts, rows
-//                                read through perm (the stream path of the grouped GEMM).
-//   3. gemm_combine_kernel       grouped GEMM 2 (down or W2) whose blocks own 16 output
-//                                columns of the layer for every token, so the gate weight,
-//                                the unpermute and the sum over a token's k experts happen in
-//                                its epilogue, in fp32, and no per-slot row goes to memory.
+//                                read through perm, each block's tile read from the table.
+//   3. gemm_combine_kernel       grouped GEMM 2 (down or W2): every 16 output columns of the
+//                                layer are shared by `nsplit` blocks, each of which streams
+//                                its share of the active experts' weight units for all tokens,
+//                                so the gate weight, the unpermute and the sum over a token's k
+//                                experts happen in its epilogue, in fp32, and no per-slot row
+//                                goes to memory.
+//   4. combine_reduce_kernel     (nsplit > 1) adds the blocks' fp32 token sums in split order
+//                                and the addend, and writes the fp16 output.
 //
 // "Specter" summary, Method steps, step 5 and Technical novelty: the draft model's expert
 // sub-computations run in one fused launch, and the verify step groups tokens by expert into
@@ -22,8 +27,10 @@
 namespace moe {
 
 // ------------------------------------------------------------------------------------
-// 1. Gating + sort.  One block of kSortWaves waves; wave w routes tokens w, w + 16, ...;
-//    then wave 0 sorts the slots (few enough that one wave beats the block-wide sort).
+// 1. Gating + sort + tile table.  One block of kSortWaves waves; the 16-lane rows route one
+//    token each (wave w tokens 4w .. 4w + 3); then wave 0 sorts the slots (few enough that one
+//    wave beats the block-wide sort) and lists the 16-row m-tiles of every expert's sorted rows
+//    (expert order).
 // ------------------------------------------------------------------------------------
 template <int PER_LANE>
 __global__ __launch_bounds__(kSortWaves * kWave) void decode_route_sort_kernel(
@@ -32,177 +39,229 @@ __global__ __launch_bounds__(kSortWaves * kWave) void decode_route_sort_kernel(
     __shared__ int keys[MOE_DECODE_MAX_ROWS];
     __shared__ float kw[MOE_DECODE_MAX_ROWS];
     __shared__ int cnt[MOE_MAX_EXPERTS];
+    __shared__ int offs[MOE_MAX_EXPERTS + 1];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    for (int t = wave; t < T; t += kSortWaves) {
-        int e = -1;              // a finished token (active[t] == 0) takes no expert
-        float w = 0.0f;
-        if (!active || active[t])
-            topk_token<PER_LANE>(logits + (size_t)t * E, E, k, gate_all, lane, e, w);
-        if (lane < k) {
-            ids[t * k + lane] = e;
-            wts[t * k + lane] = w;
-            keys[t * k + lane] = e;
-            kw[t * k + lane] = w;
+    // one token per 16-lane row: wave w routes tokens 4w .. 4w + 3 (T <= 64 = 16 waves x 4)
+    if (4 * wave < T) {
+        const int t = 4 * wave + (lane >> 4);
+        const int j = lane & 15;
+        // a finished token (active[t] == 0) takes no expert: e = -1, w = 0
+        const bool live = t < T && (!active || active[t]);
+        int e;
+        float w;
+        topk_row<PER_LANE>(live ? logits + (size_t)t * E : nullptr, E, k, gate_all, lane, e, w);
+        if (t < T && j < k) {
+            ids[t * k + j] = e;
+            wts[t * k + j] = w;
+            keys[t * k + j] = e;
+            kw[t * k + j] = w;
         }
     }
-    __syncthreads();
+    // the other waves hand over LDS keys only (their global stores need not land first)
+    lds_barrier();
     if (wave != 0) return;
-    sort_wave(T * k, E, [&](int f) { return keys[f]; }, [&](int f) { return kw[f]; }, cnt,
+    sort_wave(T * k, E, [&](int f) { return keys[f]; }, [&](int f) { return kw[f]; }, cnt, offs,
               ws.perm, ws.inv_perm, ws.offsets, ws.w_perm);
+    lds_wave_fence();
+    // tile table: expert e's rows offs[e] .. offs[e+1]-1 in tiles of 16, experts in order.
+    // At most sum_e ceil(c_e / 16) <= T*k / 16 + E <= kDecodeMaxTiles entries.
+    int base = 0;
+    for (int c0 = 0; c0 < E; c0 += kWave) {
+        const int e = c0 + lane;
+        int lo = 0, n = 0;
+        if (e < E) {
+            lo = offs[e];
+            n = offs[e + 1] - lo;
+        }
+        const int nt = (n + 15) >> 4;
+        const int incl = wave_incl_scan(nt);
+        const int b0 = base + incl - nt;
+        for (int i = 0; i < nt; ++i)
+            ws.tiles[1 + b0 + i] = tile16_pack(e, lo + 16 * i, min(16, n - 16 * i));
+        base += __builtin_amdgcn_readlane(incl, kWave - 1);
+    }
+    if (lane == 0) ws.tiles[0] = base;
 }
+
+// Second GEMM: waves per block, and 16-column blocks per wave (one activation fragment serves
+// the weight units of all of them: a CU's vector-memory pipeline moves 64 bytes per clock, and
+// a 16-row activation fragment is four times the bytes of a 1 KiB weight unit).
+constexpr int kCombineWaves = 8;
+constexpr int kCombineNcb = 2;
 
 // ------------------------------------------------------------------------------------
 // 3. Grouped GEMM 2 + gate weight + unpermute + combine.
 //
-//   grid   = N / 16 column blocks; block = S waves.
-//   work   = the units (m-tile, super-block) of every active expert for the block's 16
-//            columns: m-tiles are the 16-row tiles of each expert's sorted rows, super-blocks
-//            the 1 KiB weight units along K.  Wave w takes the w-th of S equal ranges of the
-//            unit sequence, so every weight byte of the active experts is read by one wave.
+//   grid   = (N / (16 NCB) column groups) x nsplit; block = S waves.
+//   work   = the units (m-tile, super-block) of every active expert for the block's 16 NCB
+//            columns: m-tiles are the 16-row tiles of each expert's sorted rows (from the tile
+//            table), super-blocks the 1 KiB weight units along K of each 16-column block.  The
+//            S * nsplit waves that share a column group take equal consecutive ranges of that
+//            unit sequence (split s the s-th group of S ranges), so every weight byte of the
+//            active experts is read by one wave, and a wave loads a unit's activation fragment
+//            once for its NCB column blocks.
 //   math   = as the stream path: MFMA 16x16x32 with the activation (H rows) first, so lane l
 //            holds column (l & 15) of rows 4(l >> 4) .. +3; group scales multiply the fp32
 //            sum of a super-block, a per-channel scale the sum of an m-tile.
 //   combine= when a wave finishes an m-tile (or its range), each valid row p adds
 //            w_perm[p] * y[p] into the wave's fp32 token sums in LDS at token perm[p] / k.
 //            An expert holds at most one slot of a token, so the lanes of one such update
-//            write distinct words.  The block then adds its S waves in the order 0..S-1 and
-//            the addend, and writes the fp16 output.  Every sum has a fixed order, so results
-//            are deterministic.  (Splitting a column block's units over several blocks would
-//            need a device-wide release before the last block adds the parts; on this chip
-//            that writes back the whole L2 of the XCD per block and cost more than it gained.)
+//            write distinct words.  The block then adds its S waves in the order 0..S-1: with
+//            nsplit == 1 it adds the addend and writes the fp16 output, otherwise it writes
+//            its fp32 sums to part[split], which combine_reduce_kernel adds in split order.
+//            Every sum has a fixed order, so results are deterministic.  (The blocks of one
+//            column group do not hand their sums to the last of them: that needs a
+//            device-scope release per block, which on this chip writes back the whole L2 of
+//            the XCD and cost more than the second launch.)
 // ------------------------------------------------------------------------------------
-constexpr int kCombineMaxTiles = MOE_DECODE_MAX_ROWS / 16 + MOE_MAX_EXPERTS;
-
-template <int WT, bool GROUPED, int PF>
-__global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_combine_kernel(CombineParams p) {
+template <int WT, bool GROUPED, int PF, int PA, int NCB>
+__global__ __launch_bounds__(64 * kCombineWaves) void gemm_combine_kernel(CombineParams p) {
     constexpr int KSB = WTraits<WT>::KSB;
     constexpr int KSTEPS = KSB / 32;
+    constexpr int NC = 16 * NCB;                              // columns of a block
     constexpr bool CHANNEL = !GROUPED && WT != MOE_W_FP16;   // per-channel scales
-    __shared__ int tile_e[kCombineMaxTiles], tile_r0[kCombineMaxTiles], tile_n[kCombineMaxTiles];
+    __shared__ int tile_v[kDecodeMaxTiles];
     __shared__ int tok_of[MOE_DECODE_MAX_ROWS];
     __shared__ float gate_of[MOE_DECODE_MAX_ROWS];
-    __shared__ int n_tiles;
-    extern __shared__ float tok_sum[];                        // [S][T][16]
+    extern __shared__ float tok_sum[];                        // [S][T][NC]
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
+    // wave index, held in a scalar register (the compiler cannot see it is wave-uniform)
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int S = blockDim.x / kWave;
     const int ncb = p.N / 16;
-    const int cb = blockIdx.x;
+    const int ncg = p.N / NC;
+    const int cg = blockIdx.x % ncg;
+    const int sp = blockIdx.x / ncg;
     const int K = p.K, N = p.N, T = p.T, R = p.R;
     const int nSB = K / KSB;
-    const int col = cb * 16 + (lane & 15);
+    // the table's count: at most kDecodeMaxTiles by construction, clamped all the same
+    const int n_tiles = min(max(p.tiles[0], 0), kDecodeMaxTiles);
 
-    for (int i = threadIdx.x; i < S * T * 16; i += blockDim.x) tok_sum[i] = 0.0f;
+    for (int i = threadIdx.x; i < S * T * NC; i += blockDim.x) tok_sum[i] = 0.0f;
     for (int i = threadIdx.x; i < R; i += blockDim.x) {
         const int f = p.perm[i];
         tok_of[i] = (f >= 0 && f < T * p.k) ? f / p.k : -1;
         gate_of[i] = p.w_perm[i];
     }
-    // m-tile table (wave 0): experts in chunks of 64 lanes, prefix sum of their tile counts
-    if (w == 0) {
-        int base = 0;
-        for (int c0 = 0; c0 < p.E; c0 += kWave) {
-            const int e = c0 + lane;
-            int lo = 0, hi = 0;
-            if (e < p.E) {
-                lo = min(max(p.offsets[e], 0), R);
-                hi = min(max(p.offsets[e + 1], 0), R);
-            }
-            const int cnt = max(hi - lo, 0);
-            const int nt = (cnt + 15) / 16;
-            const int incl = wave_incl_scan(nt);
-            const int b0 = base + incl - nt;
-            for (int i = 0; i < nt && b0 + i < kCombineMaxTiles; ++i) {
-                tile_e[b0 + i] = e;
-                tile_r0[b0 + i] = lo + 16 * i;
-                tile_n[b0 + i] = min(16, cnt - 16 * i);
-            }
-            base += __builtin_amdgcn_readlane(incl, kWave - 1);
-        }
-        if (lane == 0) n_tiles = min(base, kCombineMaxTiles);
-    }
-    __syncthreads();
+    for (int i = threadIdx.x; i < n_tiles; i += blockDim.x) tile_v[i] = p.tiles[1 + i];
+    lds_barrier();
 
     // this wave's unit range [ua, ub)
     const int U = n_tiles * nSB;
-    const int chunk = (U + S - 1) / S;
-    const int ua = min(U, w * chunk), ub = min(U, ua + chunk);
-    const int G = GROUPED ? K / 128 : 1;
-    float* my_sum = tok_sum + w * T * 16;
+    const int G = S * p.nsplit;
+    const int chunk = (U + G - 1) / G;
+    const int ua = min(U, (sp * S + w) * chunk), ub = min(U, ua + chunk);
+    const int NG = GROUPED ? K / 128 : 1;
+    float* my_sum = tok_sum + w * T * NC;
+    int col[NCB];
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) col[c] = (cg * NCB + c) * 16 + (lane & 15);
 
     if (ua < ub) {
-        u32x4 braw[PF];
-        f16x8 araw[PF][KSTEPS];
-        uint32_t sraw[PF] = {};
+        // Two rings, as in the stream path: weights PF units ahead, activations (H rows, in
+        // L2) PA ahead, each with its own issue cursor over the unit sequence.  Tiles come from
+        // the sort, so their rows lie in [0, R) and their expert in [0, E).
+        static_assert(PF % PA == 0, "activation slots follow the weight slots");
+        u32x4 braw[PF][NCB];
+        f16x8 araw[PA][KSTEPS];
+        uint32_t sraw[PF][NCB] = {};
 
-        // issue cursor: unit (im, ik); m-tile fields cached in registers
-        int iu = ua, im = ua / nSB, ik = ua % nSB;
-        int ie = tile_e[im], ir0 = tile_r0[im], inr = tile_n[im];
-        auto issue = [&](int slot) {
-            const u32x4* wp = (const u32x4*)p.w + ((size_t)(ie * ncb + cb) * nSB + ik) * kWave + lane;
-            braw[slot] = load_weights16(wp);
-            if constexpr (GROUPED)
-                sraw[slot] = p.scales[((size_t)ie * G + ((ik * KSB) >> 7)) * N + col];
-            else if constexpr (CHANNEL)
-                sraw[slot] = p.scales[(size_t)ie * N + col];
-            const int arow = ir0 + min(lane & 15, inr - 1);
-            const f16x8* ap = (const f16x8*)(p.h + (size_t)arow * K + ik * KSB) + (lane >> 4);
-#pragma unroll
-            for (int j = 0; j < KSTEPS; ++j) araw[slot][j] = ap[j * 4];
-            // advance; past the range the last unit is issued again (never consumed)
-            if (iu + 1 < ub) {
-                ++iu;
-                if (++ik == nSB) {
-                    ik = 0;
-                    ++im;
-                    ie = tile_e[im];
-                    ir0 = tile_r0[im];
-                    inr = tile_n[im];
+        struct Cursor {
+            int iu, im, ik, e, r0, n;
+        };
+        // table entries are wave-uniform: read into scalar registers
+        auto tile_at = [&](int i) { return __builtin_amdgcn_readfirstlane(tile_v[i]); };
+        auto start = [&](Cursor& c) {
+            c.iu = ua;
+            c.im = ua / nSB;
+            c.ik = ua % nSB;
+            tile16_unpack(tile_at(c.im), c.e, c.r0, c.n);
+        };
+        // past the range the last unit is issued again (never consumed)
+        auto advance = [&](Cursor& c) {
+            if (c.iu + 1 < ub) {
+                ++c.iu;
+                if (++c.ik == nSB) {
+                    c.ik = 0;
+                    ++c.im;
+                    tile16_unpack(tile_at(c.im), c.e, c.r0, c.n);
                 }
             }
+        };
+        Cursor cw, ca;
+        start(cw);
+        start(ca);
+        auto issue_w = [&](int slot) {
+#pragma unroll
+            for (int c = 0; c < NCB; ++c) {
+                const u32x4* wp = (const u32x4*)p.w +
+                                  ((size_t)(cw.e * ncb + cg * NCB + c) * nSB + cw.ik) * kWave + lane;
+                braw[slot][c] = load_weights16(wp);
+                if constexpr (GROUPED)
+                    sraw[slot][c] = p.scales[((size_t)cw.e * NG + ((cw.ik * KSB) >> 7)) * N + col[c]];
+                else if constexpr (CHANNEL)
+                    sraw[slot][c] = p.scales[(size_t)cw.e * N + col[c]];
+            }
+            advance(cw);
+        };
+        auto issue_a = [&](int slot) {
+            const int arow = ca.r0 + min(lane & 15, ca.n - 1);
+            const f16x8* ap = (const f16x8*)(p.h + (size_t)arow * K + ca.ik * KSB) + (lane >> 4);
+#pragma unroll
+            for (int j = 0; j < KSTEPS; ++j) araw[slot][j] = ap[j * 4];
+            advance(ca);
         };
 
         const I2F4Consts k4;
         const f16x2 one2 = {(f16)1.0f, (f16)1.0f};
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[NCB];
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
         int cu = ua, cm = ua / nSB, ck = ua % nSB;      // consume cursor
-        auto flush = [&](uint32_t sbits) {
-            f32x4 v = acc;
-            if constexpr (CHANNEL) {
-                const float s = f16_bits_to_f32((uint16_t)sbits);
+        auto flush = [&](const uint32_t (&sbits)[NCB]) {
+            int te, r0, nr;
+            tile16_unpack(tile_at(cm), te, r0, nr);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] *= s;
-            }
-            const int r0 = tile_r0[cm], nr = tile_n[cm];
+            for (int c = 0; c < NCB; ++c) {
+                f32x4 v = acc[c];
+                if constexpr (CHANNEL) {
+                    const float s = f16_bits_to_f32((uint16_t)sbits[c]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * (lane >> 4) + i;
-                if (r < nr) {
-                    const int t = tok_of[r0 + r];
-                    if (t >= 0) my_sum[t * 16 + (lane & 15)] += gate_of[r0 + r] * v[i];
+                    for (int i = 0; i < 4; ++i) v[i] *= s;
                 }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * (lane >> 4) + i;
+                    if (r < nr) {
+                        const int t = tok_of[r0 + r];
+                        if (t >= 0) my_sum[t * NC + c * 16 + (lane & 15)] += gate_of[r0 + r] * v[i];
+                    }
+                }
+                acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            acc = f32x4{0.f, 0.f, 0.f, 0.f};
         };
-        auto consume_unit = [&](int slot) {
-            if constexpr (GROUPED) {
-                // two interleaved chains (even / odd K-steps): a dependent MFMA chain stalls
-                f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+        auto consume_unit = [&](int slot, int aslot) {
 #pragma unroll
-                for (int j = 0; j < KSTEPS; ++j) {
-                    if (j & 1) t1 = mfma16x16x32(araw[slot][j], weight_frag<WT, false>(braw[slot], j, one2, k4), t1);
-                    else t0 = mfma16x16x32(araw[slot][j], weight_frag<WT, false>(braw[slot], j, one2, k4), t0);
+            for (int c = 0; c < NCB; ++c) {
+                if constexpr (GROUPED) {
+                    // two interleaved chains (even / odd K-steps): a dependent MFMA chain stalls
+                    f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int j = 0; j < KSTEPS; ++j) {
+                        if (j & 1) t1 = mfma16x16x32(araw[aslot][j], weight_frag<WT, false>(braw[slot][c], j, one2, k4), t1);
+                        else t0 = mfma16x16x32(araw[aslot][j], weight_frag<WT, false>(braw[slot][c], j, one2, k4), t0);
+                    }
+                    const f32x4 t = t0 + t1;
+                    const float s = f16_bits_to_f32((uint16_t)sraw[slot][c]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[c][i] = __builtin_fmaf(t[i], s, acc[c][i]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < KSTEPS; ++j)
+                        acc[c] = mfma16x16x32(araw[aslot][j], weight_frag<WT, false>(braw[slot][c], j, one2, k4), acc[c]);
                 }
-                const f32x4 t = t0 + t1;
-                const float s = f16_bits_to_f32((uint16_t)sraw[slot]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(t[i], s, acc[i]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < KSTEPS; ++j)
-                    acc = mfma16x16x32(araw[slot][j], weight_frag<WT, false>(braw[slot], j, one2, k4), acc);
             }
             if (ck == nSB - 1 || cu == ub - 1) flush(sraw[slot]);
             ++cu;
@@ -213,52 +272,99 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_combine_kernel(Comb
         };
 
 #pragma unroll
-        for (int u = 0; u < PF; ++u) issue(u);
+        for (int u = 0; u < PF; ++u) issue_w(u);
+#pragma unroll
+        for (int u = 0; u < PA; ++u) issue_a(u);
         int kc = ua;
         for (; kc + PF <= ub; kc += PF) {
 #pragma unroll
             for (int u = 0; u < PF; ++u) {
-                consume_unit(u);
-                issue(u);
+                consume_unit(u, u % PA);
+                issue_w(u);
+                issue_a(u % PA);
             }
         }
 #pragma unroll
-        for (int u = 0; u < PF; ++u)
-            if (kc + u < ub) consume_unit(u);
+        for (int u = 0; u < PF; ++u) {
+            if (kc + u < ub) {
+                consume_unit(u, u % PA);
+                issue_a(u % PA);
+            }
+        }
         // every ring slot holds a load (a repeat of the last unit where the range ran out)
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
-            consume(braw[u]);
-            consume(sraw[u]);
+#pragma unroll
+            for (int c = 0; c < NCB; ++c) {
+                consume(braw[u][c]);
+                consume(sraw[u][c]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < PA; ++u)
 #pragma unroll
             for (int j = 0; j < KSTEPS; ++j) consume(araw[u][j]);
+    }
+    lds_barrier();
+
+    // the S waves' token sums, added in wave order; then the addend and the fp16 output, or
+    // this split's fp32 sums
+    const int c0 = cg * NC;
+    for (int i = threadIdx.x; i < T * NC; i += blockDim.x) {
+        const int t = i / NC, c = i % NC;
+        float v = 0.0f;
+        for (int s = 0; s < S; ++s) v += tok_sum[(s * T + t) * NC + c];
+        if (p.nsplit > 1) {
+            p.part[((size_t)sp * T + t) * N + c0 + c] = v;
+        } else {
+            if (p.addend) v += f16_bits_to_f32(p.addend[(size_t)t * N + c0 + c]);
+            p.out[(size_t)t * N + c0 + c] = f32_to_f16_bits(v);
         }
     }
-    __syncthreads();
+}
 
-    // the S waves' token sums, added in wave order, then the addend
-    const int c0 = cb * 16;
-    for (int i = threadIdx.x; i < T * 16; i += blockDim.x) {
-        const int t = i >> 4, c = i & 15;
-        float v = 0.0f;
-        for (int s = 0; s < S; ++s) v += tok_sum[(s * T + t) * 16 + c];
-        if (p.addend) v += f16_bits_to_f32(p.addend[(size_t)t * N + c0 + c]);
-        p.out[(size_t)t * N + c0 + c] = f32_to_f16_bits(v);
-    }
+// ------------------------------------------------------------------------------------
+// 4. out[t, c] = fp16( part[0, t, c] + .. + part[nsplit - 1, t, c] + addend[t, c] ), fp32 in
+//    that order; one thread per 4 consecutive columns.
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_reduce_kernel(const float* __restrict__ part,
+                                                             int nsplit,
+                                                             const uint16_t* __restrict__ addend,
+                                                             uint16_t* __restrict__ out, int T,
+                                                             int N) {
+    const int n4 = N / 4;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T * n4) return;
+    const size_t at = (size_t)(i / n4) * N + (size_t)(i % n4) * 4;
+    f32x4 v = *(const f32x4*)(part + at);
+    for (int s = 1; s < nsplit; ++s) v += *(const f32x4*)(part + (size_t)s * T * N + at);
+    if (addend) v += load4_f16(addend + at);
+    store4_f16_bits(out + at, v);
 }
 
 // ------------------------------------------------------------------------------------
 // Host side.
 // ------------------------------------------------------------------------------------
-constexpr int kCombineWaves = 8;
+// Blocks of the second GEMM: enough that every CU holds two of them (the 16-column blocks
+// of a d = 2048 layer number only 128), so each wave's share of the weight units is short
+// enough to be in flight at once.
+constexpr int kCombineTargetBlocks = 256;
+constexpr int kCombineMaxSplit = 8;
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+int decode_combine_split(int d) {
+    const int ncg = d / (16 * kCombineNcb);
+    int s = 1;
+    while (s < kCombineMaxSplit && ncg * s < kCombineTargetBlocks) s *= 2;
+    return s;
+}
+
 size_t decode_workspace_layout(int T, int k, int E, int d, int inter, int wtype, DecodeWs* ws,
                                char* base) {
-    (void)d;
     (void)wtype;
     const size_t R = (size_t)T * k;
+    const int nsplit = decode_combine_split(d);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -269,22 +375,31 @@ size_t decode_workspace_layout(int T, int k, int E, int d, int inter, int wtype,
     char* inv = take(R * 4);
     char* offs = take(((size_t)E + 1) * 4);
     char* wperm = take(R * 4);
+    char* tiles = take((size_t)(1 + kDecodeMaxTiles) * 4);
     char* h = take(R * (size_t)inter * 2);
+    char* part = take(nsplit > 1 ? (size_t)nsplit * T * d * 4 : 0);
     if (ws) {
         ws->perm = (int32_t*)perm;
         ws->inv_perm = (int32_t*)inv;
         ws->offsets = (int32_t*)offs;
         ws->w_perm = (float*)wperm;
+        ws->tiles = (int32_t*)tiles;
         ws->h = (uint16_t*)h;
+        ws->part = nsplit > 1 ? (float*)part : nullptr;
     }
     return off;
 }
 
 template <int WT, bool GROUPED>
 static hipError_t combine_launch(const CombineParams& p, hipStream_t stream) {
-    const unsigned grid = (unsigned)(p.N / 16);
-    const size_t lds = (size_t)kCombineWaves * p.T * 16 * sizeof(float);
-    gemm_combine_kernel<WT, GROUPED, 8><<<grid, kCombineWaves * kWave, lds, stream>>>(p);
+    const unsigned grid = (unsigned)(p.N / (16 * kCombineNcb) * p.nsplit);
+    const size_t lds = (size_t)kCombineWaves * p.T * 16 * kCombineNcb * sizeof(float);
+    gemm_combine_kernel<WT, GROUPED, 4, 2, kCombineNcb><<<grid, kCombineWaves * kWave, lds, stream>>>(p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || p.nsplit == 1) return err;
+    const int threads = p.T * (p.N / 4);
+    combine_reduce_kernel<<<(threads + 255) / 256, 256, 0, stream>>>(p.part, p.nsplit, p.addend,
+                                                                    p.out, p.T, p.N);
     return hipGetLastError();
 }
 
@@ -293,14 +408,18 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     decode_workspace_layout(a.T, a.k, a.E, a.d, a.inter, a.wtype, &ws, (char*)a.ws);
     const int R = a.T * a.k;
 
-    if (a.E <= 64)
+    static_assert(MOE_DECODE_MAX_TOKENS <= 4 * kSortWaves, "one token per 16-lane row");
+    if (a.E <= 16)
         decode_route_sort_kernel<1><<<1, kSortWaves * kWave, 0, stream>>>(
             a.logits, a.active, a.T, a.E, a.k, a.gate_all, a.ids, a.wts, ws);
+    else if (a.E <= 64)
+        decode_route_sort_kernel<4><<<1, kSortWaves * kWave, 0, stream>>>(
+            a.logits, a.active, a.T, a.E, a.k, a.gate_all, a.ids, a.wts, ws);
     else if (a.E <= 128)
-        decode_route_sort_kernel<2><<<1, kSortWaves * kWave, 0, stream>>>(
+        decode_route_sort_kernel<8><<<1, kSortWaves * kWave, 0, stream>>>(
             a.logits, a.active, a.T, a.E, a.k, a.gate_all, a.ids, a.wts, ws);
     else
-        decode_route_sort_kernel<4><<<1, kSortWaves * kWave, 0, stream>>>(
+        decode_route_sort_kernel<16><<<1, kSortWaves * kWave, 0, stream>>>(
             a.logits, a.active, a.T, a.E, a.k, a.gate_all, a.ids, a.wts, ws);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -327,24 +446,27 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     g.act = a.act;
     g.split = gemm_choose_split(R, a.E, a.d, n1, a.wtype, a.act, 0);
     g.tile = 0;
+    g.tiles16 = ws.tiles;
     err = launch_gemm_stream(g, stream);
     if (err != hipSuccess) return err;
 
     CombineParams c;
     c.h = ws.h;
-    c.offsets = ws.offsets;
+    c.tiles = ws.tiles;
     c.perm = ws.perm;
     c.w_perm = ws.w_perm;
     c.w = a.w2;
     c.scales = a.s2;
     c.addend = a.addend;
     c.out = a.out;
+    c.part = ws.part;
     c.R = R;
     c.E = a.E;
     c.K = a.inter;
     c.N = a.d;
     c.T = a.T;
     c.k = a.k;
+    c.nsplit = decode_combine_split(a.d);
     // the addend (e.g. shared experts computed on another stream) is first read here
     if (a.addend_ready) {
         err = hipStreamWaitEvent(stream, (hipEvent_t)a.addend_ready, 0);

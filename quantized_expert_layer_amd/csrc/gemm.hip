@@ -54,34 +54,48 @@ __device__ __forceinline__ int out_dest_row(const GemmParams& p, int gp) {
 
 // ------------------------------------------------------------------------------------
 // Stream path.
-//   grid  = m-tiles(upper bound) x NBo blocks of S waves (S = p.split, 1..MOE_MAX_SPLIT_K).
-//   block = one 16-row m-tile x one 16-column output block; for SwiGLU the gate block and
-//           the up block (columns I + ...) of the same 16 outputs.  Wave w of the block
-//           streams the w-th of S equal K slices; the S partial sums meet in LDS and are
-//           added in the fixed order 0, 1, .., S-1 by wave 0, which runs the epilogue.
-//           Splitting K inside the block multiplies the waves of a decode step (which has
-//           few output blocks) without a second launch or a workspace.
+//   grid  = m-tiles(upper bound) x NGO blocks of S waves (S = p.split, 1..MOE_MAX_SPLIT_K).
+//   block = one 16-row m-tile x OPB consecutive 16-column output blocks; for SwiGLU the OPB
+//           gate blocks and the OPB up blocks (columns I + ...) of the same outputs, so a wave
+//           holds NCB = OPB (x2 for SwiGLU) weight column blocks.  One activation fragment of
+//           the tile serves all NCB of them: a 16-row fragment is four times the bytes of a
+//           1 KiB weight unit, and a CU's vector-memory pipeline moves 64 bytes per clock.
+//           Wave w of the block streams the w-th of S equal K slices; the S partial sums meet
+//           in LDS and are added in the fixed order 0, 1, .., S-1 by wave 0, which runs the
+//           epilogue.  Splitting K inside the block multiplies the waves of a decode step
+//           (which has few output blocks) without a second launch or a workspace.
 //   scales= per-channel and group scales multiply fp32 sums: a group-128 scale the sum of
 //           one super-block's MFMAs, a per-channel scale the final sum.  Mathematically this
 //           is the sum over the scaled weights; it skips the fp16 rounding of each scaled
 //           weight and saves a packed multiply per weight pair.
 // ------------------------------------------------------------------------------------
-template <int WT, int ACT, bool GROUPED, int PF>
-__global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmParams p, int nbo) {
+template <int WT, int ACT, bool GROUPED, int PF, int PA, int OPB>
+__global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmParams p, int ngo) {
     constexpr int KSB = WTraits<WT>::KSB;
     constexpr int KSTEPS = KSB / 32;
-    constexpr int NCB = (ACT == MOE_ACT_SWIGLU) ? 2 : 1;
+    constexpr bool SWI = (ACT == MOE_ACT_SWIGLU);
+    constexpr int NCB = SWI ? 2 * OPB : OPB;
     extern __shared__ f32x4 red[];          // [S - 1][NCB][64] partial sums of waves 1..S-1
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
+    // wave index, held in a scalar register (the compiler cannot see it is wave-uniform)
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int S = blockDim.x / kWave;
 
-    // (m-tile, output column block), m-tile slowest so that the blocks of existing tiles come
+    // (m-tile, output column group), m-tile slowest so that the blocks of existing tiles come
     // first and the surplus of the upper-bound grid exits last
-    const int cbo = blockIdx.x % nbo;
-    const int mt = blockIdx.x / nbo;
+    const int cgo = blockIdx.x % ngo;
+    const int mt = blockIdx.x / ngo;
     int e, row0, rows;
-    if (!find_m_tile<16>(p.offsets, p.E, p.R, mt, e, row0, rows)) return;   // block-uniform
+    if (p.tiles16) {
+        // the decode tile table: both loads are issued before the count is compared (the
+        // grid's upper bound keeps 1 + mt inside the table)
+        const int n = p.tiles16[0];
+        const int v = p.tiles16[1 + mt];
+        if (mt >= n) return;                                            // block-uniform
+        tile16_unpack(v, e, row0, rows);
+    } else if (!find_m_tile<16>(p.offsets, p.E, p.R, mt, e, row0, rows)) {
+        return;                                                         // block-uniform
+    }
 
     const int K = p.K, N = p.N;
     const int nSB = K / KSB;
@@ -90,38 +104,59 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmP
     const int kb1 = min(nSB, kb0 + chunk);
 
     const int ncbw = N / 16;
+    const int nbo = SWI ? ncbw / 2 : ncbw;       // output column blocks
     int ncol[NCB];
     const u32x4* wp[NCB];
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
-        const int cbw = cbo + c * nbo;          // SwiGLU: up block sits I/16 blocks later
+        // SwiGLU: the up block of output block o sits nbo blocks after its gate block
+        const int cbw = (c < OPB) ? cgo * OPB + c : nbo + cgo * OPB + (c - OPB);
         ncol[c] = cbw * 16 + (lane & 15);
         wp[c] = (const u32x4*)p.w + ((size_t)(e * ncbw + cbw) * nSB) * kWave + lane;
     }
     const int G = GROUPED ? K / 128 : 1;         // groups of 128 rows along K
     const uint16_t* sp = p.scales + (size_t)e * G * N;
 
-    // A fragment source: row (lane & 15) of the tile, 8 halves at k = 8 * (lane >> 4).
+    // A fragment source: row (lane & 15) of the tile, 8 halves at k = 8 * (lane >> 4).  With a
+    // row map the source row is a dependent load; it is issued before the weights and read
+    // after them, so the weights do not wait for it.
     const int arow = lane & 15;
     const bool arow_ok = arow < rows;
-    const int asrc = a_source_row(p, row0 + (arow_ok ? arow : 0));
-    const f16x8* ap = (const f16x8*)(p.a + (size_t)asrc * K) + (lane >> 4);
+    const int gp = row0 + (arow_ok ? arow : 0);
+    const int amap = p.a_rows ? p.a_rows[gp] : gp;
+    __builtin_amdgcn_sched_barrier(0);
 
     f32x4 acc[NCB];
 #pragma unroll
     for (int c = 0; c < NCB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Two rings: weights (HBM, the long latency) PF super-blocks ahead, activations (a few
+    // rows, cached) PA ahead.  An activation slot is four times a weight slot in registers,
+    // so the short ring leaves room for more resident waves.
+    static_assert(PF % PA == 0, "activation slots follow the weight slots");
     u32x4 braw[PF][NCB];
-    f16x8 araw[PF][KSTEPS];
+    f16x8 araw[PA][KSTEPS];
     uint32_t sraw[PF][NCB] = {};           // fp16 scale bits, zero-extended
 
-    auto issue = [&](int slot, int kb) {
+    auto issue_w = [&](int slot, int kb) {
         const int kl = min(kb, kb1 - 1);        // clamped: tail loads repeat the last block
 #pragma unroll
         for (int c = 0; c < NCB; ++c) {
             braw[slot][c] = load_weights16(wp[c] + (size_t)kl * kWave);
             if constexpr (GROUPED) sraw[slot][c] = (uint32_t)sp[(size_t)((kl * KSB) >> 7) * N + ncol[c]];
         }
+    };
+
+    if (kb0 < kb1) {
+        // ring of PF register slots: slot u holds super-block kc + u of the current group
+#pragma unroll
+        for (int u = 0; u < PF; ++u) issue_w(u, kb0 + u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const int asrc = p.a_rows ? min(max(amap / p.a_div, 0), p.a_nrows - 1) : amap;
+    const f16x8* ap = (const f16x8*)(p.a + (size_t)asrc * K) + (lane >> 4);
+    auto issue_a = [&](int slot, int kb) {
+        const int kl = min(kb, kb1 - 1);
 #pragma unroll
         for (int j = 0; j < KSTEPS; ++j) araw[slot][j] = ap[(kl * KSB + j * 32) / 8];
     };
@@ -153,23 +188,28 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmP
     };
 
     if (kb0 < kb1) {
-        // ring of PF register slots: slot u holds super-block kc + u of the current group
 #pragma unroll
-        for (int u = 0; u < PF; ++u) issue(u, kb0 + u);
+        for (int u = 0; u < PA; ++u) issue_a(u, kb0 + u);
         int kc = kb0;
         // steady state, branch-free: compute from slot u in place, then refill slot u with the
-        // block PF ahead (no register copies of in-flight loads, so no early waits)
+        // block PF ahead and activation slot u % PA with the block PA ahead (no register
+        // copies of in-flight loads, so no early waits)
         for (; kc + PF <= kb1; kc += PF) {
 #pragma unroll
             for (int u = 0; u < PF; ++u) {
-                compute(braw[u], sraw[u], araw[u]);
-                issue(u, kc + u + PF);
+                compute(braw[u], sraw[u], araw[u % PA]);
+                issue_w(u, kc + u + PF);
+                issue_a(u % PA, kc + u + PA);
             }
         }
-        // tail: fewer than PF blocks left, already in their slots
+        // tail: fewer than PF blocks left, their weights already in their slots
 #pragma unroll
-        for (int u = 0; u < PF; ++u)
-            if (kc + u < kb1) compute(braw[u], sraw[u], araw[u]);
+        for (int u = 0; u < PF; ++u) {
+            if (kc + u < kb1) {
+                compute(braw[u], sraw[u], araw[u % PA]);
+                issue_a(u % PA, kc + u + PA);
+            }
+        }
         // every ring slot holds a load (a repeat of the last block where the slice ran out)
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
@@ -178,9 +218,11 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmP
                 consume(braw[u][c]);
                 if constexpr (GROUPED) consume(sraw[u][c]);
             }
+        }
+#pragma unroll
+        for (int u = 0; u < PA; ++u)
 #pragma unroll
             for (int j = 0; j < KSTEPS; ++j) consume(araw[u][j]);
-        }
     }
 
     // fixed-order reduction of the K slices
@@ -189,7 +231,7 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmP
 #pragma unroll
             for (int c = 0; c < NCB; ++c) red[((w - 1) * NCB + c) * kWave + lane] = acc[c];
         }
-        __syncthreads();
+        lds_barrier();
         if (w > 0) return;
         for (int s = 1; s < S; ++s) {
 #pragma unroll
@@ -209,19 +251,24 @@ __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmP
             for (int i = 0; i < 4; ++i) acc[c][i] *= sc;
         }
     }
-    const int n_out = (ACT == MOE_ACT_SWIGLU) ? N / 2 : N;
-    uint16_t* ocol = p.out + cbo * 16 + (lane & 15);
+    const int n_out = SWI ? N / 2 : N;
+    uint16_t* ocol = p.out + cgo * OPB * 16 + (lane & 15);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * (lane >> 4) + i;      // row of the tile
         if (r >= rows) break;
-        float v;
-        if constexpr (ACT == MOE_ACT_SWIGLU) v = silu(acc[0][i]) * acc[1][i];
-        else if constexpr (ACT == MOE_ACT_RELU) v = fmaxf(acc[0][i], 0.0f);
-        else v = acc[0][i];
-        if (p.row_scale) v *= p.row_scale[row0 + r];
+        const float rs = p.row_scale ? p.row_scale[row0 + r] : 1.0f;
         const int dst = out_dest_row(p, row0 + r);
-        if (dst >= 0) ocol[(size_t)dst * n_out] = f32_to_f16_bits(v);
+        if (dst < 0) continue;
+#pragma unroll
+        for (int o = 0; o < OPB; ++o) {
+            float v;
+            if constexpr (SWI) v = silu(acc[o][i]) * acc[OPB + o][i];
+            else if constexpr (ACT == MOE_ACT_RELU) v = fmaxf(acc[o][i], 0.0f);
+            else v = acc[o][i];
+            if (p.row_scale) v *= rs;
+            ocol[(size_t)dst * n_out + o * 16] = f32_to_f16_bits(v);
+        }
     }
 }
 
@@ -641,12 +688,13 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
     const int ob0 = (cbg * 4 + wave) * NO;         // first output block of the wave
     const bool col_ok = ob0 + lc / 2 < nbo;
     uint16_t* obase = p.out + ob0 * 16 + lc * 8;
-    static_assert(RPI <= BM, "a store pass reads rows inside the wave's region");
+    // a pass may cover more rows than the tile holds (RPI need not divide MA * 16): only rows
+    // below `rows` (<= MA * 16 <= BM) are read, so every read stays in the wave's own region
 #pragma unroll
     for (int i = 0; i < (MA * 16 + RPI - 1) / RPI; ++i) {
         const int r = i * RPI + lr;
-        const u32x4 v = *(const u32x4*)(region + r * RS + lc * 8);
         if (r < rows && col_ok) {
+            const u32x4 v = *(const u32x4*)(region + r * RS + lc * 8);
             const int dst = out_dest_row(p, row0 + r);
             if (dst >= 0) *(u32x4*)(obase + (size_t)dst * n_out) = v;
         }
@@ -718,6 +766,21 @@ __global__ __launch_bounds__(256 * KG, (KG == 1 && MS < 8) ? 2 : 1) void gemm_ti
 // ------------------------------------------------------------------------------------
 static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
+// Output blocks per wave of the stream path.  A unit's activation fragment is 4 KiB for 4-bit
+// codes, 2 KiB for 8-bit codes and 1 KiB for fp16 weights, against 1 KiB of weights per column
+// block: four weight column blocks per wave for 4-bit codes (two output blocks for SwiGLU,
+// whose gate and up blocks pair up), two for 8-bit codes, one for fp16 weights (where more
+// column blocks per wave would only mean fewer waves), as far as the output blocks divide.
+static int stream_opb(int N, int act, int wtype) {
+    const bool swi = act == MOE_ACT_SWIGLU;
+    const int nbo = swi ? N / 32 : N / 16;
+    const int ncb = wtype == MOE_W_INT4 ? 4 : (wtype == MOE_W_INT8 ? 2 : 1);
+    int o = swi ? (ncb >= 2 ? ncb / 2 : 1) : ncb;
+    while (o > 1 && nbo % o != 0) o /= 2;
+    return o;
+}
+
+
 int gemm_choose_path(int R, int E, int K, int N, int wtype, int act, int forced) {
     (void)K; (void)N; (void)wtype; (void)act;
     if (forced == MOE_PATH_STREAM || forced == MOE_PATH_TILE) return forced;
@@ -733,7 +796,7 @@ int gemm_choose_split(int R, int E, int K, int N, int wtype, int act, int forced
     const int nSB = K / KSB;
     const int active = R < E ? R : E;
     const int nbo = (act == MOE_ACT_SWIGLU) ? N / 32 : N / 16;
-    const long blocks = (long)active * cdiv(R, active > 0 ? active * 16 : 16) * nbo;
+    const long blocks = (long)active * cdiv(R, active > 0 ? active * 16 : 16) * (nbo / stream_opb(N, act, wtype));
     // Split only a launch with fewer than two blocks per CU: with a few hundred streams or
     // more, extra waves per SIMD measured no faster (the streams already share each SIMD's
     // VALU issue for the in-register dequantization), and each slice keeps at least 8
@@ -743,23 +806,41 @@ int gemm_choose_split(int R, int E, int K, int N, int wtype, int act, int forced
     return s;
 }
 
+template <int WT, int ACT, bool GROUPED, int OPB>
+static hipError_t stream_launch(const GemmParams& p, int ngo, long blocks, hipStream_t stream) {
+    constexpr int NCB = (ACT == MOE_ACT_SWIGLU) ? 2 * OPB : OPB;
+    const unsigned threads = 64u * (unsigned)p.split;
+    const size_t lds = (size_t)(p.split - 1) * NCB * 64 * sizeof(f32x4);
+    // weight ring: about 16 KiB per wave for a decode step (few streams, each keeps that much
+    // in flight), half that otherwise (registers for more resident waves); the activation
+    // ring is two units deep
+    constexpr int PF_DEC = NCB >= 4 ? 4 : 8;
+    constexpr int PF = NCB >= 4 ? 2 : 4;
+    if (p.R <= 128)
+        gemm_stream_kernel<WT, ACT, GROUPED, PF_DEC, 2, OPB><<<(unsigned)blocks, threads, lds, stream>>>(p, ngo);
+    else
+        gemm_stream_kernel<WT, ACT, GROUPED, PF, 2, OPB><<<(unsigned)blocks, threads, lds, stream>>>(p, ngo);
+    return hipGetLastError();
+}
+
 template <int WT, int ACT, bool GROUPED>
 static hipError_t stream_dispatch(const GemmParams& p, hipStream_t stream) {
     const int nbo = (ACT == MOE_ACT_SWIGLU) ? p.N / 32 : p.N / 16;
+    const int opb = stream_opb(p.N, ACT, WT);
+    const int ngo = nbo / opb;
     const int active = p.R < p.E ? p.R : p.E;
     const int mt_ub = cdiv(p.R, 16) + active;
-    const long blocks = (long)mt_ub * nbo;
+    const long blocks = (long)mt_ub * ngo;
     if (blocks > 0x7fffffffL || p.split < 1 || p.split > MOE_MAX_SPLIT_K) return hipErrorInvalidValue;
-    constexpr int NCB = (ACT == MOE_ACT_SWIGLU) ? 2 : 1;
-    const unsigned threads = 64u * (unsigned)p.split;
-    const size_t lds = (size_t)(p.split - 1) * NCB * 64 * sizeof(f32x4);
-    // few rows (a decode step): few streams, so each keeps 8 super-blocks in flight;
-    // otherwise 4, which leaves registers for more resident waves
-    if (p.R <= 128)
-        gemm_stream_kernel<WT, ACT, GROUPED, 8><<<(unsigned)blocks, threads, lds, stream>>>(p, nbo);
-    else
-        gemm_stream_kernel<WT, ACT, GROUPED, 4><<<(unsigned)blocks, threads, lds, stream>>>(p, nbo);
-    return hipGetLastError();
+    if (p.tiles16 && mt_ub > kDecodeMaxTiles) return hipErrorInvalidValue;   // table bound
+    // only the combinations stream_opb chooses are instantiated
+    if constexpr (WT == MOE_W_INT4 && ACT != MOE_ACT_SWIGLU) {
+        if (opb == 4) return stream_launch<WT, ACT, GROUPED, 4>(p, ngo, blocks, stream);
+    }
+    if constexpr (WT != MOE_W_FP16) {
+        if (opb == 2) return stream_launch<WT, ACT, GROUPED, 2>(p, ngo, blocks, stream);
+    }
+    return stream_launch<WT, ACT, GROUPED, 1>(p, ngo, blocks, stream);
 }
 
 template <int WT, int ACT, bool GROUPED, int MS, int NS>

@@ -51,6 +51,7 @@ struct GemmParams {
     int wtype, group, act;
     int split;           // stream path: waves per block splitting K (1..MOE_MAX_SPLIT_K)
     int tile;            // enum moe_tile (0 = automatic)
+    const int32_t* tiles16;  // stream path: NULL, or the decode tile table (16-row m-tiles)
 };
 
 // Path/split decisions (host-only, deterministic in the arguments).
@@ -68,19 +69,23 @@ struct DecodeWs {
     int32_t* inv_perm;       // [R]
     int32_t* offsets;        // [E + 1]
     float* w_perm;           // [R]
+    int32_t* tiles;          // [1 + kDecodeMaxTiles] tile table (count, then packed tiles)
     uint16_t* h;             // fp16 [R, inter] GEMM 1 output, sorted rows
+    float* part;             // fp32 [nsplit, T, d] partial token sums of GEMM 2 (nsplit > 1)
 };
 
 struct CombineParams {
     const uint16_t* h;       // fp16 [R, K] rows sorted by expert
-    const int32_t* offsets;  // [E + 1]
+    const int32_t* tiles;    // tile table of the sorted rows
     const int32_t* perm;     // [R] flat slot t*k + j of sorted row p
     const float* w_perm;     // [R] gate weight of sorted row p
     const void* w;           // packed weights [E, K, N]
     const uint16_t* scales;  // [E, G, N], NULL for fp16 weights
     const uint16_t* addend;  // fp16 [T, N] or NULL
     uint16_t* out;           // fp16 [T, N]
+    float* part;             // fp32 [nsplit, T, N] when nsplit > 1
     int R, E, K, N, T, k;
+    int nsplit;              // blocks sharing the units of one 16-column block
 };
 
 struct DecodeArgs {
@@ -101,6 +106,8 @@ struct DecodeArgs {
     void* ws;
 };
 
+// Blocks sharing one 16-column block of the decode step's second GEMM (a power of two).
+int decode_combine_split(int d);
 // Bytes of the decode workspace; with ws and base given, also the part addresses.
 size_t decode_workspace_layout(int T, int k, int E, int d, int inter, int wtype, DecodeWs* ws,
                                char* base);

@@ -16,28 +16,22 @@
 
 namespace moe {
 
-constexpr int kSortLdsKeys = 16384;     // keys staged in LDS when R fits (64 KB)
 constexpr int kSortBlockSlots = kSortWaves * kWave;   // slots per block of the multi-block sort
 constexpr int kSortCountBlocks = 8;   // up to this many blocks each block counts all keys itself
 
-// KEYS_IN_LDS: all R keys are first copied to LDS with one coalesced pass, so the two walks
-// of the sort read LDS instead of issuing one dependent global load per 64-key chunk.
-template <bool KEYS_IN_LDS>
+// One workgroup sorts up to kSortBlockSlots slots.  The keys are first copied to LDS with one
+// coalesced pass, so the two walks of the sort read LDS instead of issuing one dependent global
+// load per 64-key chunk.
 __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ ids,
                                                     const float* __restrict__ wts, int R, int E,
                                                     int32_t* __restrict__ perm,
                                                     int32_t* __restrict__ inv_perm,
                                                     int32_t* __restrict__ offsets,
                                                     float* __restrict__ w_perm) {
-    __shared__ int keys[KEYS_IN_LDS ? kSortLdsKeys : 1];
-    if constexpr (KEYS_IN_LDS) {
-        for (int i = threadIdx.x; i < R; i += blockDim.x) keys[i] = ids[i];
-    }
-    auto key_of = [&](int f) -> int {
-        if constexpr (KEYS_IN_LDS) return keys[f];
-        else return ids[f];
-    };
-    sort_block(R, E, key_of, [&](int f) { return wts[f]; }, perm, inv_perm, offsets, w_perm);
+    __shared__ int keys[kSortBlockSlots];
+    for (int i = threadIdx.x; i < R; i += blockDim.x) keys[i] = ids[i];
+    sort_block(R, E, [&](int f) { return keys[f]; }, [&](int f) { return wts[f]; }, perm,
+               inv_perm, offsets, w_perm);
 }
 
 // x_perm[p] = x[perm[p] / k], 16 bytes per thread; rows with perm < 0 are zero-filled.
@@ -223,12 +217,8 @@ hipError_t launch_sort(const int32_t* ids, const float* wts, int R, int E, int32
             ids, wts, R, E, hist, nblk, perm, inv_perm, offsets, w_perm);
         return hipGetLastError();
     }
-    if (R <= kSortLdsKeys)
-        sort_kernel<true><<<1, kSortWaves * kWave, 0, stream>>>(ids, wts, R, E, perm, inv_perm,
-                                                                offsets, w_perm);
-    else
-        sort_kernel<false><<<1, kSortWaves * kWave, 0, stream>>>(ids, wts, R, E, perm, inv_perm,
-                                                                 offsets, w_perm);
+    sort_kernel<<<1, kSortWaves * kWave, 0, stream>>>(ids, wts, R, E, perm, inv_perm, offsets,
+                                                     w_perm);
     return hipGetLastError();
 }
 

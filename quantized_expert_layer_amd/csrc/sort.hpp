@@ -130,19 +130,19 @@ __device__ __forceinline__ void sort_block(int R, int E, KeyOf key_of, WOf w_of,
 
 // The same sort done by a single wave, for the few slots of a decode step: one running count
 // per expert in LDS (cnt [E], the caller's), no per-wave tables and no block barriers.  LDS
-// accesses of one wave take effect in program order; the wave-scope fences keep the compiler
-// from moving them across the phases.  Same outputs as sort_block.
+// accesses of one wave take effect in program order; the wave-scope LDS fences keep the
+// compiler from moving them across the phases.  Same outputs as sort_block.
+// off_lds (LDS, [E + 1]) receives a copy of the offsets.
 template <typename KeyOf, typename WOf>
 __device__ __forceinline__ void sort_wave(int R, int E, KeyOf key_of, WOf w_of, int* cnt,
-                                          int32_t* __restrict__ perm,
+                                          int* off_lds, int32_t* __restrict__ perm,
                                           int32_t* __restrict__ inv_perm,
                                           int32_t* __restrict__ offsets,
                                           float* __restrict__ w_perm) {
     const int lane = threadIdx.x & (kWave - 1);
-    auto phase = [] {
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-    };
+    // LDS ordering only: the global stores of perm / inv_perm / w_perm need not complete
+    // before the next phase
+    auto phase = [] { lds_wave_fence(); };
     for (int e = lane; e < E; e += kWave) cnt[e] = 0;
     phase();
     const int nbits = (E <= 1) ? 0 : 32 - __clz(E - 1);
@@ -163,11 +163,15 @@ __device__ __forceinline__ void sort_wave(int R, int E, KeyOf key_of, WOf w_of, 
         const int incl = wave_incl_scan(v);
         if (e < E) {
             offsets[e] = run + incl - v;
+            off_lds[e] = run + incl - v;
             cnt[e] = run + incl - v;
         }
         run += __builtin_amdgcn_readlane(incl, kWave - 1);
     }
-    if (lane == 0) offsets[E] = run;
+    if (lane == 0) {
+        offsets[E] = run;
+        off_lds[E] = run;
+    }
     phase();
     for (int c = 0; c < chunks; ++c) {
         const int f = c * kWave + lane;

@@ -228,6 +228,10 @@ def test_combine_and_dequant_validation():
     assert L.moe_dequant(FAKE, FAKE, 2, 0, 2, 128, 16, FAKE, None) == q.MOE_ERR_INVALID  # fp16
     assert L.moe_dequant(FAKE, FAKE, 0, 0, 2, 100, 16, FAKE, None) == q.MOE_ERR_UNSUPPORTED
     assert L.moe_dequant(None, FAKE, 0, 0, 2, 128, 16, FAKE, None) == q.MOE_ERR_INVALID
+    # every pointer follows the header's 16-byte convention
+    assert L.moe_dequant(MIS, FAKE, 0, 0, 2, 128, 16, FAKE, None) == q.MOE_ERR_INVALID
+    assert L.moe_dequant(FAKE, MIS, 0, 0, 2, 128, 16, FAKE, None) == q.MOE_ERR_INVALID
+    assert L.moe_dequant(FAKE, FAKE, 0, 0, 2, 128, 16, MIS, None) == q.MOE_ERR_INVALID
 
 
 @pytest.mark.skipif(gpu_available(), reason="valid calls would launch on a real GPU")

@@ -162,9 +162,10 @@ def _a256(v):
 @pytest.mark.parametrize("name,T", [("qwen15_moe", 17), ("tiny_k8", 64), ("wide_e256", 64),
                                     ("phi35_moe", 1), ("dsv2_lite", 9)])
 def test_decode_sort_matches_moe_permute(name, T):
-    """The decode step's one-wave sort leaves perm, inv_perm, offsets and w_perm at the head of
-    its workspace (256-byte aligned parts, in that order): they equal moe_permute's, bit for
-    bit, on the same routing."""
+    """The decode step's one-wave sort leaves perm, inv_perm, offsets, w_perm and the tile table
+    at the head of its workspace (256-byte aligned parts, in that order): the first four equal
+    moe_permute's, bit for bit, on the same routing, and the table lists the 16-row tiles of
+    the offsets."""
     inp, layer = _layer(name, T)
     x, L = dev(inp.x), dev(inp.logits)
     ws = layer.workspace(T)
@@ -184,6 +185,18 @@ def test_decode_sort_matches_moe_permute(name, T):
     assert np.array_equal(inv, host(i2))
     assert np.array_equal(off, host(off2))
     assert np.array_equal(wp.view(np.uint32), host(w2).view(np.uint32))
+    # then the tile table: the count, then every expert's 16-row tiles in expert order, each
+    # packed as e | first_row << 9 | (rows - 1) << 19
+    o_tiles = _a256(o_wp + 4 * R)
+    n_max = R // 16 + 256
+    tab = i32(o_tiles, 1 + n_max)
+    want = []
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        for r0 in range(lo, hi, 16):
+            want.append(e | (r0 << 9) | ((min(16, hi - r0) - 1) << 19))
+    assert tab[0] == len(want)
+    assert np.array_equal(tab[1:1 + len(want)], np.array(want, dtype=np.int32))
 
 
 def test_decode_waits_for_an_addend_made_on_another_stream():
