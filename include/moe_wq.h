@@ -9,7 +9,8 @@
  *   4. moe_unpermute_combine restore token order, scale by gate weight, sum the k rows
  *   and moe_dequant          the standalone per-expert dequantization (Algorithm 1);
  *   moe_decode_layer         steps 1-4 for the few tokens of a decode / verify step, in three
- *                            launches
+ *                            launches (moe_decode_layer_noalloc: the same on the library's
+ *                            own scratch memory, for callers that cannot allocate)
  *   moe_elb_accumulate / moe_elb_top_m   the expert lookahead buffer of a speculative draft
  *   moe_bf16_recombine       BF16 values from separately stored exponent / sign-mantissa bytes
  *
@@ -34,8 +35,9 @@
  *     nothing is enqueued and outputs are untouched.
  *   - T == 0 (or R == 0) returns MOE_OK and enqueues nothing.
  *   - Pointers must be 16-byte aligned.
- *   - The library keeps no mutable global state; calls are thread-safe.  Results are
- *     deterministic: two identical calls give identical bits.
+ *   - Apart from the scratch array of moe_decode_layer_noalloc, the library keeps no mutable
+ *     global state; the other calls are thread-safe.  Results are deterministic: two
+ *     identical calls give identical bits.
  */
 #ifndef MOE_WQ_H
 #define MOE_WQ_H
@@ -263,6 +265,30 @@ int32_t moe_decode_layer(const float* logits, const uint8_t* active, const uint1
 /* Workspace bytes of moe_decode_layer (0 for arguments it does not accept). */
 size_t moe_decode_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int32_t inter,
                                  int32_t wtype);
+
+/*
+ * moe_decode_layer_noalloc -- moe_decode_layer without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is the library's own scratch array of
+ * MOE_DECODE_SCRATCH_BYTES bytes in device memory: each device the library runs on holds one
+ * copy, from the library's load until the process ends.  The call allocates and frees
+ * nothing.  Every call on a device uses that device's one array, so calls that overlap in time
+ * on one device (different streams or threads) race and give undefined results; serialise
+ * them.  Nothing in the array needs to start at any value: every part of the workspace is
+ * written before it is read within a call (the previous call's contents are left behind).
+ *   Arguments, outputs, numerics and errors are those of moe_decode_layer (without ws and
+ *   ws_bytes), plus MOE_ERR_UNSUPPORTED for a step whose workspace,
+ *   moe_decode_workspace_size(T, k, E, d, inter, wtype), exceeds MOE_DECODE_SCRATCH_BYTES, and
+ *   MOE_ERR_HIP if the array's device address cannot be obtained.
+ */
+#define MOE_DECODE_SCRATCH_BYTES (8u << 20)
+int32_t moe_decode_layer_noalloc(const float* logits, const uint8_t* active, const uint16_t* x,
+                                 int32_t T, int32_t E, int32_t k, int32_t gate_mode, int32_t d,
+                                 int32_t inter, int32_t act,
+                                 const void* w1, const uint16_t* s1, const void* w2,
+                                 const uint16_t* s2, int32_t wtype, int32_t group_size,
+                                 const uint16_t* addend, void* addend_ready, int32_t* topk_ids,
+                                 float* topk_w, uint16_t* out, void* stream);
 
 /*
  * Attainable-peak probes (measurement aids, not part of the layer): what plain code reaches on

@@ -27,6 +27,7 @@ __all__ = [
     "moe_dequant", "moe_pack_wq", "moe_packed_bytes", "moe_gemm_workspace_size",
     "moe_permute_workspace_size", "GemmOpts", "EXPORTED_SYMBOLS", "new_output",
     "moe_probe_read", "moe_probe_mfma", "moe_decode_layer", "moe_decode_workspace_size",
+    "moe_decode_layer_noalloc", "MOE_DECODE_SCRATCH_BYTES",
     "MOE_DECODE_MAX_TOKENS", "MOE_DECODE_MAX_ROWS", "moe_elb_accumulate", "moe_elb_top_m",
     "moe_bf16_recombine",
 ]
@@ -40,6 +41,7 @@ PATH_AUTO, PATH_STREAM, PATH_TILE = 0, 1, 2
 TILE_AUTO, TILE_64x256, TILE_64x128, TILE_128x128, TILE_48x256, TILE_48x128 = 0, 1, 2, 3, 4, 5
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_SPLIT_K = 256, 8, 8
 MOE_DECODE_MAX_TOKENS, MOE_DECODE_MAX_ROWS = 64, 512
+MOE_DECODE_SCRATCH_BYTES = 8 << 20
 
 WTYPES = {"int4": W_INT4, "int8": W_INT8, "fp16": W_FP16}
 ACTS = {"none": ACT_NONE, "relu": ACT_RELU, "swiglu": ACT_SWIGLU}
@@ -53,6 +55,7 @@ EXPORTED_SYMBOLS = (
     "moe_grouped_gemm_wq_rows", "moe_gemm_workspace_size", "moe_unpermute_combine", "moe_dequant", "moe_packed_bytes",
     "moe_pack_wq", "moe_status_str", "moe_version", "moe_probe_read", "moe_probe_mfma",
     "moe_decode_layer", "moe_decode_workspace_size", "moe_route_topk_active",
+    "moe_decode_layer_noalloc",
     "moe_elb_accumulate", "moe_elb_top_m", "moe_bf16_recombine",
 )
 
@@ -116,6 +119,8 @@ def lib():
         "moe_probe_mfma": (_I, [_I, _P, _I, _P]),
         "moe_decode_layer": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I,
                                   _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+        "moe_decode_layer_noalloc": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
+                                          _I, _I, _P, _P, _P, _P, _P, _P]),
         "moe_route_topk_active": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
         "moe_elb_accumulate": (_I, [_P, _I, _I, _I, _I, _P, _P]),
         "moe_elb_top_m": (_I, [_P, _I, _I, _I, _P, _P, _P]),
@@ -395,6 +400,41 @@ def moe_decode_layer(logits, x, k, gate_mode, inter, act, w1, s1, w2, s2, wtype,
         _ptr(addend), None if addend_ready is None else addend_ready.cuda_event,
         _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
+    return out, topk_ids, topk_w
+
+
+def moe_decode_layer_noalloc(logits, x, k, gate_mode, inter, act, w1, s1, w2, s2, wtype,
+                             group_size, addend=None, topk_ids=None, topk_w=None, out=None,
+                             stream=None, active=None, addend_ready=None):
+    """moe_decode_layer on the library's own scratch array (no workspace argument; calls that
+    overlap on one device race).  Returns (out, topk_ids, topk_w)."""
+    torch = _torch()
+    T, E = logits.shape
+    d = x.shape[1]
+    wt = WTYPES.get(wtype, wtype)
+    dev = x.device
+    if out is None:
+        out = new_output((T, d), torch.float16, dev)
+    if topk_ids is None:
+        topk_ids = new_output((T, k), torch.int32, dev)
+    if topk_w is None:
+        topk_w = new_output((T, k), torch.float32, dev)
+    _need(logits, torch.float32, "logits", T * E)
+    _need(x, torch.float16, "x", T * d)
+    _need(w1, torch.uint8, "w1")
+    _need(s1, torch.float16, "s1")
+    _need(w2, torch.uint8, "w2")
+    _need(s2, torch.float16, "s2")
+    _need(addend, torch.float16, "addend", T * d)
+    _need(topk_ids, torch.int32, "topk_ids", T * k)
+    _need(topk_w, torch.float32, "topk_w", T * k)
+    _need(out, torch.float16, "out", T * d)
+    _need(active, torch.uint8, "active", T)
+    _check("moe_decode_layer_noalloc", lib().moe_decode_layer_noalloc(
+        _ptr(logits), _ptr(active), _ptr(x), T, E, k, GATES.get(gate_mode, gate_mode), d,
+        int(inter), ACTS.get(act, act), _ptr(w1), _ptr(s1), _ptr(w2), _ptr(s2), wt,
+        int(group_size), _ptr(addend), None if addend_ready is None else addend_ready.cuda_event,
+        _ptr(topk_ids), _ptr(topk_w), _ptr(out), _stream(stream)))
     return out, topk_ids, topk_w
 
 

@@ -2,6 +2,7 @@
 // Validation runs before any HIP call, so argument errors are reported (and nothing is
 // enqueued) even on a machine without a GPU.
 #include <atomic>
+#include <mutex>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -79,6 +80,35 @@ int32_t validate_gemm(const uint16_t* a, const int32_t* offsets, int32_t R, int3
         return MOE_ERR_INVALID;
     if (scales && !aligned(scales, 16)) return MOE_ERR_INVALID;
     return MOE_OK;
+}
+
+}  // namespace
+
+// Scratch memory of moe_decode_layer_noalloc: a workspace that lives in the code object, so the
+// call needs no allocation.  Each device that loads the library holds its own copy until the
+// process ends; host code reaches it only through the address hipGetSymbolAddress returns for
+// the current device (the array's name is a host-side stand-in, not a device address).
+static __device__ __align__(256) uint8_t scratch[MOE_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+std::atomic<void*> g_scratch_ptr[64];   // device address of `scratch`, per device id
+std::mutex g_scratch_mu;
+
+// Address of this device's `scratch`, looked up once per device (with that device current).
+void* scratch_address(int dev) {
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+    return ptr;
 }
 
 }  // namespace
@@ -308,6 +338,28 @@ int32_t moe_decode_layer(const float* logits, const uint8_t* active, const uint1
     a.out = out;
     a.ws = ws;
     return hip_status(moe::launch_decode(a, (hipStream_t)stream));
+}
+
+int32_t moe_decode_layer_noalloc(const float* logits, const uint8_t* active, const uint16_t* x,
+                                 int32_t T, int32_t E, int32_t k, int32_t gate_mode, int32_t d,
+                                 int32_t inter, int32_t act, const void* w1, const uint16_t* s1,
+                                 const void* w2, const uint16_t* s2, int32_t wtype,
+                                 int32_t group_size, const uint16_t* addend, void* addend_ready,
+                                 int32_t* topk_ids, float* topk_w, uint16_t* out, void* stream) {
+    if (int32_t st = validate_decode(T, E, k, gate_mode, d, inter, act, wtype, group_size))
+        return st;
+    if (T == 0) return MOE_OK;
+    const size_t need = moe::decode_workspace_layout(T, k, E, d, inter, wtype, nullptr, nullptr);
+    if (need > (size_t)MOE_DECODE_SCRATCH_BYTES) return MOE_ERR_UNSUPPORTED;
+    if (int32_t st = check_device()) return st;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_NO_DEVICE;
+    void* ws = scratch_address(dev);
+    if (!ws) return MOE_ERR_HIP;
+    // the rest is moe_decode_layer's validation and launch, on the scratch workspace
+    return moe_decode_layer(logits, active, x, T, E, k, gate_mode, d, inter, act, w1, s1, w2, s2,
+                            wtype, group_size, addend, addend_ready, topk_ids, topk_w, out, ws,
+                            (size_t)MOE_DECODE_SCRATCH_BYTES, stream);
 }
 
 int32_t moe_unpermute_combine(const uint16_t* y_perm, const int32_t* inv_perm, const float* topk_w,

@@ -333,6 +333,27 @@ def test_decode_layer_validation():
         assert f(*args(T=64, k=8, E=16, wsb=big)) == q.MOE_ERR_NO_DEVICE
 
 
+def test_decode_noalloc_rejects_a_step_beyond_its_scratch():
+    """moe_decode_layer_noalloc validates as moe_decode_layer, then refuses a step whose workspace
+    exceeds its scratch array, before touching a device."""
+    L = q.lib()
+    f = L.moe_decode_layer_noalloc
+    # 64 tokens x 8 experts x 6400 intermediate columns: 6.5 MB of hidden rows alone, plus the
+    # second GEMM's partial sums, over the array's 8 MiB
+    assert L.moe_decode_workspace_size(64, 8, 16, 4096, 6400, 0) > q.MOE_DECODE_SCRATCH_BYTES
+    args = [FAKE, None, FAKE, 64, 16, 8, 0, 4096, 6400, 2, FAKE, FAKE, FAKE, FAKE, 0, 128, None,
+            None, FAKE, FAKE, FAKE, None]
+    assert f(*args) == q.MOE_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[5] = 9                                             # k > MOE_MAX_TOPK
+    assert f(*bad) == q.MOE_ERR_INVALID
+    small = list(args)
+    small[3], small[8] = 4, 512                            # fits the array
+    assert L.moe_decode_workspace_size(4, 8, 16, 4096, 512, 0) <= q.MOE_DECODE_SCRATCH_BYTES
+    if not gpu_available():
+        assert f(*small) == q.MOE_ERR_NO_DEVICE
+
+
 def test_decode_workspace_size():
     L = q.lib()
     assert L.moe_decode_workspace_size(65, 1, 8, 256, 512, 0) == 0          # T too large
