@@ -57,6 +57,10 @@ def parse():
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 stream, 2 tile")
     ap.add_argument("--tile", type=int, default=0,
                     help="tile-path block tile: 0 auto, 1 64x256, 2 64x128, 3 128x128")
+    ap.add_argument("--i2f", default="trick", choices=["trick", "native"],
+                    help="int-to-float conversion of the codes in the tile GEMMs: the "
+                         "exponent-of-1024 construction (default) or the conversion "
+                         "instructions (the baseline it is measured against; MT encoder shape)")
     ap.add_argument("--rotate-gb", type=float, default=1.0,
                     help="cycle weight copies totalling at least this many GB (cold weights)")
     ap.add_argument("--no-fuse-rows", action="store_true",
@@ -272,7 +276,8 @@ def main():
     torch.cuda.set_device(dev)
     layer = q.DeviceLayer.from_inputs(inp, device=dev, gemm_path=args.path, gemm_tile=args.tile,
                                       fuse_rows=not args.no_fuse_rows,
-                                      decode=False if args.no_decode else None)
+                                      decode=False if args.no_decode else None,
+                                      gemm_i2f=q.I2FS[args.i2f])
     ws = layer.workspace(T)
     x = torch.from_numpy(inp.x).to(dev)
     logits = torch.from_numpy(inp.logits).to(dev)
@@ -352,7 +357,8 @@ def main():
     traffic = None
     src_hash = kernel_source_hash()
     workload = f"{cfg.name}_{args.wtype}_T{T}" + (f"_A{args.active}" if args.active else "") + \
-        (f"_fin{args.finished:g}" if args.finished else "")
+        (f"_fin{args.finished:g}" if args.finished else "") + \
+        ("_i2fnative" if args.i2f == "native" else "")
     if os.path.exists(TRAFFIC_FILE):
         try:
             rec = json.load(open(TRAFFIC_FILE)).get(workload, {})

@@ -83,8 +83,17 @@ typedef struct moe_gemm_opts {
                        /* 48-row tiles for per-channel scales and for experts with */
                        /* under ~96 rows, 64x256 for group scales beyond that,     */
                        /* 128-column tiles for 8-bit codes)                        */
-    int32_t reserved[5];
+    int32_t i2f;       /* enum moe_i2f: how codes become fp16 in the tile path      */
+    int32_t reserved[4];
 } moe_gemm_opts;
+
+/* Int-to-float conversion of the codes inside the GEMM ([W] section 3, optimized I2F).  Both give
+ * the same fp16 values, so the same results bit for bit; NATIVE is the baseline the exponent-of-
+ * 1024 construction is measured against.  NATIVE is built for the tile path with per-channel
+ * scales, ReLU or no activation (the MT encoder's two GEMMs), 4- or 8-bit codes and the 48x256,
+ * 48x128 and 64x128 tiles; other calls that ask for it get MOE_ERR_UNSUPPORTED. */
+enum moe_i2f   { MOE_I2F_TRICK = 0,           /* OR into the mantissa of 1024, subtract    */
+                 MOE_I2F_NATIVE = 1 };        /* byte-to-float conversion instructions     */
 
 /* Limits. */
 #define MOE_MAX_EXPERTS 256

@@ -19,7 +19,8 @@ __all__ = [
     "MOE_ERR_NO_DEVICE", "MOE_ERR_HIP",
     "GATE_TOPK", "GATE_ALL", "W_INT4", "W_INT8", "W_FP16", "ACT_NONE", "ACT_RELU",
     "ACT_SWIGLU", "PATH_AUTO", "PATH_STREAM", "PATH_TILE", "TILE_AUTO", "TILE_64x256",
-    "TILE_64x128", "TILE_128x128", "TILE_48x256", "TILE_48x128", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SPLIT_K",
+    "TILE_64x128", "TILE_128x128", "TILE_48x256", "TILE_48x128", "I2F_TRICK", "I2F_NATIVE",
+    "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SPLIT_K",
     "MoEError", "MoELibraryError", "lib", "lib_path", "status_str", "version",
     "moe_route_topk", "moe_route_topk_active", "moe_permute", "moe_grouped_gemm_wq",
     "moe_grouped_gemm_wq_rows",
@@ -39,6 +40,8 @@ W_INT4, W_INT8, W_FP16 = 0, 1, 2
 ACT_NONE, ACT_RELU, ACT_SWIGLU = 0, 1, 2
 PATH_AUTO, PATH_STREAM, PATH_TILE = 0, 1, 2
 TILE_AUTO, TILE_64x256, TILE_64x128, TILE_128x128, TILE_48x256, TILE_48x128 = 0, 1, 2, 3, 4, 5
+I2F_TRICK, I2F_NATIVE = 0, 1
+I2FS = {"trick": I2F_TRICK, "native": I2F_NATIVE}
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_SPLIT_K = 256, 8, 8
 MOE_DECODE_MAX_TOKENS, MOE_DECODE_MAX_ROWS = 64, 512
 MOE_DECODE_SCRATCH_BYTES = 8 << 20
@@ -72,7 +75,8 @@ class MoELibraryError(ImportError):
 
 class GemmOpts(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("split_k", ctypes.c_int32),
-                ("tile", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
+                ("tile", ctypes.c_int32), ("i2f", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 4)]
 
 
 _lib = None
@@ -196,11 +200,11 @@ def _need(t, dtype, name, numel=None):
         raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
 
 
-def _opts(path=PATH_AUTO, split_k=0, tile=TILE_AUTO):
-    if path == PATH_AUTO and split_k == 0 and tile == TILE_AUTO:
+def _opts(path=PATH_AUTO, split_k=0, tile=TILE_AUTO, i2f=I2F_TRICK):
+    if path == PATH_AUTO and split_k == 0 and tile == TILE_AUTO and i2f == I2F_TRICK:
         return None
     o = GemmOpts()
-    o.path, o.split_k, o.tile = int(path), int(split_k), int(tile)
+    o.path, o.split_k, o.tile, o.i2f = int(path), int(split_k), int(tile), int(i2f)
     return o
 
 
@@ -277,7 +281,7 @@ def moe_permute_workspace_size(T, k, E):
 
 def moe_grouped_gemm_wq(a, expert_offsets, E, K, N, w_packed, scales, wtype, group_size, act,
                         row_scale=None, out=None, path=PATH_AUTO, split_k=0, ws=None,
-                        stream=None, tile=TILE_AUTO):
+                        stream=None, tile=TILE_AUTO, i2f=I2F_TRICK):
     torch = _torch()
     R = a.shape[0]
     wt = WTYPES.get(wtype, wtype)
@@ -285,7 +289,7 @@ def moe_grouped_gemm_wq(a, expert_offsets, E, K, N, w_packed, scales, wtype, gro
     n_out = N // 2 if ac == ACT_SWIGLU else N
     if out is None:
         out = new_output((R, n_out), torch.float16, a.device)
-    o = _opts(path, split_k, tile)
+    o = _opts(path, split_k, tile, I2FS.get(i2f, i2f))
     need_ws = lib().moe_gemm_workspace_size(R, E, K, N, wt, ac, ctypes.byref(o) if o else None)
     if need_ws and ws is None:
         ws = torch.empty(need_ws, dtype=torch.uint8, device=a.device)
@@ -305,7 +309,8 @@ def moe_grouped_gemm_wq(a, expert_offsets, E, K, N, w_packed, scales, wtype, gro
 
 def moe_grouped_gemm_wq_rows(a, a_rows, a_row_div, expert_offsets, R, E, K, N, w_packed, scales,
                              wtype, group_size, act, row_scale=None, out=None, out_rows=None,
-                             path=PATH_AUTO, split_k=0, stream=None, tile=TILE_AUTO):
+                             path=PATH_AUTO, split_k=0, stream=None, tile=TILE_AUTO,
+                             i2f=I2F_TRICK):
     """GEMM row p reads a[a_rows[p] // a_row_div] (a[p] if a_rows is None) and writes
     out[out_rows[p]] (out[p] if out_rows is None); R = number of GEMM rows."""
     torch = _torch()
@@ -314,7 +319,7 @@ def moe_grouped_gemm_wq_rows(a, a_rows, a_row_div, expert_offsets, R, E, K, N, w
     n_out = N // 2 if ac == ACT_SWIGLU else N
     if out is None:
         out = new_output((R, n_out), torch.float16, a.device)
-    o = _opts(path, split_k, tile)
+    o = _opts(path, split_k, tile, I2FS.get(i2f, i2f))
     a_nrows = a.shape[0]
     out_nrows = out.shape[0]
     _need(a, torch.float16, "a", a_nrows * K)

@@ -71,6 +71,14 @@ int32_t validate_gemm(const uint16_t* a, const int32_t* offsets, int32_t R, int3
         if (opts->path < MOE_PATH_AUTO || opts->path > MOE_PATH_TILE) return MOE_ERR_INVALID;
         if (opts->split_k < 0 || opts->split_k > MOE_MAX_SPLIT_K) return MOE_ERR_INVALID;
         if (opts->tile < MOE_TILE_AUTO || opts->tile > MOE_TILE_48x128) return MOE_ERR_INVALID;
+        if (opts->i2f != MOE_I2F_TRICK && opts->i2f != MOE_I2F_NATIVE) return MOE_ERR_INVALID;
+        if (opts->i2f == MOE_I2F_NATIVE) {
+            // built for the tile path of the MT encoder shapes only
+            const int path = moe::gemm_choose_path(R, E, K, N, wtype, act, opts->path);
+            const int tile = moe::gemm_choose_tile(R, E, N, act, wtype, group != 0, opts->tile);
+            if (path != MOE_PATH_TILE || !moe::gemm_native_supported(wtype, act, group, tile))
+                return MOE_ERR_UNSUPPORTED;
+        }
     }
     if ((int64_t)R * K >= (int64_t)1 << 40) return MOE_ERR_UNSUPPORTED;
     if (R == 0) return MOE_OK;
@@ -237,6 +245,7 @@ static int32_t grouped_gemm(const uint16_t* a, int32_t a_nrows, const int32_t* a
     p.act = act;
     p.split = pl.split;
     p.tile = opts ? opts->tile : MOE_TILE_AUTO;
+    p.i2f = opts ? opts->i2f : MOE_I2F_TRICK;
     p.tiles16 = nullptr;
     hipStream_t s = (hipStream_t)stream;
     return hip_status(pl.path == MOE_PATH_TILE ? moe::launch_gemm_tile(p, s)

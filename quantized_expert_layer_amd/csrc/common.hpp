@@ -85,6 +85,35 @@ __device__ __forceinline__ void i2f_int8(uint32_t w, f16x2 out[2]) {
     out[1] = as_f16x2(__builtin_amdgcn_perm(0x64646464u, w, 0x05030402u)) - sub;  // [e2,e3]
 }
 
+// The same codes through the conversion instructions instead (the baseline of the construction
+// above): each byte of a word becomes fp32 with v_cvt_f32_ubyte0..3, two values are packed to
+// fp16 (the integers below 256 are exact, so the rounding mode does not matter), and the
+// storage offset is subtracted.  4-bit codes first split the word into its low and high
+// nibbles (w & 0x0F0F0F0F, (w >> 4) & 0x0F0F0F0F): byte b of the low part is nibble 2b, of the
+// high part nibble 2b + 1, which by the nibble order [e0,e2,e4,e6,e1,e3,e5,e7] hold
+// e0 e4 e1 e5 and e2 e6 e3 e7.
+__device__ __forceinline__ f16x2 cvt_pair(float a, float b) {
+    return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+// byte b of w as fp32 (the backend selects v_cvt_f32_ubyte<b> for this pattern)
+template <int B>
+__device__ __forceinline__ float ubyte_f32(uint32_t w) {
+    return (float)((w >> (8 * B)) & 0xFFu);
+}
+__device__ __forceinline__ void i2f_int4_native(uint32_t w, f16x2 out[4]) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const f16x2 off = {(f16)8.0f, (f16)8.0f};
+    out[0] = cvt_pair(ubyte_f32<0>(lo), ubyte_f32<2>(lo)) - off;    // [e0, e1]
+    out[1] = cvt_pair(ubyte_f32<0>(hi), ubyte_f32<2>(hi)) - off;    // [e2, e3]
+    out[2] = cvt_pair(ubyte_f32<1>(lo), ubyte_f32<3>(lo)) - off;    // [e4, e5]
+    out[3] = cvt_pair(ubyte_f32<1>(hi), ubyte_f32<3>(hi)) - off;    // [e6, e7]
+}
+__device__ __forceinline__ void i2f_int8_native(uint32_t w, f16x2 out[2]) {
+    const f16x2 off = {(f16)128.0f, (f16)128.0f};
+    out[0] = cvt_pair(ubyte_f32<0>(w), ubyte_f32<1>(w)) - off;      // [e0, e1]
+    out[1] = cvt_pair(ubyte_f32<2>(w), ubyte_f32<3>(w)) - off;      // [e2, e3]
+}
+
 __device__ __forceinline__ f16x8 pack8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
     f16x8 r;
     r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
@@ -97,15 +126,21 @@ __device__ __forceinline__ f16x8 pack8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
 // Group scales (group 128) are folded in by one fp16 multiply, giving exactly Algorithm 1's
 // fp16 weight; per-channel scales are applied to the fp32 result instead.
 // ------------------------------------------------------------------------------------
-template <int WT, bool SCALE>
+template <int WT, bool SCALE, bool NATIVE = false>
 __device__ __forceinline__ f16x8 weight_frag(const u32x4& raw, int j, f16x2 s2,
                                              const I2F4Consts& k4) {
     f16x2 q[4];
     if constexpr (WT == MOE_W_INT4) {
-        i2f_int4(raw[j], q, k4);
+        if constexpr (NATIVE) i2f_int4_native(raw[j], q);
+        else i2f_int4(raw[j], q, k4);
     } else if constexpr (WT == MOE_W_INT8) {
-        i2f_int8(raw[2 * j], q);
-        i2f_int8(raw[2 * j + 1], q + 2);
+        if constexpr (NATIVE) {
+            i2f_int8_native(raw[2 * j], q);
+            i2f_int8_native(raw[2 * j + 1], q + 2);
+        } else {
+            i2f_int8(raw[2 * j], q);
+            i2f_int8(raw[2 * j + 1], q + 2);
+        }
     } else {
         return __builtin_bit_cast(f16x8, raw);
     }

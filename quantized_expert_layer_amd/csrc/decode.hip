@@ -446,6 +446,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     g.act = a.act;
     g.split = gemm_choose_split(R, a.E, a.d, n1, a.wtype, a.act, 0);
     g.tile = 0;
+    g.i2f = MOE_I2F_TRICK;
     g.tiles16 = ws.tiles;
     err = launch_gemm_stream(g, stream);
     if (err != hipSuccess) return err;

@@ -339,7 +339,7 @@ __device__ __forceinline__ void tie_to_wait(T& v) {
 // KG > 1 (fp16 weights only): the block holds KG groups of 4 waves; group g runs the K stages
 // [g * n, (g + 1) * n) of the tile with its own A buffers, and groups 1..KG-1 hand their fp32
 // partial tiles to group 0 through LDS, which adds them in group order and writes the tile.
-template <int WT, int ACT, bool GROUPED, int MA, int NS, int BM, int KG = 1>
+template <int WT, int ACT, bool GROUPED, int MA, int NS, int BM, int KG = 1, bool NATIVE = false>
 __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__ lds, int e,
                                           int row0, int rows, int cbg) {
     constexpr int KSB = WTraits<WT>::KSB;
@@ -500,7 +500,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
             for (int c = 0; c < NS; ++c) {
                 const f16 sv = __builtin_bit_cast(f16, (uint16_t)scur[c][GROUPED ? ks / KSPS : 0]);
                 const f16x2 s2 = {sv, sv};
-                bq[c] = weight_frag<WT, GROUPED>(bcur[c][ks / KSPS], ks % KSPS, s2, k4);
+                bq[c] = weight_frag<WT, GROUPED, NATIVE>(bcur[c][ks / KSPS], ks % KSPS, s2, k4);
             }
         };
         f16x8 bq[NS];
@@ -701,7 +701,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
     }
 }
 
-template <int WT, int ACT, bool GROUPED, int MS, int NS, int KG>
+template <int WT, int ACT, bool GROUPED, int MS, int NS, int KG, bool NATIVE = false>
 __global__ __launch_bounds__(256 * KG, (KG == 1 && MS < 8) ? 2 : 1) void gemm_tile_kernel(GemmParams p, int ncbg, int mt_ub,
                                                            int grid_real, int a_major) {
     constexpr int BM = 16 * MS;
@@ -748,16 +748,16 @@ __global__ __launch_bounds__(256 * KG, (KG == 1 && MS < 8) ? 2 : 1) void gemm_ti
     // body specialised for the tile's number of 16-row subtiles (1, 2, 3, 4; 5-6 as 6; MS)
     static_assert(MS >= 3, "the subtile cases below assume tiles of at least 48 rows");
     switch ((rows + 15) / 16) {
-        case 1: tile_body<WT, ACT, GROUPED, 1, NS, BM, KG>(p, lds, e, row0, rows, cbg); break;
-        case 2: tile_body<WT, ACT, GROUPED, 2, NS, BM, KG>(p, lds, e, row0, rows, cbg); break;
-        case 3: tile_body<WT, ACT, GROUPED, 3, NS, BM, KG>(p, lds, e, row0, rows, cbg); break;
+        case 1: tile_body<WT, ACT, GROUPED, 1, NS, BM, KG, NATIVE>(p, lds, e, row0, rows, cbg); break;
+        case 2: tile_body<WT, ACT, GROUPED, 2, NS, BM, KG, NATIVE>(p, lds, e, row0, rows, cbg); break;
+        case 3: tile_body<WT, ACT, GROUPED, 3, NS, BM, KG, NATIVE>(p, lds, e, row0, rows, cbg); break;
         case 4:
-            tile_body<WT, ACT, GROUPED, (MS >= 4 ? 4 : MS), NS, BM, KG>(p, lds, e, row0, rows, cbg);
+            tile_body<WT, ACT, GROUPED, (MS >= 4 ? 4 : MS), NS, BM, KG, NATIVE>(p, lds, e, row0, rows, cbg);
             break;
         case 5: case 6:
-            tile_body<WT, ACT, GROUPED, (MS >= 6 ? 6 : MS), NS, BM, KG>(p, lds, e, row0, rows, cbg);
+            tile_body<WT, ACT, GROUPED, (MS >= 6 ? 6 : MS), NS, BM, KG, NATIVE>(p, lds, e, row0, rows, cbg);
             break;
-        default: tile_body<WT, ACT, GROUPED, MS, NS, BM, KG>(p, lds, e, row0, rows, cbg); break;
+        default: tile_body<WT, ACT, GROUPED, MS, NS, BM, KG, NATIVE>(p, lds, e, row0, rows, cbg); break;
     }
 }
 
@@ -843,6 +843,18 @@ static hipError_t stream_dispatch(const GemmParams& p, hipStream_t stream) {
     return stream_launch<WT, ACT, GROUPED, 1>(p, ngo, blocks, stream);
 }
 
+// Tile kernels built with the native int-to-float conversion as well: integer codes, per-channel
+// scales, ReLU or no activation, and the tiles gemm_choose_tile picks for those (48x256, 48x128,
+// 64x128).
+template <int WT, int ACT, bool GROUPED, int MS, int NS>
+constexpr bool kNativeTile = WT != MOE_W_FP16 && ACT != MOE_ACT_SWIGLU && !GROUPED &&
+                             ((MS == 3 && (NS == 4 || NS == 2)) || (MS == 4 && NS == 2));
+
+bool gemm_native_supported(int wtype, int act, int group, int tile) {
+    return wtype != MOE_W_FP16 && act != MOE_ACT_SWIGLU && group == 0 &&
+           (tile == MOE_TILE_48x256 || tile == MOE_TILE_48x128 || tile == MOE_TILE_64x128);
+}
+
 template <int WT, int ACT, bool GROUPED, int MS, int NS>
 static hipError_t tile_launch(const GemmParams& p, hipStream_t stream) {
     constexpr int BM = 16 * MS;
@@ -885,6 +897,13 @@ static hipError_t tile_launch(const GemmParams& p, hipStream_t stream) {
         if constexpr (WT == MOE_W_FP16 && kFit2)
             gemm_tile_kernel<WT, ACT, GROUPED, MS, NS, 2><<<(unsigned)grid, 512, 0, stream>>>(
                 p, ncbg, mt_ub, (int)real, a_major);
+    } else if (p.i2f == MOE_I2F_NATIVE) {
+        // the conversion-instruction baseline: MT encoder shapes only (per-channel scales, no SwiGLU)
+        if constexpr (kNativeTile<WT, ACT, GROUPED, MS, NS>)
+            gemm_tile_kernel<WT, ACT, GROUPED, MS, NS, 1, true><<<(unsigned)grid, 256, 0, stream>>>(
+                p, ncbg, mt_ub, (int)real, a_major);
+        else
+            return hipErrorInvalidValue;
     } else {
         gemm_tile_kernel<WT, ACT, GROUPED, MS, NS, 1><<<(unsigned)grid, 256, 0, stream>>>(
             p, ncbg, mt_ub, (int)real, a_major);

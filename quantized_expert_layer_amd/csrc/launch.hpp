@@ -51,6 +51,7 @@ struct GemmParams {
     int wtype, group, act;
     int split;           // stream path: waves per block splitting K (1..MOE_MAX_SPLIT_K)
     int tile;            // enum moe_tile (0 = automatic)
+    int i2f;             // enum moe_i2f
     const int32_t* tiles16;  // stream path: NULL, or the decode tile table (16-row m-tiles)
 };
 
@@ -58,6 +59,8 @@ struct GemmParams {
 int gemm_choose_path(int R, int E, int K, int N, int wtype, int act, int forced);
 int gemm_choose_split(int R, int E, int K, int N, int wtype, int act, int forced);
 int gemm_choose_tile(int R, int E, int N, int act, int wtype, bool grouped, int forced);
+// Whether the native int-to-float conversion is built for this call (tile path).
+bool gemm_native_supported(int wtype, int act, int group, int tile);
 
 hipError_t launch_gemm_stream(const GemmParams& p, hipStream_t stream);
 hipError_t launch_gemm_tile(const GemmParams& p, hipStream_t stream);

@@ -40,7 +40,7 @@ class DeviceLayer:
                  gate_mode: str, codes1: np.ndarray, scales1: np.ndarray, codes2: np.ndarray,
                  scales2: np.ndarray, shared: Optional[List[Tuple[np.ndarray, np.ndarray]]] = None,
                  device: str = "cuda", gemm_path: int = 0, gemm_tile: int = 0,
-                 fuse_rows: bool = True, decode: Optional[bool] = None):
+                 fuse_rows: bool = True, decode: Optional[bool] = None, gemm_i2f: int = 0):
         import torch
         self.E, self.k, self.d, self.inter = E, k, d, inter
         self.act, self.wtype, self.group, self.gate_mode = act, wtype, group, gate_mode
@@ -48,6 +48,9 @@ class DeviceLayer:
         self.device = torch.device(device)
         self.gemm_path = gemm_path
         self.gemm_tile = gemm_tile
+        # int-to-float conversion of the routed GEMMs (0: exponent-of-1024 construction,
+        # 1: conversion instructions, the baseline it is measured against)
+        self.gemm_i2f = gemm_i2f
         # fuse_rows: the first GEMM reads x through perm (no x_perm copy), and with k = 1 the
         # second GEMM writes the output rows through perm (no combine launch)
         self.fuse_rows = fuse_rows
@@ -75,13 +78,13 @@ class DeviceLayer:
 
     @classmethod
     def from_inputs(cls, inp, device="cuda", gemm_path=0, gemm_tile=0, fuse_rows=True,
-                    decode=None):
+                    decode=None, gemm_i2f=0):
         c = inp.cfg
         return cls(E=c.E, k=c.k, d=c.d, inter=c.inter, act=c.act, wtype=inp.wtype,
                    group=c.group, gate_mode=c.gate_mode, codes1=inp.codes1,
                    scales1=inp.scales1, codes2=inp.codes2, scales2=inp.scales2,
                    shared=inp.shared or None, device=device, gemm_path=gemm_path,
-                   gemm_tile=gemm_tile, fuse_rows=fuse_rows, decode=decode)
+                   gemm_tile=gemm_tile, fuse_rows=fuse_rows, decode=decode, gemm_i2f=gemm_i2f)
 
     def uses_decode(self, T: int, gate_in_gemm: bool = True) -> bool:
         """Whether a step of T tokens runs as one moe_decode_layer call."""
@@ -92,7 +95,7 @@ class DeviceLayer:
                 raise ValueError(f"moe_decode_layer does not take T={T}, k={self.k}")
             return True
         return (self.decode is None and fits and self.gemm_path == 0 and self.gemm_tile == 0
-                and self.fuse_rows and gate_in_gemm)
+                and self.gemm_i2f == 0 and self.fuse_rows and gate_in_gemm)
 
     def _scatter_out(self, gate_in_gemm: bool, pruned: bool = False) -> bool:
         """Whether the second GEMM writes the layer output itself: one expert per token, the
@@ -185,21 +188,23 @@ class DeviceLayer:
         if fused:
             moe_grouped_gemm_wq_rows(x, b["perm"], self.k, b["off"], R, self.E, self.d, self.n1,
                                      self.w1, self.s1, self.wtype, self.group, self.act,
-                                     out=b["h"], path=path, stream=stream, tile=self.gemm_tile)
+                                     out=b["h"], path=path, stream=stream, tile=self.gemm_tile,
+                                     i2f=self.gemm_i2f)
         else:
             moe_grouped_gemm_wq(b["xp"], b["off"], self.E, self.d, self.n1, self.w1, self.s1,
                                 self.wtype, self.group, self.act, out=b["h"], path=path,
-                                ws=b["ws"], stream=stream, tile=self.gemm_tile)
+                                ws=b["ws"], stream=stream, tile=self.gemm_tile, i2f=self.gemm_i2f)
         rs = b["wp"] if gate_in_gemm else None
         if scatter:
             moe_grouped_gemm_wq_rows(b["h"], None, 1, b["off"], R, self.E, self.inter, self.d,
                                      self.w2, self.s2, self.wtype, self.group, "none",
                                      row_scale=rs, out=b["out"], out_rows=b["perm"], path=path,
-                                     stream=stream, tile=self.gemm_tile)
+                                     stream=stream, tile=self.gemm_tile, i2f=self.gemm_i2f)
             return b["out"]
         moe_grouped_gemm_wq(b["h"], b["off"], self.E, self.inter, self.d, self.w2, self.s2,
                             self.wtype, self.group, "none", row_scale=rs, out=b["y"],
-                            path=path, ws=b["ws"], stream=stream, tile=self.gemm_tile)
+                            path=path, ws=b["ws"], stream=stream, tile=self.gemm_tile,
+                            i2f=self.gemm_i2f)
         addend = None
         if self.shared is not None:
             moe_grouped_gemm_wq(x, b["sh_off"], 1, self.d, 2 * self.shared_inter,
@@ -224,11 +229,12 @@ class DeviceLayer:
         st = _stream(stream)
         path = self.gemm_path
         opts = None
-        if path or self.gemm_tile:
+        if path or self.gemm_tile or self.gemm_i2f:
             from . import GemmOpts
             opts = GemmOpts()
             opts.path = path
             opts.tile = self.gemm_tile
+            opts.i2f = self.gemm_i2f
         ob = ctypes.byref(opts) if opts is not None else None
         wsp, wsn = _ptr(b["ws"]), b["ws"].numel()
         wt, ac = WTYPES[self.wtype], ACTS[self.act]

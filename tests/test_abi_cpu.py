@@ -213,6 +213,23 @@ def test_gemm_validation():
     assert g(*_gemm_args(opts=ctypes.byref(o))) == q.MOE_ERR_INVALID
     o.split_k = -1
     assert g(*_gemm_args(opts=ctypes.byref(o))) == q.MOE_ERR_INVALID
+    # the int-to-float choice: 0 or 1; the conversion-instruction kernels exist for the tile
+    # path with per-channel scales, ReLU or no activation and the 48-row / 64x128 tiles
+    o.path, o.split_k, o.i2f = q.PATH_TILE, 0, 2
+    assert g(*_gemm_args(opts=ctypes.byref(o))) == q.MOE_ERR_INVALID
+    o.i2f = -1
+    assert g(*_gemm_args(opts=ctypes.byref(o))) == q.MOE_ERR_INVALID
+    o.i2f, o.tile = q.I2F_NATIVE, q.TILE_48x256
+    for kw in (dict(g=128), dict(act=2), dict(wt=2, g=0, s=None)):
+        assert g(*_gemm_args(opts=ctypes.byref(o), **kw)) == q.MOE_ERR_UNSUPPORTED, kw
+    for t in (q.TILE_64x256, q.TILE_128x128):
+        o.tile = t
+        assert g(*_gemm_args(g=0, opts=ctypes.byref(o))) == q.MOE_ERR_UNSUPPORTED, t
+    o.path, o.tile = q.PATH_STREAM, q.TILE_AUTO
+    assert g(*_gemm_args(g=0, opts=ctypes.byref(o))) == q.MOE_ERR_UNSUPPORTED
+    o.path, o.tile = q.PATH_TILE, q.TILE_48x128
+    assert g(*_gemm_args(g=0, R=0, a=None, out=None, opts=ctypes.byref(o))) == q.MOE_OK
+    o.i2f, o.tile = q.I2F_TRICK, q.TILE_AUTO
     # the K split happens inside a block: no path needs a workspace
     for path in (q.PATH_AUTO, q.PATH_STREAM, q.PATH_TILE):
         for split in (0, 1, q.MOE_MAX_SPLIT_K):

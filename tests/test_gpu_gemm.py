@@ -136,6 +136,37 @@ def test_grouped_gemm_matches_oracle(E, K, N, wtype, group, T, k, act, path, til
     assert_layer_close(host(out), ref, "grouped gemm")
 
 
+NATIVE_TILES = [q.TILE_48x256, q.TILE_48x128, q.TILE_64x128]
+
+
+@pytest.mark.parametrize("tile", NATIVE_TILES)
+@pytest.mark.parametrize("wtype", ["int4", "int8"])
+def test_native_i2f_equals_exponent_construction(wtype, tile):
+    # [W] section 3 (optimized I2F): the exponent-of-1024 construction and the conversion
+    # instructions give the same fp16 code values, so the GEMMs agree bit for bit; both against
+    # the oracle.  Expert row counts: SUBTILE_COUNTS (every subtile body, ragged tails, an empty
+    # expert); per-channel scales, the MT encoder's ReLU GEMM and its gate-weighted second GEMM.
+    E, K, N = len(SUBTILE_COUNTS), 512, 256
+    counts = np.array(SUBTILE_COUNTS)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(off[-1])
+    rng = np.random.default_rng(21)
+    a = rng.standard_normal((R, K)).astype(np.float16)
+    rs = rng.random(R, dtype=np.float32)
+    codes, scales = synth.gen.make_expert_weights(E, K, N, wtype, 0, seed=23, coverage=True)
+    wdq = oracle.dequant_algorithm1(codes, scales, 0)
+    w = dev(q.moe_pack_wq(codes, wtype))
+    for act, row_scale in (("relu", None), ("none", rs)):
+        case(f"native i2f {wtype} tile={tile} act={act}")
+        outs = [host(q.moe_grouped_gemm_wq(dev(a), dev(off), E, K, N, w, dev(scales), wtype, 0,
+                                           act, row_scale=None if row_scale is None else
+                                           dev(row_scale), path=q.PATH_TILE, tile=tile, i2f=i2f))
+                for i2f in ("trick", "native")]
+        assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16))
+        ref = oracle.grouped_gemm(a, off, wdq, act, row_scale=row_scale)
+        assert_layer_close(outs[1], ref, "native i2f gemm")
+
+
 @pytest.mark.parametrize("split", [2, 3, 4, 5, 8])
 def test_stream_split_k_matches_oracle_and_unsplit(split):
     # K = 2048 is 16 int4 super-blocks: splits 3 and 5 leave a short last slice, 8 gives

@@ -39,15 +39,43 @@ LAYER_CASES = [
     ("dsv2_lite", 288, None, 0, None),
     ("phi35_moe", 1, None, 0, None),
     ("phi35_moe", 17, None, 0, None),
-    ("phi35_moe", 8192, None, 0, 24),
+    ("phi35_moe", 8192, None, 0, 256),
+    # the active-expert sweep of the MT encoder ([W] section 4, tokens spread over A experts)
+    ("mt_encoder", 3840, "int4", 4, 512),
+    ("mt_encoder", 3840, "int4", 16, 512),
+    ("mt_encoder", 3840, "int4", 24, 512),
 ]
 
 
-def _tokens(T, n):
+def _edge_rows(inp):
+    """Tokens behind the rows at every expert's tile edges in the sorted order: each expert's
+    first and last row, and the first row of its last (ragged) tile and the row before it, for
+    the 48- and 64-row tiles.  Routing and sort are the oracle's."""
+    k = inp.cfg.k
+    ids, _ = oracle.topk_route(inp.logits, k, inp.cfg.gate_mode)
+    perm, _, off = oracle.stable_expert_sort(ids, inp.cfg.E)
+    rows = []
+    for e in range(inp.cfg.E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        rows += [lo, hi - 1]
+        for bm in (48, 64):
+            last = lo + (hi - lo - 1) // bm * bm
+            rows += [last, max(lo, last - 1)]
+    return np.unique(perm[np.array(rows)] // k)
+
+
+def _tokens(T, n, inp=None):
+    """All T tokens (n None), else n of them: token 0 and T - 1, the tile-edge rows' tokens
+    (with inp) and seeded random others."""
     if n is None or n >= T:
         return np.arange(T)
     rng = np.random.default_rng(T)
-    return np.unique(np.concatenate([[0, T - 1], rng.choice(T, n - 2, replace=False)]))
+    must = np.unique(np.concatenate([[0, T - 1]] + ([_edge_rows(inp)] if inp is not None else [])))
+    rest = np.setdiff1d(np.arange(T), must)
+    extra = rng.choice(rest, max(0, n - must.size), replace=False)
+    return np.unique(np.concatenate([must, extra]))
 
 
 @pytest.mark.parametrize("name,T,wtype,active,n_check", LAYER_CASES)
@@ -55,7 +83,7 @@ def test_layer_matches_oracle(name, T, wtype, active, n_check):
     inp, layer = _layer(name, T, wtype, active)
     case(f"layer {name} T={T} wtype={inp.wtype} active={active}")
     out = host(layer.forward(dev(inp.x), dev(inp.logits)))
-    toks = _tokens(T, n_check)
+    toks = _tokens(T, n_check, inp)
     ref = oracle.moe_layer_tokens(inp, toks)
     rel, mx = assert_layer_close(out[toks], ref, f"{name} T={T}")
     print(f"[gpu-case] {name} T={T}: rel-L2 {rel:.2e} max/rms {mx:.2e}", flush=True)
@@ -89,6 +117,20 @@ def test_layer_row_fusion_is_bit_identical_to_the_copies(fuse):
     case(f"row fusion {fuse} {name} T={T}")
     got = host(layer.forward(x, L))
     layer.fuse_rows = True
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("wtype", ["int4", "int8"])
+def test_layer_native_i2f_is_bit_identical(wtype):
+    """The MT encoder layer with the tile GEMMs converting codes by the conversion instructions
+    ([W] section 3, the baseline of the optimized I2F) gives the default layer's output bit for
+    bit."""
+    inp, layer = _layer("mt_encoder", 3840, wtype, 0)
+    native = q.DeviceLayer.from_inputs(inp, gemm_i2f=q.I2F_NATIVE)
+    x, L = dev(inp.x), dev(inp.logits)
+    case(f"layer native i2f mt_encoder T=3840 {wtype}")
+    want = host(layer.forward(x, L)).copy()
+    got = host(native.forward(x, L))
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
 
 
@@ -131,7 +173,7 @@ def test_plan_outlives_its_layer(name, T):
 
 
 @pytest.mark.parametrize("name,T,n_check", [("mt_encoder", 3840, 64), ("qwen15_moe", 544, 64),
-                                            ("dsv2_lite", 288, 64), ("phi35_moe", 8192, 16)])
+                                            ("dsv2_lite", 288, 64), ("phi35_moe", 8192, 256)])
 def test_layer_replays_from_a_graph(name, T, n_check):
     """The step the bench times: the layer plan captured once in a HIP graph and replayed with
     eager work in between.  Every replay gives the eager output bit for bit, and sampled tokens
@@ -157,5 +199,5 @@ def test_layer_replays_from_a_graph(name, T, n_check):
         # eager work on other inputs between the replays
         layer.forward(dev(inp.x[::-1].copy()), dev(inp.logits[::-1].copy()), ws=ws)
         torch.cuda.synchronize()
-    toks = _tokens(T, n_check)
+    toks = _tokens(T, n_check, inp)
     assert_layer_close(got[toks], oracle.moe_layer_tokens(inp, toks), f"graph {name} T={T}")
