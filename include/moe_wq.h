@@ -91,7 +91,7 @@ typedef struct moe_gemm_opts {
  * the same fp16 values, so the same results bit for bit; NATIVE is the baseline the exponent-of-
  * 1024 construction is measured against.  NATIVE is built for the tile path with per-channel
  * scales, ReLU or no activation (the MT encoder's two GEMMs), 4- or 8-bit codes and the 48x256,
- * 48x128 and 64x128 tiles; other calls that ask for it get MOE_ERR_UNSUPPORTED. */
+ * 48x128, 64x128 and 64x256 tiles; other calls that ask for it get MOE_ERR_UNSUPPORTED. */
 enum moe_i2f   { MOE_I2F_TRICK = 0,           /* OR into the mantissa of 1024, subtract    */
                  MOE_I2F_NATIVE = 1 };        /* byte-to-float conversion instructions     */
 

@@ -701,8 +701,17 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
     }
 }
 
+// Blocks per CU the tile kernel is built for: two (one for 128-row tiles), three for the 64x256
+// tile with 4-bit codes and per-channel scales, whose body fits the 168 registers of three waves
+// per SIMD without spilling (with the exponent-of-1024 conversion; the conversion instructions
+// need more and keep two).
+template <int WT, bool GROUPED, int MS, int NS, int KG, bool NATIVE> constexpr int tile_min_blocks() {
+    if (KG != 1 || MS >= 8) return 1;
+    return (MS == 4 && NS == 4 && WT == MOE_W_INT4 && !GROUPED && !NATIVE) ? 3 : 2;
+}
+
 template <int WT, int ACT, bool GROUPED, int MS, int NS, int KG, bool NATIVE = false>
-__global__ __launch_bounds__(256 * KG, (KG == 1 && MS < 8) ? 2 : 1) void gemm_tile_kernel(GemmParams p, int ncbg, int mt_ub,
+__global__ __launch_bounds__(256 * KG, (tile_min_blocks<WT, GROUPED, MS, NS, KG, NATIVE>())) void gemm_tile_kernel(GemmParams p, int ncbg, int mt_ub,
                                                            int grid_real, int a_major) {
     constexpr int BM = 16 * MS;
     // the A ring starts the block's LDS (its DMA writes stay aligned); 16 bytes after the body's
@@ -845,14 +854,15 @@ static hipError_t stream_dispatch(const GemmParams& p, hipStream_t stream) {
 
 // Tile kernels built with the native int-to-float conversion as well: integer codes, per-channel
 // scales, ReLU or no activation, and the tiles gemm_choose_tile picks for those (48x256, 48x128,
-// 64x128).
+// 64x128, 64x256).
 template <int WT, int ACT, bool GROUPED, int MS, int NS>
 constexpr bool kNativeTile = WT != MOE_W_FP16 && ACT != MOE_ACT_SWIGLU && !GROUPED &&
-                             ((MS == 3 && (NS == 4 || NS == 2)) || (MS == 4 && NS == 2));
+                             ((MS == 3 && (NS == 4 || NS == 2)) || (MS == 4 && (NS == 2 || NS == 4)));
 
 bool gemm_native_supported(int wtype, int act, int group, int tile) {
     return wtype != MOE_W_FP16 && act != MOE_ACT_SWIGLU && group == 0 &&
-           (tile == MOE_TILE_48x256 || tile == MOE_TILE_48x128 || tile == MOE_TILE_64x128);
+           (tile == MOE_TILE_48x256 || tile == MOE_TILE_48x128 || tile == MOE_TILE_64x128 ||
+            tile == MOE_TILE_64x256);
 }
 
 template <int WT, int ACT, bool GROUPED, int MS, int NS>
@@ -914,8 +924,9 @@ static hipError_t tile_launch(const GemmParams& p, hipStream_t stream) {
 // Block tile of the tile path.  Measured on the layer shapes here (rotated weights, one GEMM per
 // call): with integer codes, 48-row tiles beat 64-row ones wherever experts hold few rows (fewer
 // padded rows in each expert's last tile, and about two full rounds of blocks instead of one and a
-// half) and for per-channel scales at every size; 64x256 stays ahead for group scales once an
-// expert holds about 96 rows or more.  8-bit codes keep to 128-column tiles (their 256-column
+// half); 64x256 stays ahead for group scales once an expert holds about 96 rows or more, and for
+// per-channel scales on grids of 1.5 rounds or more of its three blocks per CU (the MT encoder's
+// first GEMM: 49 against 53 us; its second GEMM, with a quarter of the columns, stays at 48 rows).  8-bit codes keep to 128-column tiles (their 256-column
 // bodies hold too many registers for three waves per SIMD).  fp16 weights: 64x256 when there are
 // blocks for four per CU, else 64x128.  128x128 is only used when asked for.
 int gemm_choose_tile(int R, int E, int N, int act, int wtype, bool grouped, int forced) {
@@ -934,6 +945,9 @@ int gemm_choose_tile(int R, int E, int N, int act, int wtype, bool grouped, int 
         return blocks_wide >= 4L * 256 ? MOE_TILE_48x128 : MOE_TILE_64x128;
     }
     if (grouped && rows_per_expert >= 96.0) return MOE_TILE_64x256;
+    // per-channel scales: the 64x256 body runs three blocks per CU; it takes a grid of at least
+    // one and a half rounds of those (3 x 256 CUs) for its four-subtile dequantization to pay
+    if (!grouped && groups_wide * (cdiv(R, 64) + active / 2) >= 3L * 256 * 3 / 2) return MOE_TILE_64x256;
     const long blocks_48 = groups_wide * (cdiv(R, 48) + active / 2);
     return blocks_48 >= 256 ? MOE_TILE_48x256 : MOE_TILE_48x128;
 }

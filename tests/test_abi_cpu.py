@@ -222,7 +222,7 @@ def test_gemm_validation():
     o.i2f, o.tile = q.I2F_NATIVE, q.TILE_48x256
     for kw in (dict(g=128), dict(act=2), dict(wt=2, g=0, s=None)):
         assert g(*_gemm_args(opts=ctypes.byref(o), **kw)) == q.MOE_ERR_UNSUPPORTED, kw
-    for t in (q.TILE_64x256, q.TILE_128x128):
+    for t in (q.TILE_128x128,):
         o.tile = t
         assert g(*_gemm_args(g=0, opts=ctypes.byref(o))) == q.MOE_ERR_UNSUPPORTED, t
     o.path, o.tile = q.PATH_STREAM, q.TILE_AUTO

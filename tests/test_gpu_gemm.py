@@ -136,7 +136,7 @@ def test_grouped_gemm_matches_oracle(E, K, N, wtype, group, T, k, act, path, til
     assert_layer_close(host(out), ref, "grouped gemm")
 
 
-NATIVE_TILES = [q.TILE_48x256, q.TILE_48x128, q.TILE_64x128]
+NATIVE_TILES = [q.TILE_48x256, q.TILE_48x128, q.TILE_64x128, q.TILE_64x256]
 
 
 @pytest.mark.parametrize("tile", NATIVE_TILES)
