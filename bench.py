@@ -84,6 +84,9 @@ def parse():
     ap.add_argument("--elb-steps", type=int, default=16)
     ap.add_argument("--elb-m", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the per-configuration block (graph step and dominant-kernel "
+                         "roofline of the other layer shapes) of the default line")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-graph", action="store_true",
                     help="report the eager launches (one ctypes call per kernel) as the value "
@@ -251,27 +254,10 @@ def bench_bf16(args, q, torch, np, synth):
                    "copies_rotated": n_copies}}), flush=True)
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this layer build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-
-    import quantized_expert_layer_amd as q
-    import synth
-
-    if args.workload in ("elb", "bf16"):
-        torch.cuda.set_device(torch.device("cuda:0"))
-        (bench_elb if args.workload == "elb" else bench_bf16)(args, q, torch, np, synth)
-        return
-    cfg = synth.get_config(args.config)
-    T = args.T or cfg.T_list[0]
-    inp = synth.make_inputs(cfg, T, wtype=args.wtype, active=args.active)
+def measure_layer(args, q, torch, np, synth, cfg, T, wtype, active_n, steps, warmup, att):
+    """One layer configuration: eager per-call times (HIP events on the launch stream), the
+    dominant kernel's roofline, and the HIP-graph replayed step.  Returns (result, inputs)."""
+    inp = synth.make_inputs(cfg, T, wtype=wtype, active=active_n)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     layer = q.DeviceLayer.from_inputs(inp, device=dev, gemm_path=args.path, gemm_tile=args.tile,
@@ -303,11 +289,11 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         plans[i % n_copies].run()
     torch.cuda.synchronize()
 
-    K = args.steps
+    K = steps
     n_ev = len(names) + 1
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(K)]
     stream = torch.cuda.current_stream()
@@ -356,7 +342,7 @@ def main():
     roof["avg_us"] = dom_us
     traffic = None
     src_hash = kernel_source_hash()
-    workload = f"{cfg.name}_{args.wtype}_T{T}" + (f"_A{args.active}" if args.active else "") + \
+    workload = f"{cfg.name}_{wtype}_T{T}" + (f"_A{active_n}" if active_n else "") + \
         (f"_fin{args.finished:g}" if args.finished else "") + \
         ("_i2fnative" if args.i2f == "native" else "")
     if os.path.exists(TRAFFIC_FILE):
@@ -367,7 +353,6 @@ def main():
         except Exception:
             traffic = None
     roof["traffic"] = traffic
-    att = attainable(q, torch, dev)
     roof["frac_of_attainable"] = roof["achieved"] / (att["hbm_read_GBps"] if roof["bound"] == "hbm"
                                                      else att["mfma_f16_TFLOPs"])
 
@@ -395,7 +380,7 @@ def main():
                 raise RuntimeError("graph replay differs from the eager layer output")
             plans[1 % n_copies].run()
             torch.cuda.synchronize()
-        for i in range(args.warmup):
+        for i in range(warmup):
             graphs[i % n_copies].replay()
         torch.cuda.synchronize()
         tg0 = time.perf_counter()
@@ -419,7 +404,7 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": step_ms,
         "timing": "hip-graph replay" if graph_info is not None else "eager launches",
         "higher_is_better": True,
@@ -428,7 +413,7 @@ def main():
         "dtype": "fp16",
         "data": "synthetic",
         "config": {"workload": workload, "d": cfg.d, "ffn": cfg.inter, "act": cfg.act,
-                   "experts": cfg.E, "top_k": cfg.k, "tokens": T, "weights": args.wtype,
+                   "experts": cfg.E, "top_k": cfg.k, "tokens": T, "weights": wtype,
                    "group": cfg.group or "per-channel", "gate": cfg.gate_mode,
                    "active_experts": n_active, "max_rows_per_expert": int(counts.max()),
                    "finished_fraction": float(args.finished), "routed_rows": R,
@@ -444,6 +429,64 @@ def main():
     result["eager"] = {"ms_per_step": ms_per_step, "tokens_per_s": T / (ms_per_step * 1e-3)}
     if graph_info is not None:
         result["graph_replay"] = graph_info
+    return result, inp
+
+
+# The configurations of the pages' tables besides the headline (tokens per step as listed there):
+# decode / verify steps and the mid-M and prefill layers of the fine-grained MoE shapes.
+PER_CONFIG = (("qwen15_moe", 17), ("qwen15_moe", 544), ("dsv2_lite", 9), ("dsv2_lite", 288),
+              ("phi35_moe", 1), ("phi35_moe", 17), ("phi35_moe", 8192))
+
+
+def per_config(args, q, torch, np, synth, att):
+    """Graph-replayed step and dominant-kernel roofline fraction of every other configuration
+    (INT4 weights, their default routing), each timed like the headline on fewer steps."""
+    out = {}
+    for name, T in PER_CONFIG:
+        cfg = synth.get_config(name)
+        steps = 5 if T >= 4096 else 50
+        res, _ = measure_layer(args, q, torch, np, synth, cfg, T, "int4", 0, steps, 5, att)
+        roof = res["roofline"]
+        out[res["config"]["workload"]] = {
+            "ms_per_step": res["ms_per_step"], "timing": res["timing"],
+            "tokens_per_s": res["value"], "steps": steps,
+            "dominant": roof["kernel"], "dominant_us": roof["avg_us"], "bound": roof["bound"],
+            "achieved": roof["achieved"], "unit": roof["unit"], "frac": roof["frac"],
+            "traffic": roof["traffic"],
+            "layer_weight_frac_hbm": res["layer"]["weight_frac_hbm"],
+            "layer_mfma_frac": res["layer"]["mfma_frac"]}
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this layer build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_expert_layer_amd as q
+    import synth
+
+    if args.workload in ("elb", "bf16"):
+        torch.cuda.set_device(torch.device("cuda:0"))
+        (bench_elb if args.workload == "elb" else bench_bf16)(args, q, torch, np, synth)
+        return
+    cfg = synth.get_config(args.config)
+    T = args.T or cfg.T_list[0]
+    att = attainable(q, torch, torch.device("cuda:0"))
+    result, inp = measure_layer(args, q, torch, np, synth, cfg, T, args.wtype, args.active,
+                                args.steps, args.warmup, att)
+    if not args.no_per_config and args.config == "mt_encoder" and not args.T and not args.active \
+            and args.wtype == "int4" and not args.finished and not args.path and not args.tile \
+            and args.i2f == "trick" and not args.no_graph:
+        result["per_config"] = per_config(args, q, torch, np, synth, att)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)
     print(json.dumps(result), flush=True)

@@ -65,3 +65,12 @@ def test_bench_json_line():
     assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], rel=1e-9)
     assert roof["traffic"] is None or roof["traffic"] > 0
     assert "cpu_baseline" not in d
+    # the other layer shapes: graph-replayed step and dominant-kernel roofline each
+    pc = d["per_config"]
+    assert set(pc) == {"qwen15_moe_int4_T17", "qwen15_moe_int4_T544", "dsv2_lite_int4_T9",
+                       "dsv2_lite_int4_T288", "phi35_moe_int4_T1", "phi35_moe_int4_T17",
+                       "phi35_moe_int4_T8192"}, sorted(pc)
+    for name, c in pc.items():
+        assert c["timing"] == "hip-graph replay" and c["ms_per_step"] > 0, name
+        assert c["bound"] in ("hbm", "mfma") and 0 < c["frac"] < 1, name
+        assert c["dominant_us"] < c["ms_per_step"] * 1e3 * 1.5, name
