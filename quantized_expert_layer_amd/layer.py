@@ -139,6 +139,13 @@ class DeviceLayer:
             b["dws"] = new_output(dws, torch.uint8, dev)
         return Workspace(T=T, bufs=b)
 
+    def _side_stream(self):
+        """The stream the shared experts of a decode step run on (one per layer)."""
+        import torch
+        if getattr(self, "_side", None) is None:
+            self._side = torch.cuda.Stream(device=self.device)
+        return self._side
+
     def _shared_calls(self, b, x, T):
         """(name, C function, args) of the shared experts (fp16, E = 1) into b["sh_y"]."""
         L, st = lib(), None
@@ -165,17 +172,25 @@ class DeviceLayer:
         b = ws.bufs
         path = self.gemm_path
         if self.uses_decode(T, gate_in_gemm):
-            addend = None
+            addend, ready = None, None
             if self.shared is not None:
+                # the shared experts run on a side stream beside the routed step; the decode
+                # call waits for them only before its last launch, which adds their output
+                import torch
+                main = stream if stream is not None else torch.cuda.current_stream(self.device)
+                side, fork, ready = self._side_stream(), torch.cuda.Event(), torch.cuda.Event()
+                fork.record(main)
+                side.wait_event(fork)
                 for name, fn, args in self._shared_calls(b, x, T):
-                    st = fn(*(args[:-1] + (_stream(stream),)))
+                    st = fn(*(args[:-1] + (_stream(side),)))
                     if st != 0:
                         raise MoEError(name, st)
+                ready.record(side)
                 addend = b["sh_y"]
             moe_decode_layer(logits, x, self.k, self.gate_mode, self.inter, self.act, self.w1,
                              self.s1, self.w2, self.s2, self.wtype, self.group, addend=addend,
                              topk_ids=b["ids"], topk_w=b["w"], out=b["out"], ws=b["dws"],
-                             stream=stream, active=active)
+                             stream=stream, active=active, addend_ready=ready)
             return b["out"]
         moe_route_topk(logits, self.k, self.gate_mode, b["ids"], b["w"], stream=stream,
                        active=active)
@@ -245,15 +260,38 @@ class DeviceLayer:
         keep = (opts, x, logits, w1, w2, self.s1, self.s2, self.shared, ws, active)
         if self.uses_decode(T, gate_in_gemm):
             calls = []
-            addend = None
+            addend, ready = None, None
             if self.shared is not None:
+                # shared experts on a side stream, joined by the decode call before the launch
+                # that adds their output (fork and join are event records and waits, which a
+                # captured graph keeps as dependencies)
+                import torch
                 addend = b["sh_y"]
-                calls = [(n, fn, args[:-1] + (st,)) for n, fn, args in self._shared_calls(b, x, T)]
+                main = stream if stream is not None else torch.cuda.current_stream(self.device)
+                side = torch.cuda.Stream(device=self.device)
+                fork, join = torch.cuda.Event(), torch.cuda.Event()
+                join.record(side)                  # creates the event whose handle is passed
+
+                def do_fork():
+                    fork.record(main)
+                    side.wait_event(fork)
+                    return 0
+
+                def do_join():
+                    join.record(side)
+                    return 0
+
+                ss = _stream(side)
+                calls = [("fork", do_fork, ())]
+                calls += [(n, fn, args[:-1] + (ss,)) for n, fn, args in self._shared_calls(b, x, T)]
+                calls.append(("join", do_join, ()))
+                ready = join.cuda_event
+                keep = keep + (side, fork, join)
             calls.append(("decode", L.moe_decode_layer,
                           (_ptr(logits), _ptr(active), _ptr(x), T, self.E, self.k,
                            GATES[self.gate_mode], self.d, self.inter, ac, _ptr(w1),
                            _ptr(self.s1), _ptr(w2), _ptr(self.s2), wt, self.group, _ptr(addend),
-                           None, _ptr(b["ids"]), _ptr(b["w"]), _ptr(b["out"]), _ptr(b["dws"]),
+                           ready, _ptr(b["ids"]), _ptr(b["w"]), _ptr(b["out"]), _ptr(b["dws"]),
                            b["dws"].numel(), st)))
             return LayerPlan(calls, b["out"], keep=keep)
         calls = [
