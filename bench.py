@@ -28,12 +28,16 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ("quantized_expert_layer_amd/csrc/gemm.hip",
-                  "quantized_expert_layer_amd/csrc/common.hpp")
+                  "quantized_expert_layer_amd/csrc/common.hpp",
+                  "quantized_expert_layer_amd/csrc/decode.hip",
+                  "quantized_expert_layer_amd/csrc/route.hpp",
+                  "quantized_expert_layer_amd/csrc/sort.hpp")
 
 
 def kernel_source_hash():
-    """Hash of the GEMM sources with comments and blank lines dropped, so that a traffic record
-    stays valid across comment edits but not across any change to the code itself."""
+    """Hash of the layer kernels' sources (GEMMs and the decode step) with comments and blank
+    lines dropped, so that a traffic record stays valid across comment edits but not across any
+    change to the code itself."""
     import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
