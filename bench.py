@@ -29,6 +29,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ("quantized_expert_layer_amd/csrc/gemm.hip",
                   "quantized_expert_layer_amd/csrc/common.hpp",
+                  "quantized_expert_layer_amd/csrc/stream.hpp",
                   "quantized_expert_layer_amd/csrc/decode.hip",
                   "quantized_expert_layer_amd/csrc/route.hpp",
                   "quantized_expert_layer_amd/csrc/sort.hpp")
@@ -279,11 +280,12 @@ def measure_layer(args, q, torch, np, synth, cfg, T, wtype, active_n, steps, war
         running = ~np.repeat(fin, args.sentence_len)[:T]
         active = torch.from_numpy(running.astype(np.uint8)).to(dev)
 
-    # weight rotation: enough copies that each step reads weights the caches do not hold
-    wbytes = layer.w1.numel() + layer.w2.numel()
+    # weight rotation: enough copies that each step reads weights the caches do not hold (the
+    # shared experts' too: every layer of a model has its own)
+    own = (layer.w1, layer.w2) + (tuple(layer.shared) if layer.shared is not None else ())
+    wbytes = sum(t.numel() for t in own)
     n_copies = max(1, int(np.ceil(args.rotate_gb * 1e9 / wbytes)))
-    copies = [(layer.w1, layer.w2)] + [(layer.w1.clone(), layer.w2.clone())
-                                       for _ in range(n_copies - 1)]
+    copies = [own] + [tuple(t.clone() for t in own) for _ in range(n_copies - 1)]
     plans = [layer.plan(ws, x, logits, weights=c, active=active) for c in copies]
     names = plans[0].names
 
@@ -324,11 +326,19 @@ def measure_layer(args, q, torch, np, synth, cfg, T, wtype, active_n, steps, war
     per_expert_w2 = layer.w2.numel() // cfg.E + (0 if inp.scales2 is None else 2 * inp.scales2[0].size)
     g1 = {"flops": 2.0 * R * cfg.d * layer.n1, "bytes": n_active * per_expert_w1}
     g2 = {"flops": 2.0 * R * cfg.inter * cfg.d, "bytes": n_active * per_expert_w2}
+    # the shared experts (fp16, every token): their weights once, over all T rows
+    sh = {"flops": 0.0, "bytes": 0}
+    if layer.shared is not None:
+        sh = {"flops": 2.0 * T * cfg.d * 3 * layer.shared_inter,
+              "bytes": int(sum(t.numel() for t in layer.shared))}
     if "decode" in stage_us:
-        # one moe_decode_layer call (gating + sort, GEMM 1, GEMM 2 with the combine): its
-        # events bracket all three launches, so the unit is the whole call
+        # one moe_decode_layer call (gating + sort, GEMM 1, GEMM 2 with the combine; with
+        # shared experts, theirs inside the same launches): its events bracket all its
+        # launches, so the unit is the whole call
         dom_name = "decode"
         dom = {"flops": g1["flops"] + g2["flops"], "bytes": g1["bytes"] + g2["bytes"]}
+        if layer._shared_in_decode():
+            dom = {"flops": dom["flops"] + sh["flops"], "bytes": dom["bytes"] + sh["bytes"]}
     else:
         dom_name, dom = max((("gemm1", g1), ("gemm2", g2)), key=lambda kv: stage_us[kv[0]])
     dom_us = stage_us[dom_name]
@@ -400,8 +410,8 @@ def measure_layer(args, q, torch, np, synth, cfg, T, wtype, active_n, steps, war
     # decode-sized layer, is as long as the GPU work itself).
     step_ms = graph_info["ms_per_step"] if graph_info is not None else ms_per_step
     layer_s = step_ms * 1e-3
-    weight_bytes = g1["bytes"] + g2["bytes"]
-    flops = g1["flops"] + g2["flops"]
+    weight_bytes = g1["bytes"] + g2["bytes"] + sh["bytes"]
+    flops = g1["flops"] + g2["flops"] + sh["flops"]
     result = {
         "metric": METRIC,
         "value": T / layer_s,

@@ -9,7 +9,8 @@
  *   4. moe_unpermute_combine restore token order, scale by gate weight, sum the k rows
  *   and moe_dequant          the standalone per-expert dequantization (Algorithm 1);
  *   moe_decode_layer         steps 1-4 for the few tokens of a decode / verify step, in three
- *                            launches (moe_decode_layer_noalloc: the same on the library's
+ *                            launches (moe_decode_layer_shared: with the shared experts in
+ *                            the same launches; moe_decode_layer_noalloc: on the library's
  *                            own scratch memory, for callers that cannot allocate)
  *   moe_elb_accumulate / moe_elb_top_m   the expert lookahead buffer of a speculative draft
  *   moe_bf16_recombine       BF16 values from separately stored exponent / sign-mantissa bytes
@@ -274,6 +275,40 @@ int32_t moe_decode_layer(const float* logits, const uint8_t* active, const uint1
 /* Workspace bytes of moe_decode_layer (0 for arguments it does not accept). */
 size_t moe_decode_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int32_t inter,
                                  int32_t wtype);
+
+/*
+ * moe_decode_layer_shared -- moe_decode_layer for a layer with shared experts (every token
+ * passes through them with weight 1 beside its k routed experts), computed inside the same
+ * launches: the shared first GEMM runs as extra blocks of the routed first-GEMM launch (as a
+ * launch of its own when T*k > 128), the shared second GEMM as extra blocks of the
+ * second-GEMM launch, and the final reduction adds its output.
+ *   [S] Core method (the router and the shared experts stay fp16 in the quantized copy) and
+ *   Method step 5, as for moe_decode_layer.
+ *
+ *   shared_w1     fp16 weights packed by moe_pack_wq for (MOE_W_FP16, 1, d, 2*shared_inter),
+ *                 columns [gate | up] of all shared experts side by side (SwiGLU)
+ *   shared_w2     fp16 weights packed for (MOE_W_FP16, 1, shared_inter, d)
+ *   shared_inter  the shared experts' combined intermediate size
+ *   out           fp16 [T, d]  out: out[t] = fp16( sum_j topk_w[t,j] * FFN_{topk_ids[t,j]}(x[t])
+ *                 + fp16(SwiGLU-FFN_shared(x[t])) ): the shared output is rounded to fp16
+ *                 once, as moe_grouped_gemm_wq writes it, then added in fp32.  A finished
+ *                 token (active[t] == 0) still receives the shared output.
+ *   The other arguments, the numerics of the routed part and the errors are those of
+ *   moe_decode_layer (no addend: the shared output takes its place), plus MOE_ERR_INVALID for
+ *   shared_inter <= 0 or a NULL shared weight, MOE_ERR_UNSUPPORTED for fp16 routed weights or
+ *   shared_inter % 128 != 0.  ws: at least moe_decode_shared_workspace_size(...) bytes.
+ */
+int32_t moe_decode_layer_shared(const float* logits, const uint8_t* active, const uint16_t* x,
+                                int32_t T, int32_t E, int32_t k, int32_t gate_mode, int32_t d,
+                                int32_t inter, int32_t act, const void* w1, const uint16_t* s1,
+                                const void* w2, const uint16_t* s2, int32_t wtype,
+                                int32_t group_size, const void* shared_w1,
+                                const void* shared_w2, int32_t shared_inter, int32_t* topk_ids,
+                                float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                                void* stream);
+/* Workspace bytes of moe_decode_layer_shared (0 for arguments it does not accept). */
+size_t moe_decode_shared_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d,
+                                        int32_t inter, int32_t wtype, int32_t shared_inter);
 
 /*
  * moe_decode_layer_noalloc -- moe_decode_layer without a caller workspace, for callers that

@@ -28,7 +28,8 @@ __all__ = [
     "moe_dequant", "moe_pack_wq", "moe_packed_bytes", "moe_gemm_workspace_size",
     "moe_permute_workspace_size", "GemmOpts", "EXPORTED_SYMBOLS", "new_output",
     "moe_probe_read", "moe_probe_mfma", "moe_decode_layer", "moe_decode_workspace_size",
-    "moe_decode_layer_noalloc", "MOE_DECODE_SCRATCH_BYTES",
+    "moe_decode_layer_noalloc", "MOE_DECODE_SCRATCH_BYTES", "moe_decode_layer_shared",
+    "moe_decode_shared_workspace_size",
     "MOE_DECODE_MAX_TOKENS", "MOE_DECODE_MAX_ROWS", "moe_elb_accumulate", "moe_elb_top_m",
     "moe_bf16_recombine",
 ]
@@ -58,7 +59,7 @@ EXPORTED_SYMBOLS = (
     "moe_grouped_gemm_wq_rows", "moe_gemm_workspace_size", "moe_unpermute_combine", "moe_dequant", "moe_packed_bytes",
     "moe_pack_wq", "moe_status_str", "moe_version", "moe_probe_read", "moe_probe_mfma",
     "moe_decode_layer", "moe_decode_workspace_size", "moe_route_topk_active",
-    "moe_decode_layer_noalloc",
+    "moe_decode_layer_noalloc", "moe_decode_layer_shared", "moe_decode_shared_workspace_size",
     "moe_elb_accumulate", "moe_elb_top_m", "moe_bf16_recombine",
 )
 
@@ -130,6 +131,9 @@ def lib():
         "moe_elb_top_m": (_I, [_P, _I, _I, _I, _P, _P, _P]),
         "moe_bf16_recombine": (_I, [_P, _P, _SZ, _P, _P]),
         "moe_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+        "moe_decode_layer_shared": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
+                                         _I, _I, _P, _P, _I, _P, _P, _P, _P, _SZ, _P]),
+        "moe_decode_shared_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -405,6 +409,51 @@ def moe_decode_layer(logits, x, k, gate_mode, inter, act, w1, s1, w2, s2, wtype,
         _ptr(addend), None if addend_ready is None else addend_ready.cuda_event,
         _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
+    return out, topk_ids, topk_w
+
+
+def moe_decode_shared_workspace_size(T, k, E, d, inter, wtype, shared_inter):
+    return lib().moe_decode_shared_workspace_size(T, k, E, d, inter, WTYPES.get(wtype, wtype),
+                                                  shared_inter)
+
+
+def moe_decode_layer_shared(logits, x, k, gate_mode, inter, act, w1, s1, w2, s2, wtype,
+                            group_size, shared_w1, shared_w2, shared_inter, topk_ids=None,
+                            topk_w=None, out=None, ws=None, stream=None, active=None):
+    """moe_decode_layer with the shared experts (fp16, SwiGLU, packed for E = 1) computed in
+    the same launches.  Returns (out fp16 [T, d], topk_ids int32 [T, k], topk_w fp32 [T, k])."""
+    torch = _torch()
+    T, E = logits.shape
+    d = x.shape[1]
+    wt = WTYPES.get(wtype, wtype)
+    dev = x.device
+    if out is None:
+        out = new_output((T, d), torch.float16, dev)
+    if topk_ids is None:
+        topk_ids = new_output((T, k), torch.int32, dev)
+    if topk_w is None:
+        topk_w = new_output((T, k), torch.float32, dev)
+    if ws is None:
+        need = lib().moe_decode_shared_workspace_size(T, k, E, d, inter, wt, int(shared_inter))
+        ws = new_output(max(need, 16), torch.uint8, dev)
+    _need(logits, torch.float32, "logits", T * E)
+    _need(x, torch.float16, "x", T * d)
+    _need(w1, torch.uint8, "w1")
+    _need(s1, torch.float16, "s1")
+    _need(w2, torch.uint8, "w2")
+    _need(s2, torch.float16, "s2")
+    _need(shared_w1, torch.uint8, "shared_w1")
+    _need(shared_w2, torch.uint8, "shared_w2")
+    _need(topk_ids, torch.int32, "topk_ids", T * k)
+    _need(topk_w, torch.float32, "topk_w", T * k)
+    _need(out, torch.float16, "out", T * d)
+    _need(ws, torch.uint8, "ws")
+    _need(active, torch.uint8, "active", T)
+    _check("moe_decode_layer_shared", lib().moe_decode_layer_shared(
+        _ptr(logits), _ptr(active), _ptr(x), T, E, k, GATES.get(gate_mode, gate_mode), d,
+        int(inter), ACTS.get(act, act), _ptr(w1), _ptr(s1), _ptr(w2), _ptr(s2), wt,
+        int(group_size), _ptr(shared_w1), _ptr(shared_w2), int(shared_inter), _ptr(topk_ids),
+        _ptr(topk_w), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return out, topk_ids, topk_w
 
 

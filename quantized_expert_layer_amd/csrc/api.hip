@@ -299,28 +299,54 @@ size_t moe_decode_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d, int
     if (validate_decode(T, E, k, MOE_GATE_SOFTMAX_TOPK, d, inter, MOE_ACT_NONE, wtype, 0) !=
         MOE_OK)
         return 0;
-    return moe::decode_workspace_layout(T, k, E, d, inter, wtype, nullptr, nullptr);
+    return moe::decode_workspace_layout(T, k, E, d, inter, wtype, 0, nullptr, nullptr);
 }
 
-int32_t moe_decode_layer(const float* logits, const uint8_t* active, const uint16_t* x,
-                         int32_t T, int32_t E, int32_t k, int32_t gate_mode, int32_t d,
-                         int32_t inter, int32_t act,
-                         const void* w1, const uint16_t* s1, const void* w2,
-                         const uint16_t* s2, int32_t wtype, int32_t group_size,
-                         const uint16_t* addend, void* addend_ready, int32_t* topk_ids,
-                         float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
-                         void* stream) {
+// The shared experts of moe_decode_layer_shared: fp16 weights beside integer-coded routed ones.
+static int32_t validate_shared(int32_t wtype, int32_t shared_inter) {
+    if (shared_inter <= 0) return MOE_ERR_INVALID;
+    if (wtype == MOE_W_FP16 || shared_inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)shared_inter * 2 * MOE_DECODE_MAX_TOKENS >= (int64_t)1 << 31)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+size_t moe_decode_shared_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d,
+                                        int32_t inter, int32_t wtype, int32_t shared_inter) {
+    if (validate_decode(T, E, k, MOE_GATE_SOFTMAX_TOPK, d, inter, MOE_ACT_NONE, wtype, 0) !=
+            MOE_OK ||
+        validate_shared(wtype, shared_inter) != MOE_OK)
+        return 0;
+    return moe::decode_workspace_layout(T, k, E, d, inter, wtype, shared_inter, nullptr, nullptr);
+}
+
+// moe_decode_layer and moe_decode_layer_shared: sw1 == NULL for no shared experts.
+static int32_t decode_layer(const float* logits, const uint8_t* active, const uint16_t* x,
+                            int32_t T, int32_t E, int32_t k, int32_t gate_mode, int32_t d,
+                            int32_t inter, int32_t act, const void* w1, const uint16_t* s1,
+                            const void* w2, const uint16_t* s2, int32_t wtype, int32_t group_size,
+                            const void* sw1, const void* sw2, int32_t shared_inter,
+                            const uint16_t* addend, void* addend_ready, int32_t* topk_ids,
+                            float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                            void* stream) {
     if (int32_t st = validate_decode(T, E, k, gate_mode, d, inter, act, wtype, group_size))
         return st;
+    const bool shared = sw1 != nullptr;
+    if (shared) {
+        if (int32_t st = validate_shared(wtype, shared_inter)) return st;
+    }
     if (T == 0) return MOE_OK;
     if (!logits || !x || !w1 || !w2 || !topk_ids || !topk_w || !out) return MOE_ERR_INVALID;
     if (wtype != MOE_W_FP16 && (!s1 || !s2)) return MOE_ERR_INVALID;
+    if (shared && !sw2) return MOE_ERR_INVALID;
     if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
         !aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(out, 16))
         return MOE_ERR_INVALID;
     if ((s1 && !aligned(s1, 16)) || (s2 && !aligned(s2, 16)) || (addend && !aligned(addend, 16)))
         return MOE_ERR_INVALID;
-    const size_t need = moe::decode_workspace_layout(T, k, E, d, inter, wtype, nullptr, nullptr);
+    if (shared && (!aligned(sw1, 16) || !aligned(sw2, 16))) return MOE_ERR_INVALID;
+    const size_t need = moe::decode_workspace_layout(T, k, E, d, inter, wtype,
+                                                     shared ? shared_inter : 0, nullptr, nullptr);
     if (!ws || ws_bytes < need || !aligned(ws, 16)) return MOE_ERR_WORKSPACE;
     if (int32_t st = check_device()) return st;
     moe::DecodeArgs a;
@@ -340,13 +366,43 @@ int32_t moe_decode_layer(const float* logits, const uint8_t* active, const uint1
     a.s2 = s2;
     a.wtype = wtype;
     a.group = group_size;
-    a.addend = addend;
-    a.addend_ready = addend_ready;
+    a.sw1 = shared ? sw1 : nullptr;
+    a.sw2 = shared ? sw2 : nullptr;
+    a.shared_inter = shared ? shared_inter : 0;
+    a.addend = shared ? nullptr : addend;
+    a.addend_ready = shared ? nullptr : addend_ready;
     a.ids = topk_ids;
     a.wts = topk_w;
     a.out = out;
     a.ws = ws;
     return hip_status(moe::launch_decode(a, (hipStream_t)stream));
+}
+
+int32_t moe_decode_layer(const float* logits, const uint8_t* active, const uint16_t* x,
+                         int32_t T, int32_t E, int32_t k, int32_t gate_mode, int32_t d,
+                         int32_t inter, int32_t act,
+                         const void* w1, const uint16_t* s1, const void* w2,
+                         const uint16_t* s2, int32_t wtype, int32_t group_size,
+                         const uint16_t* addend, void* addend_ready, int32_t* topk_ids,
+                         float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                         void* stream) {
+    return decode_layer(logits, active, x, T, E, k, gate_mode, d, inter, act, w1, s1, w2, s2,
+                        wtype, group_size, nullptr, nullptr, 0, addend, addend_ready, topk_ids,
+                        topk_w, out, ws, ws_bytes, stream);
+}
+
+int32_t moe_decode_layer_shared(const float* logits, const uint8_t* active, const uint16_t* x,
+                                int32_t T, int32_t E, int32_t k, int32_t gate_mode, int32_t d,
+                                int32_t inter, int32_t act, const void* w1, const uint16_t* s1,
+                                const void* w2, const uint16_t* s2, int32_t wtype,
+                                int32_t group_size, const void* shared_w1,
+                                const void* shared_w2, int32_t shared_inter, int32_t* topk_ids,
+                                float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                                void* stream) {
+    if (!shared_w1) return MOE_ERR_INVALID;
+    return decode_layer(logits, active, x, T, E, k, gate_mode, d, inter, act, w1, s1, w2, s2,
+                        wtype, group_size, shared_w1, shared_w2, shared_inter, nullptr, nullptr,
+                        topk_ids, topk_w, out, ws, ws_bytes, stream);
 }
 
 int32_t moe_decode_layer_noalloc(const float* logits, const uint8_t* active, const uint16_t* x,
@@ -358,7 +414,7 @@ int32_t moe_decode_layer_noalloc(const float* logits, const uint8_t* active, con
     if (int32_t st = validate_decode(T, E, k, gate_mode, d, inter, act, wtype, group_size))
         return st;
     if (T == 0) return MOE_OK;
-    const size_t need = moe::decode_workspace_layout(T, k, E, d, inter, wtype, nullptr, nullptr);
+    const size_t need = moe::decode_workspace_layout(T, k, E, d, inter, wtype, 0, nullptr, nullptr);
     if (need > (size_t)MOE_DECODE_SCRATCH_BYTES) return MOE_ERR_UNSUPPORTED;
     if (int32_t st = check_device()) return st;
     int dev = 0;

@@ -14,6 +14,10 @@
 //   4. combine_reduce_kernel     (nsplit > 1) adds the blocks' fp32 token sums in split order
 //                                and the addend, and writes the fp16 output.
 //
+// With shared experts (fp16, SwiGLU, every token, weight 1) launches 2 and 3 are their _side
+// variants: after the routed blocks come the blocks of the shared experts' dense first GEMM
+// (into sh_h) and second GEMM (into sh_y), and sh_y is the addend of launch 4.
+//
 // "Specter" summary, Method steps, step 5 and Technical novelty: the draft model's expert
 // sub-computations run in one fused launch, and the verify step groups tokens by expert into
 // one GEMM per expert and scatters the results back.  "Who Says Elephants Can't Run",
@@ -21,6 +25,7 @@
 // expert_scale.  Here the second GEMM's launch also does the unpermute and the combine.
 #include "common.hpp"
 #include "launch.hpp"
+#include "stream.hpp"
 #include "route.hpp"
 #include "sort.hpp"
 
@@ -115,8 +120,11 @@ constexpr int kCombineNcb = 2;
 //            device-scope release per block, which on this chip writes back the whole L2 of
 //            the XCD and cost more than the second launch.)
 // ------------------------------------------------------------------------------------
-template <int WT, bool GROUPED, int PF, int PA, int NCB>
-__global__ __launch_bounds__(64 * kCombineWaves) void gemm_combine_kernel(CombineParams p) {
+// Block `bid` of the launch; tok_sum: LDS for [S][T][NC] token sums.  TAG: a specialization
+// of its own per calling kernel.
+template <int WT, bool GROUPED, int PF, int PA, int NCB, int TAG = 0>
+__device__ __forceinline__ void combine_body(const CombineParams& p, int bid,
+                                             float* __restrict__ tok_sum) {
     constexpr int KSB = WTraits<WT>::KSB;
     constexpr int KSTEPS = KSB / 32;
     constexpr int NC = 16 * NCB;                              // columns of a block
@@ -124,7 +132,6 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gemm_combine_kernel(Combin
     __shared__ int tile_v[kDecodeMaxTiles];
     __shared__ int tok_of[MOE_DECODE_MAX_ROWS];
     __shared__ float gate_of[MOE_DECODE_MAX_ROWS];
-    extern __shared__ float tok_sum[];                        // [S][T][NC]
 
     const int lane = threadIdx.x & (kWave - 1);
     // wave index, held in a scalar register (the compiler cannot see it is wave-uniform)
@@ -132,8 +139,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gemm_combine_kernel(Combin
     const int S = blockDim.x / kWave;
     const int ncb = p.N / 16;
     const int ncg = p.N / NC;
-    const int cg = blockIdx.x % ncg;
-    const int sp = blockIdx.x / ncg;
+    const int cg = bid % ncg;
+    const int sp = bid / ncg;
     const int K = p.K, N = p.N, T = p.T, R = p.R;
     const int nSB = K / KSB;
     // the table's count: at most kDecodeMaxTiles by construction, clamped all the same
@@ -323,6 +330,28 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gemm_combine_kernel(Combin
     }
 }
 
+template <int WT, bool GROUPED, int PF, int PA, int NCB>
+__global__ __launch_bounds__(64 * kCombineWaves) void gemm_combine_kernel(CombineParams p) {
+    extern __shared__ float tok_sum[];                        // [S][T][NC]
+    combine_body<WT, GROUPED, PF, PA, NCB>(p, blockIdx.x, tok_sum);
+}
+
+// The second launch with the shared experts' second GEMM beside it ([S] Method step 5): blocks
+// [0, nb) run the routed GEMM 2 + combine above (writing fp32 partials, which the reduction adds
+// with the shared experts' output), the rest the dense fp16 GEMM ps (H_shared . W2_shared over
+// every token, 8 waves splitting K).
+template <int WT, bool GROUPED, int PF, int PA, int NCB>
+__global__ __launch_bounds__(64 * kCombineWaves) void gemm_combine_side_kernel(CombineParams p, int nb,
+                                                                              GemmParams ps,
+                                                                              int ngo_s) {
+    extern __shared__ float dyn[];
+    if ((int)blockIdx.x < nb)
+        combine_body<WT, GROUPED, PF, PA, NCB, 1>(p, blockIdx.x, dyn);
+    else
+        stream_body<MOE_W_FP16, MOE_ACT_NONE, false, 8, 2, 1, 64 + WT * 2 + (GROUPED ? 1 : 0)>(
+            ps, ngo_s, blockIdx.x - nb, (f32x4*)dyn);
+}
+
 // ------------------------------------------------------------------------------------
 // 4. out[t, c] = fp16( part[0, t, c] + .. + part[nsplit - 1, t, c] + addend[t, c] ), fp32 in
 //    that order; one thread per 4 consecutive columns.
@@ -353,18 +382,19 @@ constexpr int kCombineMaxSplit = 8;
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-int decode_combine_split(int d) {
+int decode_combine_split(int d, bool shared) {
     const int ncg = d / (16 * kCombineNcb);
     int s = 1;
     while (s < kCombineMaxSplit && ncg * s < kCombineTargetBlocks) s *= 2;
-    return s;
+    // with shared experts the reduction launch adds their output: at least two splits
+    return (shared && s < 2) ? 2 : s;
 }
 
-size_t decode_workspace_layout(int T, int k, int E, int d, int inter, int wtype, DecodeWs* ws,
-                               char* base) {
+size_t decode_workspace_layout(int T, int k, int E, int d, int inter, int wtype,
+                               int shared_inter, DecodeWs* ws, char* base) {
     (void)wtype;
     const size_t R = (size_t)T * k;
-    const int nsplit = decode_combine_split(d);
+    const int nsplit = decode_combine_split(d, shared_inter > 0);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -378,7 +408,11 @@ size_t decode_workspace_layout(int T, int k, int E, int d, int inter, int wtype,
     char* tiles = take((size_t)(1 + kDecodeMaxTiles) * 4);
     char* h = take(R * (size_t)inter * 2);
     char* part = take(nsplit > 1 ? (size_t)nsplit * T * d * 4 : 0);
+    char* sh_h = take((size_t)T * shared_inter * 2);
+    char* sh_y = take(shared_inter > 0 ? (size_t)T * d * 2 : 0);
     if (ws) {
+        ws->sh_h = shared_inter > 0 ? (uint16_t*)sh_h : nullptr;
+        ws->sh_y = shared_inter > 0 ? (uint16_t*)sh_y : nullptr;
         ws->perm = (int32_t*)perm;
         ws->inv_perm = (int32_t*)inv;
         ws->offsets = (int32_t*)offs;
@@ -391,10 +425,30 @@ size_t decode_workspace_layout(int T, int k, int E, int d, int inter, int wtype,
 }
 
 template <int WT, bool GROUPED>
-static hipError_t combine_launch(const CombineParams& p, hipStream_t stream) {
+static hipError_t combine_launch(const CombineParams& p, hipStream_t stream,
+                                 const GemmParams* side) {
     const unsigned grid = (unsigned)(p.N / (16 * kCombineNcb) * p.nsplit);
-    const size_t lds = (size_t)kCombineWaves * p.T * 16 * kCombineNcb * sizeof(float);
-    gemm_combine_kernel<WT, GROUPED, 4, 2, kCombineNcb><<<grid, kCombineWaves * kWave, lds, stream>>>(p);
+    size_t lds = (size_t)kCombineWaves * p.T * 16 * kCombineNcb * sizeof(float);
+    if (side) {
+        // the shared experts' second GEMM beside the routed one: its output is the addend,
+        // added by the reduction launch below (so the combine blocks must write partials);
+        // integer-coded routed weights only
+        if constexpr (WT == MOE_W_FP16) {
+            return hipErrorInvalidValue;
+        } else {
+            if (p.nsplit < 2 || side->split != kCombineWaves || side->act != MOE_ACT_NONE)
+                return hipErrorInvalidValue;
+            const int ngo_s = side->N / 16;
+            const long blocks_s = (long)((side->R + 15) / 16) * ngo_s;
+            const size_t lds_s = (size_t)(kCombineWaves - 1) * 64 * sizeof(f32x4);
+            if (lds_s > lds) lds = lds_s;
+            gemm_combine_side_kernel<WT, GROUPED, 4, 2, kCombineNcb>
+                <<<grid + (unsigned)blocks_s, kCombineWaves * kWave, lds, stream>>>(
+                    p, (int)grid, *side, ngo_s);
+        }
+    } else {
+        gemm_combine_kernel<WT, GROUPED, 4, 2, kCombineNcb><<<grid, kCombineWaves * kWave, lds, stream>>>(p);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || p.nsplit == 1) return err;
     const int threads = p.T * (p.N / 4);
@@ -405,7 +459,8 @@ static hipError_t combine_launch(const CombineParams& p, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     DecodeWs ws;
-    decode_workspace_layout(a.T, a.k, a.E, a.d, a.inter, a.wtype, &ws, (char*)a.ws);
+    decode_workspace_layout(a.T, a.k, a.E, a.d, a.inter, a.wtype, a.sw1 ? a.shared_inter : 0, &ws,
+                            (char*)a.ws);
     const int R = a.T * a.k;
 
     static_assert(MOE_DECODE_MAX_TOKENS <= 4 * kSortWaves, "one token per 16-lane row");
@@ -448,7 +503,49 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     g.tile = 0;
     g.i2f = MOE_I2F_TRICK;
     g.tiles16 = ws.tiles;
-    err = launch_gemm_stream(g, stream);
+    // the shared experts (fp16, every token): their first GEMM runs beside the routed GEMM 1,
+    // their second beside the routed GEMM 2, and the reduction adds their output
+    const bool shared = a.sw1 != nullptr;
+    GemmParams sg1, sg2;
+    if (shared) {
+        sg1.a = a.x;
+        sg1.a_rows = nullptr;
+        sg1.a_div = 1;
+        sg1.a_nrows = a.T;
+        sg1.out_rows = nullptr;
+        sg1.out_nrows = a.T;
+        sg1.offsets = nullptr;
+        sg1.w = a.sw1;
+        sg1.scales = nullptr;
+        sg1.row_scale = nullptr;
+        sg1.out = ws.sh_h;
+        sg1.R = a.T;
+        sg1.E = 1;
+        sg1.K = a.d;
+        sg1.N = 2 * a.shared_inter;
+        sg1.wtype = MOE_W_FP16;
+        sg1.group = 0;
+        sg1.act = MOE_ACT_SWIGLU;
+        sg1.split = g.split;
+        sg1.tile = 0;
+        sg1.i2f = MOE_I2F_TRICK;
+        sg1.tiles16 = nullptr;
+        sg2 = sg1;
+        sg2.a = ws.sh_h;
+        sg2.w = a.sw2;
+        sg2.out = ws.sh_y;
+        sg2.K = a.shared_inter;
+        sg2.N = a.d;
+        sg2.act = MOE_ACT_NONE;
+        sg2.split = kCombineWaves;
+    }
+    if (shared && R <= 128) {
+        err = launch_gemm_stream_side(g, sg1, stream);
+    } else {
+        // (more routed rows than the side launch takes: the shared GEMM 1 follows on its own)
+        err = launch_gemm_stream(g, stream);
+        if (err == hipSuccess && shared) err = launch_gemm_stream(sg1, stream);
+    }
     if (err != hipSuccess) return err;
 
     CombineParams c;
@@ -458,7 +555,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     c.w_perm = ws.w_perm;
     c.w = a.w2;
     c.scales = a.s2;
-    c.addend = a.addend;
+    c.addend = shared ? ws.sh_y : a.addend;
     c.out = a.out;
     c.part = ws.part;
     c.R = R;
@@ -467,19 +564,22 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     c.N = a.d;
     c.T = a.T;
     c.k = a.k;
-    c.nsplit = decode_combine_split(a.d);
+    c.nsplit = decode_combine_split(a.d, shared);
     // the addend (e.g. shared experts computed on another stream) is first read here
-    if (a.addend_ready) {
+    if (a.addend_ready && !shared) {
         err = hipStreamWaitEvent(stream, (hipEvent_t)a.addend_ready, 0);
         if (err != hipSuccess) return err;
     }
+    const GemmParams* side = shared ? &sg2 : nullptr;
     const bool grouped = a.group != 0;
     switch (a.wtype * 2 + (grouped ? 1 : 0)) {
-        case MOE_W_INT4 * 2 + 0: return combine_launch<MOE_W_INT4, false>(c, stream);
-        case MOE_W_INT4 * 2 + 1: return combine_launch<MOE_W_INT4, true>(c, stream);
-        case MOE_W_INT8 * 2 + 0: return combine_launch<MOE_W_INT8, false>(c, stream);
-        case MOE_W_INT8 * 2 + 1: return combine_launch<MOE_W_INT8, true>(c, stream);
-        case MOE_W_FP16 * 2 + 0: return combine_launch<MOE_W_FP16, false>(c, stream);
+        case MOE_W_INT4 * 2 + 0: return combine_launch<MOE_W_INT4, false>(c, stream, side);
+        case MOE_W_INT4 * 2 + 1: return combine_launch<MOE_W_INT4, true>(c, stream, side);
+        case MOE_W_INT8 * 2 + 0: return combine_launch<MOE_W_INT8, false>(c, stream, side);
+        case MOE_W_INT8 * 2 + 1: return combine_launch<MOE_W_INT8, true>(c, stream, side);
+        case MOE_W_FP16 * 2 + 0:
+            if (shared) return hipErrorInvalidValue;
+            return combine_launch<MOE_W_FP16, false>(c, stream, nullptr);
         default: return hipErrorInvalidValue;
     }
 }

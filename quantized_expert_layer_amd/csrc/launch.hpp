@@ -63,6 +63,11 @@ int gemm_choose_tile(int R, int E, int N, int act, int wtype, bool grouped, int 
 bool gemm_native_supported(int wtype, int act, int group, int tile);
 
 hipError_t launch_gemm_stream(const GemmParams& p, hipStream_t stream);
+// The stream launch of a decode step's first GEMM (integer codes, at most 128 rows) with a
+// dense fp16 GEMM over all rows of `side` in the same launch (offsets, row maps and tile table
+// NULL; side.split == p.split).
+hipError_t launch_gemm_stream_side(const GemmParams& p, const GemmParams& side,
+                                   hipStream_t stream);
 hipError_t launch_gemm_tile(const GemmParams& p, hipStream_t stream);
 
 // ---- decode step (few tokens): gating + sort, GEMM 1, GEMM 2 with the combine ----
@@ -75,6 +80,8 @@ struct DecodeWs {
     int32_t* tiles;          // [1 + kDecodeMaxTiles] tile table (count, then packed tiles)
     uint16_t* h;             // fp16 [R, inter] GEMM 1 output, sorted rows
     float* part;             // fp32 [nsplit, T, d] partial token sums of GEMM 2 (nsplit > 1)
+    uint16_t* sh_h;          // fp16 [T, shared_inter] shared experts' hidden rows (or NULL)
+    uint16_t* sh_y;          // fp16 [T, d] shared experts' output (or NULL)
 };
 
 struct CombineParams {
@@ -101,6 +108,9 @@ struct DecodeArgs {
     const void* w2;
     const uint16_t* s2;
     int wtype, group;
+    const void* sw1;         // shared experts, fp16 packed [d, 2 shared_inter] (gate | up), or NULL
+    const void* sw2;         //   and [shared_inter, d]; SwiGLU, weight 1, every token
+    int shared_inter;
     const uint16_t* addend;
     void* addend_ready;      // hipEvent_t or NULL: waited for before the launch that adds addend
     int32_t* ids;
@@ -109,11 +119,13 @@ struct DecodeArgs {
     void* ws;
 };
 
-// Blocks sharing one 16-column block of the decode step's second GEMM (a power of two).
-int decode_combine_split(int d);
-// Bytes of the decode workspace; with ws and base given, also the part addresses.
-size_t decode_workspace_layout(int T, int k, int E, int d, int inter, int wtype, DecodeWs* ws,
-                               char* base);
+// Blocks sharing one column group of the decode step's second GEMM (a power of two; at least
+// two with shared experts, whose output the reduction launch adds).
+int decode_combine_split(int d, bool shared);
+// Bytes of the decode workspace (shared_inter 0: no shared experts); with ws and base given,
+// also the part addresses.
+size_t decode_workspace_layout(int T, int k, int E, int d, int inter, int wtype, int shared_inter,
+                               DecodeWs* ws, char* base);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace moe

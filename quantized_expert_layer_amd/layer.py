@@ -6,8 +6,9 @@ DeviceLayer owns the packed expert weights in device memory; forward() enqueues
   [-> shared fp16 experts through the same GEMM entry, E = 1]
   -> moe_unpermute_combine
 on one stream, with no host synchronisation.  A step of at most MOE_DECODE_MAX_TOKENS tokens
-(decode / verify) instead makes one moe_decode_layer call (after the shared experts, whose
-output it adds).  Nothing here computes: torch only allocates.
+(decode / verify) instead makes one moe_decode_layer call, or one moe_decode_layer_shared call
+for a layer with shared experts (fp16 routed weights: the shared experts on a side stream, and
+moe_decode_layer adds their output).  Nothing here computes: torch only allocates.
 """
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Tuple
@@ -17,7 +18,8 @@ import numpy as np
 import ctypes
 
 from . import (ACTS, GATES, MOE_DECODE_MAX_ROWS, MOE_DECODE_MAX_TOKENS, WTYPES, MoEError, _ptr,
-               _stream, lib, moe_decode_layer, moe_decode_workspace_size,
+               _stream, lib, moe_decode_layer, moe_decode_layer_shared,
+               moe_decode_shared_workspace_size, moe_decode_workspace_size,
                moe_gemm_workspace_size, moe_grouped_gemm_wq, moe_grouped_gemm_wq_rows,
                moe_pack_wq, moe_permute, moe_permute_workspace_size, moe_route_topk,
                moe_unpermute_combine, new_output)
@@ -134,10 +136,19 @@ class DeviceLayer:
         b["ws"] = new_output(max(wsz, 16), torch.uint8, dev)
         b["pws"] = new_output(max(moe_permute_workspace_size(T, self.k, self.E), 16),
                               torch.uint8, dev)
-        dws = moe_decode_workspace_size(T, self.k, self.E, d, self.inter, self.wtype)
+        if self._shared_in_decode():
+            dws = moe_decode_shared_workspace_size(T, self.k, self.E, d, self.inter, self.wtype,
+                                                   self.shared_inter)
+        else:
+            dws = moe_decode_workspace_size(T, self.k, self.E, d, self.inter, self.wtype)
         if dws:
             b["dws"] = new_output(dws, torch.uint8, dev)
         return Workspace(T=T, bufs=b)
+
+    def _shared_in_decode(self) -> bool:
+        """Whether a decode step computes the shared experts inside its own launches
+        (moe_decode_layer_shared: integer-coded routed weights)."""
+        return self.shared is not None and self.wtype != "fp16"
 
     def _side_stream(self):
         """The stream the shared experts of a decode step run on (one per layer)."""
@@ -146,17 +157,18 @@ class DeviceLayer:
             self._side = torch.cuda.Stream(device=self.device)
         return self._side
 
-    def _shared_calls(self, b, x, T):
+    def _shared_calls(self, b, x, T, shared=None):
         """(name, C function, args) of the shared experts (fp16, E = 1) into b["sh_y"]."""
         L, st = lib(), None
+        sw1, sw2 = shared if shared is not None else self.shared
         return [
             ("shared1", L.moe_grouped_gemm_wq, (_ptr(x), _ptr(b["sh_off"]), T, 1, self.d,
-                                                2 * self.shared_inter, _ptr(self.shared[0]),
+                                                2 * self.shared_inter, _ptr(sw1),
                                                 None, 2, 0, 2, None, _ptr(b["sh_h"]), None,
                                                 _ptr(b["ws"]), b["ws"].numel(), st)),
             ("shared2", L.moe_grouped_gemm_wq, (_ptr(b["sh_h"]), _ptr(b["sh_off"]), T, 1,
                                                 self.shared_inter, self.d,
-                                                _ptr(self.shared[1]), None, 2, 0, 0, None,
+                                                _ptr(sw2), None, 2, 0, 0, None,
                                                 _ptr(b["sh_y"]), None, _ptr(b["ws"]),
                                                 b["ws"].numel(), st)),
         ]
@@ -172,6 +184,14 @@ class DeviceLayer:
         b = ws.bufs
         path = self.gemm_path
         if self.uses_decode(T, gate_in_gemm):
+            if self._shared_in_decode():
+                moe_decode_layer_shared(logits, x, self.k, self.gate_mode, self.inter, self.act,
+                                        self.w1, self.s1, self.w2, self.s2, self.wtype,
+                                        self.group, self.shared[0], self.shared[1],
+                                        self.shared_inter, topk_ids=b["ids"], topk_w=b["w"],
+                                        out=b["out"], ws=b["dws"], stream=stream,
+                                        active=active)
+                return b["out"]
             addend, ready = None, None
             if self.shared is not None:
                 # the shared experts run on a side stream beside the routed step; the decode
@@ -237,9 +257,11 @@ class DeviceLayer:
     def plan(self, ws: Workspace, x, logits, weights=None, gate_in_gemm: bool = True,
              stream=None, active=None) -> "LayerPlan":
         """Pre-marshal every C call of one forward() for fixed buffers, so that a step is
-        just the C calls (no per-call Python argument checks).  `weights` = (w1, w2) device
-        tensors in the packed layout (defaults to this layer's own)."""
-        w1, w2 = weights if weights is not None else (self.w1, self.w2)
+        just the C calls (no per-call Python argument checks).  `weights` = (w1, w2) or, for a
+        layer with shared experts, (w1, w2, shared w1, shared w2): device tensors in the packed
+        layout (defaults to this layer's own)."""
+        w1, w2 = weights[:2] if weights is not None else (self.w1, self.w2)
+        shw = tuple(weights[2:4]) if weights is not None and len(weights) == 4 else self.shared
         b, L, T = ws.bufs, lib(), ws.T
         st = _stream(stream)
         path = self.gemm_path
@@ -257,8 +279,17 @@ class DeviceLayer:
         scatter = self._scatter_out(gate_in_gemm, active is not None)
         R = T * self.k
         rs = _ptr(b["wp"]) if gate_in_gemm else None
-        keep = (opts, x, logits, w1, w2, self.s1, self.s2, self.shared, ws, active)
+        keep = (opts, x, logits, w1, w2, self.s1, self.s2, self.shared, shw, ws, active)
         if self.uses_decode(T, gate_in_gemm):
+            if self._shared_in_decode():
+                calls = [("decode", L.moe_decode_layer_shared,
+                          (_ptr(logits), _ptr(active), _ptr(x), T, self.E, self.k,
+                           GATES[self.gate_mode], self.d, self.inter, ac, _ptr(w1),
+                           _ptr(self.s1), _ptr(w2), _ptr(self.s2), wt, self.group,
+                           _ptr(shw[0]), _ptr(shw[1]), self.shared_inter,
+                           _ptr(b["ids"]), _ptr(b["w"]), _ptr(b["out"]), _ptr(b["dws"]),
+                           b["dws"].numel(), st))]
+                return LayerPlan(calls, b["out"], keep=keep)
             calls = []
             addend, ready = None, None
             if self.shared is not None:
@@ -283,7 +314,8 @@ class DeviceLayer:
 
                 ss = _stream(side)
                 calls = [("fork", do_fork, ())]
-                calls += [(n, fn, args[:-1] + (ss,)) for n, fn, args in self._shared_calls(b, x, T)]
+                calls += [(n, fn, args[:-1] + (ss,))
+                          for n, fn, args in self._shared_calls(b, x, T, shw)]
                 calls.append(("join", do_join, ()))
                 ready = join.cuda_event
                 keep = keep + (side, fork, join)
@@ -326,12 +358,12 @@ class DeviceLayer:
         if self.shared is not None:
             calls += [
                 ("shared1", L.moe_grouped_gemm_wq, (_ptr(x), _ptr(b["sh_off"]), T, 1, self.d,
-                                                    2 * self.shared_inter, _ptr(self.shared[0]),
+                                                    2 * self.shared_inter, _ptr(shw[0]),
                                                     None, 2, 0, 2, None, _ptr(b["sh_h"]), ob,
                                                     wsp, wsn, st)),
                 ("shared2", L.moe_grouped_gemm_wq, (_ptr(b["sh_h"]), _ptr(b["sh_off"]), T, 1,
                                                     self.shared_inter, self.d,
-                                                    _ptr(self.shared[1]), None, 2, 0, 0, None,
+                                                    _ptr(shw[1]), None, 2, 0, 0, None,
                                                     _ptr(b["sh_y"]), ob, wsp, wsn, st)),
             ]
             addend = b["sh_y"]

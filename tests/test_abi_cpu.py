@@ -350,6 +350,51 @@ def test_decode_layer_validation():
         assert f(*args(T=64, k=8, E=16, wsb=big)) == q.MOE_ERR_NO_DEVICE
 
 
+def test_decode_shared_validation():
+    """moe_decode_layer_shared validates as moe_decode_layer, plus its shared-expert arguments:
+    a positive shared_inter that is a multiple of 128, both shared weights, 16-byte aligned, and
+    integer-coded routed weights."""
+    L = q.lib()
+    f = L.moe_decode_layer_shared
+    ws_need = L.moe_decode_shared_workspace_size(4, 2, 8, 256, 512, 0, 384)
+    # the shared experts' hidden rows and output rows on top of the routed step's workspace
+    assert ws_need >= L.moe_decode_workspace_size(4, 2, 8, 256, 512, 0) + 2 * 4 * (384 + 256)
+
+    def args(**kw):
+        d = dict(logits=FAKE, active=None, x=FAKE, T=4, E=8, k=2, gate=0, d=256, inter=512,
+                 act=2, w1=FAKE, s1=FAKE, w2=FAKE, s2=FAKE, wt=0, g=128, sw1=FAKE, sw2=FAKE,
+                 si=384, ids=FAKE, w=FAKE, out=FAKE, ws=FAKE, wsb=ws_need, stream=None)
+        d.update(kw)
+        return [d[n] for n in ("logits", "active", "x", "T", "E", "k", "gate", "d", "inter",
+                               "act", "w1", "s1", "w2", "s2", "wt", "g", "sw1", "sw2", "si",
+                               "ids", "w", "out", "ws", "wsb", "stream")]
+
+    assert f(*args(k=9)) == q.MOE_ERR_INVALID
+    assert f(*args(si=0)) == q.MOE_ERR_INVALID
+    assert f(*args(si=-128)) == q.MOE_ERR_INVALID
+    assert f(*args(si=200)) == q.MOE_ERR_UNSUPPORTED                     # shared_inter % 128
+    assert f(*args(sw1=None)) == q.MOE_ERR_INVALID
+    assert f(*args(sw2=None)) == q.MOE_ERR_INVALID
+    assert f(*args(sw1=MIS)) == q.MOE_ERR_INVALID
+    assert f(*args(sw2=MIS)) == q.MOE_ERR_INVALID
+    assert f(*args(wt=2, g=0, s1=None, s2=None)) == q.MOE_ERR_UNSUPPORTED  # fp16 routed weights
+    assert f(*args(d=200)) == q.MOE_ERR_UNSUPPORTED
+    assert f(*args(ws=None)) == q.MOE_ERR_WORKSPACE
+    assert f(*args(wsb=ws_need - 1)) == q.MOE_ERR_WORKSPACE
+    # the routed step's workspace is not enough
+    assert f(*args(wsb=L.moe_decode_workspace_size(4, 2, 8, 256, 512, 0))) == q.MOE_ERR_WORKSPACE
+    assert f(*args(T=0, logits=None, x=None, ids=None, w=None, out=None, ws=None)) == q.MOE_OK
+    if not gpu_available():
+        assert f(*args()) == q.MOE_ERR_NO_DEVICE
+        # more routed rows than the side launch takes (T * k > 128) is accepted too
+        big = L.moe_decode_shared_workspace_size(64, 8, 16, 256, 512, 0, 384)
+        assert f(*args(T=64, k=8, E=16, wsb=big)) == q.MOE_ERR_NO_DEVICE
+    assert L.moe_decode_shared_workspace_size(4, 2, 8, 256, 512, 0, 0) == 0
+    assert L.moe_decode_shared_workspace_size(4, 2, 8, 256, 512, 0, 200) == 0
+    assert L.moe_decode_shared_workspace_size(4, 2, 8, 256, 512, 2, 384) == 0    # fp16 routed
+    assert L.moe_decode_shared_workspace_size(65, 2, 8, 256, 512, 0, 384) == 0
+
+
 def test_decode_noalloc_rejects_a_step_beyond_its_scratch():
     """moe_decode_layer_noalloc validates as moe_decode_layer, then refuses a step whose workspace
     exceeds its scratch array, before touching a device."""

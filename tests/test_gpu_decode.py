@@ -19,7 +19,14 @@ TINY = synth.get_config("tiny")
 MAX_ROWS = dataclasses.replace(TINY, name="tiny_k8", cfg_id=101, k=8, T_list=(64,))
 MAX_EXPERTS = dataclasses.replace(TINY, name="wide_e256", cfg_id=102, E=256, k=8, inter=128,
                                   T_list=(64,))
-CONFIGS = {c.name: c for c in (MAX_ROWS, MAX_EXPERTS)}
+# shared experts inside the decode launches: 2 x 64 intermediate columns (the second GEMM's
+# K = 128 leaves most of its eight K slices empty), and with more routed rows (T * k = 512) than
+# the first launch takes beside them
+TINY_SHARED = dataclasses.replace(TINY, name="tiny_shared", cfg_id=103, n_shared=2,
+                                  shared_inter=64)
+TINY_SHARED_K8 = dataclasses.replace(TINY_SHARED, name="tiny_shared_k8", cfg_id=104, k=8,
+                                     T_list=(64,))
+CONFIGS = {c.name: c for c in (MAX_ROWS, MAX_EXPERTS, TINY_SHARED, TINY_SHARED_K8)}
 
 
 def _cfg(name):
@@ -48,7 +55,13 @@ DECODE_CASES = [
     ("mt_encoder", 8, "int8"),
     ("mt_encoder", 8, "fp16"),
     ("qwen15_moe", 17, None),      # SwiGLU, group 128, k = 4
-    ("dsv2_lite", 9, None),        # + shared experts as the addend, k = 6
+    ("dsv2_lite", 9, None),        # + shared experts in the same launches, k = 6
+    ("dsv2_lite", 9, "int8"),
+    ("dsv2_lite", 32, None),       # 192 routed rows: the shared GEMM 1 as a launch of its own
+    ("tiny_shared", 16, None),
+    ("tiny_shared", 16, "int8"),
+    ("tiny_shared", 16, "fp16"),   # fp16 routed weights: shared experts on a side stream
+    ("tiny_shared_k8", 64, None),
     ("phi35_moe", 1, None),
     ("phi35_moe", 17, None),
     ("tiny_k8", 64, None),         # 512 routed rows: every expert takes every token
@@ -74,7 +87,7 @@ def test_decode_layer_matches_oracle(name, T, wtype):
 
 
 @pytest.mark.parametrize("name,T", [("qwen15_moe", 17), ("dsv2_lite", 9), ("phi35_moe", 1),
-                                    ("mt_encoder", 8)])
+                                    ("mt_encoder", 8), ("tiny_shared_k8", 64)])
 def test_decode_layer_agrees_with_the_five_calls(name, T):
     """Only the fp16 rounding of each expert's output row differs from the five-call path."""
     inp, fused = _layer(name, T)
@@ -89,7 +102,7 @@ def test_decode_layer_agrees_with_the_five_calls(name, T):
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 16), ("dsv2_lite", 9), ("mt_encoder", 8),
-                                    ("phi35_moe", 1)])
+                                    ("phi35_moe", 1), ("tiny_shared", 16)])
 def test_decode_layer_is_deterministic_and_token_order_equivariant(name, T):
     """Bit-identical on repeat, and (every expert holding at most 16 rows here, so a row's
     contributions land in the same place whatever its position) under a token permutation."""
@@ -129,16 +142,18 @@ def test_decode_workspace_is_reusable_across_token_counts():
     assert_layer_close(outs[1], oracle.moe_layer(inp5), "T=5 in the T=17 workspace")
 
 
-def test_decode_layer_replays_from_a_graph():
+@pytest.mark.parametrize("name,T,wtype", [("dsv2_lite", 9, None), ("tiny_shared", 16, "fp16"),
+                                          ("tiny_shared_k8", 64, None)])
+def test_decode_layer_replays_from_a_graph(name, T, wtype):
     """Captured once, replayed several times with eager work in between: every replay gives
-    the eager output."""
+    the eager output (shared experts in the decode launches; on a side stream that the graph
+    forks and joins, for fp16 routed weights; the shared GEMM 1 as a launch of its own)."""
     import torch
 
-    name, T = "dsv2_lite", 9
-    inp, layer = _layer(name, T)
+    inp, layer = _layer(name, T, wtype)
     x, L = dev(inp.x), dev(inp.logits)
     ws = layer.workspace(T)
-    case(f"decode graph {name} T={T}")
+    case(f"decode graph {name} T={T} wtype={inp.wtype}")
     want = host(layer.forward(x, L, ws=ws)).copy()
     s = torch.cuda.Stream()
     plan = layer.plan(ws, x, L, stream=s)
