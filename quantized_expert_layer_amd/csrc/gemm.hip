@@ -92,6 +92,7 @@ template <int WT> constexpr int tile_kc() { return WT == MOE_W_FP16 ? 64 : 128; 
 // ahead), two for fp16 weights (register-staged).
 template <int WT> constexpr int tile_a_stages() { return WT == MOE_W_FP16 ? 2 : 3; }
 
+
 // Epilogue staging: row stride (halves) of a wave's output region in LDS, padded by 16 bytes
 // so the 16 rows of one fragment store start in different banks.
 template <int ACT, int NS> constexpr int tile_epi_stride() {
@@ -217,8 +218,14 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         asrc[i] = (const u32x4*)(p.a + (size_t)a_source_row(p, row0 + min(r, rows - 1)) * K) + c;
         adst[i] = r * KC + ((c ^ (r & (CPR - 1))) * 8);
     }
-    // two register sets: the A stage two ahead is loaded while the one ahead waits to be stored
-    u32x4 areg[2][ACH];
+    // WD weight buffers and (register-staged path) WD A register sets, which rotate statically
+    // (the stage loops below run WD stages per iteration; copying a buffer whose loads are in
+    // flight would make the compiler wait for every outstanding load).  A stage's weights are
+    // loaded WD - 1 stages ahead and its A rows WD stages ahead, then stored to the idle LDS
+    // buffer at the end of the stage before.  Four-deep rings on the fp16 shapes with few
+    // blocks (the shared experts of a 288-token step) measured no faster than two.
+    constexpr int WD = 2;
+    u32x4 areg[WD][ACH];
     auto load_a = [&](int set, int st) {
 #pragma unroll
         for (int i = 0; i < ACH; ++i)
@@ -233,11 +240,8 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
 
     // group scales: one per (column block, super-block) -- a super-block never spans groups
     constexpr int SCS = GROUPED ? SBPS : 1;
-    // Two weight buffers that alternate statically (the stage loops below run two stages per
-    // iteration): copying a buffer whose loads are in flight would make the compiler wait for
-    // every outstanding load, the A stages two ahead included, at the top of each stage.
-    u32x4 bbuf[2][NS][SBPS];
-    uint32_t sbuf[2][NS][SCS] = {};
+    u32x4 bbuf[WD][NS][SBPS];
+    uint32_t sbuf[WD][NS][SCS] = {};
     auto load_b = [&](u32x4 (&b)[NS][SBPS], uint32_t (&sc)[NS][SCS], int st) {
 #pragma unroll
         for (int c = 0; c < NS; ++c) {
@@ -366,21 +370,24 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         const int ns = nstage / KG;
         const int s0 = kg * ns;
         load_a(0, s0);
-        load_b(bbuf[0], sbuf[0], s0);
-        load_a(1, s0 + min(1, ns - 1));
+#pragma unroll
+        for (int u = 0; u < WD - 1; ++u) load_b(bbuf[u], sbuf[u], s0 + min(u, ns - 1));
+#pragma unroll
+        for (int u = 1; u < WD; ++u) load_a(u, s0 + min(u, ns - 1));
         store_a(0, 0);
         __syncthreads();
 
         // The stage body is branch-free: the last stages prefetch (and store to the idle LDS
         // buffer) copies of the last one, so the compiler can count outstanding loads exactly
         // and keep the following stages' loads in flight across the whole compute of this one.
-        // The loop runs two stages per iteration so the A register sets and the weight buffers
-        // alternate statically.
+        // Stage st computes from weight buffer st % WD and refills the buffer stage st - 1
+        // used with stage st + WD - 1; it refills A set st % WD (stored to LDS before the
+        // stage) with stage st + WD and stores set (st + 1) % WD for the next stage.
         auto stage = [&](int st, int set_new, int set_old, const u32x4 (&bc)[NS][SBPS],
                          const uint32_t (&sc)[NS][SCS], u32x4 (&bn)[NS][SBPS],
                          uint32_t (&sn)[NS][SCS]) {
-            const int nxt = s0 + min(st + 1, ns - 1);
-            load_a(set_new, s0 + min(st + 2, ns - 1));
+            const int nxt = s0 + min(st + WD - 1, ns - 1);
+            load_a(set_new, s0 + min(st + WD, ns - 1));
             load_b(bn, sn, nxt);
             // keep the prefetch at the top (see above)
             __builtin_amdgcn_sched_barrier(0);
@@ -388,12 +395,24 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
             store_a(set_old, (st + 1) & 1);
             __syncthreads();
         };
-        for (int st = 0; st < ns; st += 2) {
-            stage(st, 0, 1, bbuf[0], sbuf[0], bbuf[1], sbuf[1]);
-            if (st + 1 < ns) stage(st + 1, 1, 0, bbuf[1], sbuf[1], bbuf[0], sbuf[0]);
+        static_assert(WD % 2 == 0, "the LDS buffers alternate with the stage parity");
+        // whole rounds of WD stages with no branch between them (a join of paths with different
+        // loads in flight makes the compiler wait for nearly all of them), then the rest
+        int st = 0;
+        for (; st + WD <= ns; st += WD) {
+#pragma unroll
+            for (int u = 0; u < WD; ++u)
+                stage(st + u, u, (u + 1) % WD, bbuf[u], sbuf[u], bbuf[(u + WD - 1) % WD],
+                      sbuf[(u + WD - 1) % WD]);
         }
 #pragma unroll
-        for (int set = 0; set < 2; ++set)
+        for (int u = 0; u < WD - 1; ++u) {
+            if (st + u < ns)
+                stage(st + u, u, (u + 1) % WD, bbuf[u], sbuf[u], bbuf[(u + WD - 1) % WD],
+                      sbuf[(u + WD - 1) % WD]);
+        }
+#pragma unroll
+        for (int set = 0; set < WD; ++set)
 #pragma unroll
             for (int i = 0; i < ACH; ++i) consume(areg[set][i]);
         if constexpr (KG > 1) {
@@ -419,14 +438,16 @@ __device__ __forceinline__ void tile_body(const GemmParams& p, f16* __restrict__
         }
     }
 
-    // the last stage prefetched a repeat of itself, which nothing reads
+    // the last stages prefetched repeats of the last one, which nothing reads
 #pragma unroll
-    for (int c = 0; c < NS; ++c) {
+    for (int b = 0; b < WD; ++b)
 #pragma unroll
-        for (int q = 0; q < SBPS; ++q) { consume(bbuf[0][c][q]); consume(bbuf[1][c][q]); }
+        for (int c = 0; c < NS; ++c) {
 #pragma unroll
-        for (int q = 0; q < SCS; ++q) { consume(sbuf[0][c][q]); consume(sbuf[1][c][q]); }
-    }
+            for (int q = 0; q < SBPS; ++q) consume(bbuf[b][c][q]);
+#pragma unroll
+            for (int q = 0; q < SCS; ++q) consume(sbuf[b][c][q]);
+        }
 
     if constexpr (KG > 1) {
         if (kg > 0) return;                      // group 0 writes the tile
@@ -698,11 +719,14 @@ static hipError_t tile_launch(const GemmParams& p, hipStream_t stream) {
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
     // Which operand to keep XCD-local: re-reading the activations once per column group
     // costs (ncbg - 1) * R*K*2 bytes; re-reading weights across the XCDs an expert's tiles
-    // span costs about the weight bytes of the active experts once more.
+    // span costs about the weight bytes of the active experts once more.  A single dense
+    // expert (E = 1: the shared experts) keeps its weights XCD-local: its m-tiles all read
+    // the same weights, which the other order fetches once per m-tile (measured 21 against
+    // 25 us on the 288 x 2048 x 5632 fp16 GEMM of a DeepSeek-V2-Lite-shaped layer).
     const int wbits = (WT == MOE_W_INT4) ? 4 : (WT == MOE_W_INT8 ? 8 : 16);
     const double a_bytes = 2.0 * p.R * p.K;
     const double w_bytes = (double)active * p.K * p.N * wbits / 8.0;
-    const int a_major = a_bytes * (ncbg - 1) > w_bytes ? 1 : 0;
+    const int a_major = (p.E > 1 && a_bytes * (ncbg - 1) > w_bytes) ? 1 : 0;
     // fp16 weights on a grid smaller than the machine: split each tile's K stages over 2 or 4
     // groups of 4 waves in the block (the register-staged A path takes any split that divides
     // the stages; integer codes keep one group)
