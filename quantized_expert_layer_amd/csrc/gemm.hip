@@ -717,16 +717,30 @@ static hipError_t tile_launch(const GemmParams& p, hipStream_t stream) {
     const long real = (long)mt_ub * ncbg;
     const long grid = (real + 7) / 8 * 8;
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
-    // Which operand to keep XCD-local: re-reading the activations once per column group
-    // costs (ncbg - 1) * R*K*2 bytes; re-reading weights across the XCDs an expert's tiles
-    // span costs about the weight bytes of the active experts once more.  A single dense
-    // expert (E = 1: the shared experts) keeps its weights XCD-local: its m-tiles all read
-    // the same weights, which the other order fetches once per m-tile (measured 21 against
-    // 25 us on the 288 x 2048 x 5632 fp16 GEMM of a DeepSeek-V2-Lite-shaped layer).
+    // Which operand to keep XCD-local, by the bytes each order fetches into the XCDs' L2s
+    // (4 MiB each; the logical tiles are split into 8 contiguous ranges, one per XCD):
+    //   m-tile major: the activation rows once; an expert's weights once per XCD range its
+    //     tiles cross (its m-tiles re-read them from the L2), or once per m-tile where one
+    //     expert's weights exceed an L2;
+    //   column-group major: the weights once; the activation rows once per XCD (at most one
+    //     per column group), or once per column group where they exceed an L2.
+    // Measured: a single dense expert (the fp16 shared experts, 288 x 2048 x 5632) takes
+    // 21 us column-group major against 25 us (its m-tiles fetch every weight once each); the
+    // mid-sized routed GEMMs (about one m-tile per expert) read their rows once m-tile major.
+    // Well above the ridge point (300 flop per byte) the re-reads come from the last-level
+    // cache under MFMA-bound work and the order measured the same (Phi-3.5-MoE-shaped prefill:
+    // 1840 against 1855 us): there the m-tile-major order stays.
     const int wbits = (WT == MOE_W_INT4) ? 4 : (WT == MOE_W_INT8 ? 8 : 16);
-    const double a_bytes = 2.0 * p.R * p.K;
-    const double w_bytes = (double)active * p.K * p.N * wbits / 8.0;
-    const int a_major = (p.E > 1 && a_bytes * (ncbg - 1) > w_bytes) ? 1 : 0;
+    const double l2 = 4.0 * 1024 * 1024;
+    const double a_bytes = 2.0 * (p.a_rows ? min(p.a_nrows, p.R) : p.R) * p.K;  // distinct rows
+    const double w_e = (double)p.K * p.N * wbits / 8.0;
+    const double w_bytes = active * w_e;
+    const double m_e = fmax(1.0, (double)p.R / ((double)active * BM));      // m-tiles / expert
+    const double xcd_range = fmax(1.0, (double)real / 8.0);
+    const double s_w = w_e > l2 ? m_e : fmin(m_e, 1.0 + (m_e * ncbg - 1.0) / xcd_range);
+    const double s_a = a_bytes > l2 ? (double)ncbg : fmin(8.0, (double)ncbg);
+    const bool mfma_bound = 2.0 * p.R * p.K * p.N > 300.0 * (w_bytes + a_bytes);
+    const int a_major = (mfma_bound || a_bytes + w_bytes * s_w < w_bytes + a_bytes * s_a) ? 1 : 0;
     // fp16 weights on a grid smaller than the machine: split each tile's K stages over 2 or 4
     // groups of 4 waves in the block (the register-staged A path takes any split that divides
     // the stages; integer codes keep one group)
