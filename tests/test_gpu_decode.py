@@ -244,3 +244,21 @@ def test_decode_waits_for_an_addend_made_on_another_stream():
     got = host(q.moe_decode_layer(L, x, addend=late, addend_ready=ready, **kw)[0])
     torch.cuda.synchronize()
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("name,T,finished", [("tiny_shared", 16, "all"), ("tiny_shared", 16, "half"),
+                                             ("tiny_shared_k8", 64, "all")])
+def test_decode_shared_with_finished_tokens(name, T, finished):
+    """Batch pruning with the shared experts inside the decode launches: a finished token takes
+    no routed expert but still gets the shared experts' output; with every token finished the
+    routed blocks find no tile and the output is the shared experts' alone."""
+    inp, layer = _layer(name, T)
+    active = np.zeros(T, dtype=bool) if finished == "all" else (np.arange(T) % 2 == 0)
+    case(f"decode shared pruned {name} T={T} finished={finished}")
+    x, L = dev(inp.x), dev(inp.logits)
+    ws = layer.workspace(T)
+    out = host(layer.forward(x, L, ws=ws, active=dev(active.astype(np.uint8))))
+    ref = oracle.moe_layer(inp, active=active)
+    assert_layer_close(out, ref, f"decode shared pruned {name} T={T}")
+    ids = host(ws.bufs["ids"])
+    assert np.all(ids[~active] == -1)
