@@ -223,6 +223,24 @@ def test_fp16_weights_and_zero_row_experts(path, tile, K):
         assert_layer_close(host(out), ref, "fp16 gemm")
 
 
+@pytest.mark.parametrize("R", [288, 100, 1])
+@pytest.mark.parametrize("act", ["none", "relu", "swiglu"])
+def test_dense_fp16_expert_small_grid(R, act):
+    # one dense fp16 expert (E = 1, the shared experts' form) on a grid of a few tiles: without
+    # SwiGLU it runs 64x64 tiles, with SwiGLU 64x128; both column-group major, K split over
+    # wave groups; ragged last m-tile at R = 100, a single row at R = 1
+    K, N = 512, 512
+    rng = np.random.default_rng(R)
+    w = (rng.standard_normal((1, K, N)) * 0.05).astype(np.float16)
+    a = rng.standard_normal((R, K)).astype(np.float16)
+    off = np.array([0, R], np.int32)
+    case(f"dense fp16 E=1 R={R} act={act}")
+    out = q.moe_grouped_gemm_wq(dev(a), dev(off), 1, K, N, dev(q.moe_pack_wq(w, "fp16")), None,
+                                "fp16", 0, act, path=2)
+    ref = oracle.grouped_gemm(a, off, w.astype(np.float64), act)
+    assert_layer_close(host(out), ref, "dense fp16 gemm")
+
+
 def test_gemm_rows_beyond_offsets_are_untouched():
     E, K, N = 2, 128, 32
     codes, scales, _, a = _gemm_case(E, K, N, "int4", 0, 20, 1, seed=4)
