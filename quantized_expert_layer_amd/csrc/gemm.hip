@@ -617,12 +617,13 @@ int gemm_choose_split(int R, int E, int K, int N, int wtype, int act, int forced
     const int active = R < E ? R : E;
     const int nbo = (act == MOE_ACT_SWIGLU) ? N / 32 : N / 16;
     const long blocks = (long)active * cdiv(R, active > 0 ? active * 16 : 16) * (nbo / stream_opb(N, act, wtype));
-    // Split only a launch with fewer than two blocks per CU: with a few hundred streams or
-    // more, extra waves per SIMD measured no faster (the streams already share each SIMD's
-    // VALU issue for the in-register dequantization), and each slice keeps at least 8
-    // super-blocks so its load ring stays filled.
+    // Split only a launch with fewer than four blocks per CU: with a few thousand streams,
+    // extra waves per SIMD measured no faster (the streams already share each SIMD's VALU
+    // issue for the in-register dequantization), while a single-token step (two experts of
+    // 4096 x 12800: 400 blocks) took 35.0 against 38.2 us split four ways instead of two; each
+    // slice keeps at least 8 super-blocks so its load ring stays filled.
     int s = 1;
-    while (s < MOE_MAX_SPLIT_K && blocks * s < 512 && nSB / (2 * s) >= 8) s *= 2;
+    while (s < MOE_MAX_SPLIT_K && blocks * s < 1024 && nSB / (2 * s) >= 8) s *= 2;
     return s;
 }
 
