@@ -349,7 +349,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gemm_combine_side_kernel(C
         combine_body<WT, GROUPED, PF, PA, NCB, 1>(p, blockIdx.x, dyn);
     else
         stream_body<MOE_W_FP16, MOE_ACT_NONE, false, 8, 2, 1, 64 + WT * 2 + (GROUPED ? 1 : 0)>(
-            ps, ngo_s, blockIdx.x - nb, (f32x4*)dyn);
+            ps, ngo_s, blockIdx.x - nb, blockDim.x / kWave,
+            __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), (f32x4*)dyn);
 }
 
 // ------------------------------------------------------------------------------------

@@ -43,23 +43,39 @@ __device__ __forceinline__ f32x4 load4_scale(const uint16_t* src) {
 template <int WT, int ACT, bool GROUPED, int PF, int PA, int OPB>
 __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_kernel(GemmParams p, int ngo) {
     extern __shared__ f32x4 red[];          // [S - 1][NCB][64] partial sums of waves 1..S-1
-    stream_body<WT, ACT, GROUPED, PF, PA, OPB>(p, ngo, blockIdx.x, red);
+    // wave index, held in a scalar register (the compiler cannot see it is wave-uniform)
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    stream_body<WT, ACT, GROUPED, PF, PA, OPB>(p, ngo, blockIdx.x, blockDim.x / kWave, w, red);
 }
 
 // The stream launch with a second, dense GEMM beside it ([S] Method step 5: the step's expert
-// sub-computations in one launch): blocks [0, nb) run the grouped GEMM p, the rest the fp16
-// GEMM ps over all of its rows (the decode step's shared experts, E = 1, every token).
+// sub-computations in one launch): workgroups [0, nwg) run the grouped GEMM p, the rest the fp16
+// GEMM ps over all of its rows (the decode step's shared experts, E = 1, every token), each
+// dense block's K split over the workgroup's W waves.  With p unsplit (rs == 1) each wave of a
+// grouped workgroup runs a block of its own (block W * workgroup + wave), so the dense GEMM's
+// long K streams still get W waves; otherwise every workgroup runs one block of rs == W waves.
 constexpr int kDenseSidePF = 8;
+constexpr int kDenseSideWaves = 4;
 template <int WT, int ACT, bool GROUPED, int PF, int PA, int OPB, int SACT>
 __global__ __launch_bounds__(64 * MOE_MAX_SPLIT_K) void gemm_stream_side_kernel(GemmParams p, int ngo,
-                                                                              int nb, GemmParams ps,
+                                                                              int nb, int nwg,
+                                                                              GemmParams ps,
                                                                               int ngo_s) {
     extern __shared__ f32x4 red[];
     constexpr int kTagSide = 16 + ((((WT * 3 + ACT) * 2 + (GROUPED ? 1 : 0)) * 16 + PF) * 4 + OPB) * 3 + SACT;
-    if ((int)blockIdx.x < nb)
-        stream_body<WT, ACT, GROUPED, PF, PA, OPB, 1 + SACT>(p, ngo, blockIdx.x, red);
-    else
-        stream_body<MOE_W_FP16, SACT, false, kDenseSidePF, 2, 1, kTagSide>(ps, ngo_s, blockIdx.x - nb, red);
+    const int W = blockDim.x / kWave;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if ((int)blockIdx.x < nwg) {
+        if (p.split == 1) {
+            const int b = (int)blockIdx.x * W + w;
+            if (b < nb) stream_body<WT, ACT, GROUPED, PF, PA, OPB, 1 + SACT>(p, ngo, b, 1, 0, red);
+        } else {
+            stream_body<WT, ACT, GROUPED, PF, PA, OPB, 1 + SACT>(p, ngo, blockIdx.x, W, w, red);
+        }
+    } else {
+        stream_body<MOE_W_FP16, SACT, false, kDenseSidePF, 2, 1, kTagSide>(
+            ps, ngo_s, (int)blockIdx.x - nwg, W, w, red);
+    }
 }
 
 // ------------------------------------------------------------------------------------
@@ -630,18 +646,22 @@ int gemm_choose_split(int R, int E, int K, int N, int wtype, int act, int forced
 template <int WT, int ACT, bool GROUPED, int PF, int OPB>
 static hipError_t side_launch(const GemmParams& p, int ngo, long blocks, const GemmParams& ps,
                               hipStream_t stream) {
-    // the dense GEMM's grid: 16-row m-tiles of its R rows x one 16-column output block each
+    // the dense GEMM's grid: 16-row m-tiles of its R rows x one 16-column output block each,
+    // K split over the workgroup's W waves (the grouped GEMM's split, or kDenseSideWaves waves
+    // sharing a workgroup with W unsplit grouped blocks)
+    const int W = p.split == 1 ? kDenseSideWaves : p.split;
+    const long nwg = p.split == 1 ? (blocks + W - 1) / W : blocks;
     const int nbo_s = (ps.act == MOE_ACT_SWIGLU) ? ps.N / 32 : ps.N / 16;
     const long blocks_s = (long)cdiv(ps.R, 16) * nbo_s;
-    if (blocks + blocks_s > 0x7fffffffL || ps.split != p.split) return hipErrorInvalidValue;
+    if (nwg + blocks_s > 0x7fffffffL) return hipErrorInvalidValue;
     constexpr int NCB = (ACT == MOE_ACT_SWIGLU) ? 2 * OPB : OPB;
     const int ncb_s = (ps.act == MOE_ACT_SWIGLU) ? 2 : 1;
-    const size_t lds = (size_t)(p.split - 1) * (NCB > ncb_s ? NCB : ncb_s) * 64 * sizeof(f32x4);
-    const unsigned grid = (unsigned)(blocks + blocks_s), threads = 64u * (unsigned)p.split;
+    const size_t lds = (size_t)(W - 1) * (NCB > ncb_s ? NCB : ncb_s) * 64 * sizeof(f32x4);
+    const unsigned grid = (unsigned)(nwg + blocks_s), threads = 64u * (unsigned)W;
     // the shared experts' first GEMM: SwiGLU (the only activation built for the side GEMM)
     if (ps.act != MOE_ACT_SWIGLU) return hipErrorInvalidValue;
     gemm_stream_side_kernel<WT, ACT, GROUPED, PF, 2, OPB, MOE_ACT_SWIGLU><<<grid, threads, lds, stream>>>(
-        p, ngo, (int)blocks, ps, nbo_s);
+        p, ngo, (int)blocks, (int)nwg, ps, nbo_s);
     return hipGetLastError();
 }
 

@@ -64,8 +64,9 @@ bool gemm_native_supported(int wtype, int act, int group, int tile);
 
 hipError_t launch_gemm_stream(const GemmParams& p, hipStream_t stream);
 // The stream launch of a decode step's first GEMM (integer codes, at most 128 rows) with a
-// dense fp16 GEMM over all rows of `side` in the same launch (offsets, row maps and tile table
-// NULL; side.split == p.split).
+// dense fp16 SwiGLU GEMM over all rows of `side` in the same launch (offsets, row maps and tile
+// table NULL; side.split is not read: its K is split over the launch's waves per workgroup,
+// p.split, or 4 when p is unsplit).
 hipError_t launch_gemm_stream_side(const GemmParams& p, const GemmParams& side,
                                    hipStream_t stream);
 hipError_t launch_gemm_tile(const GemmParams& p, hipStream_t stream);

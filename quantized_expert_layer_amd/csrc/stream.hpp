@@ -38,20 +38,18 @@ __device__ __forceinline__ int out_dest_row(const GemmParams& p, int gp) {
 //           is the sum over the scaled weights; it skips the fp16 rounding of each scaled
 //           weight and saves a packed multiply per weight pair.
 // ------------------------------------------------------------------------------------
-// The body of one stream-path block: block `bid` of the call's grid (blocks of S = blockDim.x /
-// 64 waves); red: LDS for [S - 1][NCB][64] partial sums of waves 1..S-1.  TAG tells apart the
-// kernels that run the same body (a specialization of its own per calling kernel).
+// The body of one stream-path block: block `bid` of the call's grid, run by S waves of which
+// this is wave w (wave-uniform; S = 1 runs without LDS or barriers, so several such blocks can
+// share one workgroup); red: LDS for [S - 1][NCB][64] partial sums of waves 1..S-1.  TAG tells
+// apart the kernels that run the same body (a specialization of its own per calling kernel).
 template <int WT, int ACT, bool GROUPED, int PF, int PA, int OPB, int TAG = 0>
-__device__ __forceinline__ void stream_body(const GemmParams& p, int ngo, int bid,
+__device__ __forceinline__ void stream_body(const GemmParams& p, int ngo, int bid, int S, int w,
                                             f32x4* __restrict__ red) {
     constexpr int KSB = WTraits<WT>::KSB;
     constexpr int KSTEPS = KSB / 32;
     constexpr bool SWI = (ACT == MOE_ACT_SWIGLU);
     constexpr int NCB = SWI ? 2 * OPB : OPB;
     const int lane = threadIdx.x & (kWave - 1);
-    // wave index, held in a scalar register (the compiler cannot see it is wave-uniform)
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int S = blockDim.x / kWave;
 
     // (m-tile, output column group), m-tile slowest so that the blocks of existing tiles come
     // first and the surplus of the upper-bound grid exits last
