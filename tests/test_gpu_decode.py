@@ -58,6 +58,7 @@ DECODE_CASES = [
     ("dsv2_lite", 9, None),        # + shared experts in the same launches, k = 6
     ("dsv2_lite", 9, "int8"),
     ("dsv2_lite", 32, None),       # 192 routed rows: the shared GEMM 1 as a launch of its own
+    ("dsv2_lite", 1, None),        # one token: the first GEMM split over waves, shared beside it
     ("tiny_shared", 16, None),
     ("tiny_shared", 16, "int8"),
     ("tiny_shared", 16, "fp16"),   # fp16 routed weights: shared experts on a side stream
