@@ -375,7 +375,8 @@ def measure_layer(args, q, torch, np, synth, cfg, T, wtype, active_n, steps, war
         # one graph per weight copy, captured on a side stream; replays are checked against
         # the eager output of the same weights before they are timed
         gs = torch.cuda.Stream()
-        gplans = [layer.plan(ws, x, logits, weights=c, stream=gs, active=active) for c in copies]
+        gplans = [layer.plan(ws, x, logits, weights=c, stream=gs, active=active,
+                             overlap_shared=True) for c in copies]
         graphs = []
         ref_out = None
         for gp in gplans:

@@ -255,11 +255,14 @@ class DeviceLayer:
 
     # ------------------------------------------------------------------ cached launch plan
     def plan(self, ws: Workspace, x, logits, weights=None, gate_in_gemm: bool = True,
-             stream=None, active=None) -> "LayerPlan":
+             stream=None, active=None, overlap_shared: bool = False) -> "LayerPlan":
         """Pre-marshal every C call of one forward() for fixed buffers, so that a step is
         just the C calls (no per-call Python argument checks).  `weights` = (w1, w2) or, for a
         layer with shared experts, (w1, w2, shared w1, shared w2): device tensors in the packed
-        layout (defaults to this layer's own)."""
+        layout (defaults to this layer's own).  overlap_shared (for a plan captured into a HIP
+        graph): the five-call step runs the shared experts on a side stream forked before the
+        gating and joined before the combine, so the graph runs them beside the routed
+        launches (the fork and join cost host time when the plan runs eagerly)."""
         w1, w2 = weights[:2] if weights is not None else (self.w1, self.w2)
         shw = tuple(weights[2:4]) if weights is not None and len(weights) == 4 else self.shared
         b, L, T = ws.bufs, lib(), ws.T
@@ -356,16 +359,42 @@ class DeviceLayer:
                        _ptr(self.s2), wt, self.group, 0, rs, _ptr(b["y"]), ob, wsp, wsn, st)))
         addend = None
         if self.shared is not None:
-            calls += [
+            overlap = overlap_shared
+            ss = st
+            if overlap:
+                # the shared experts on a side stream forked before the gating, joined before
+                # the combine (event records and waits, which a captured graph keeps as edges)
+                import torch
+                main = stream if stream is not None else torch.cuda.current_stream(self.device)
+                side = torch.cuda.Stream(device=self.device)
+                fork, join = torch.cuda.Event(), torch.cuda.Event()
+
+                def do_fork():
+                    fork.record(main)
+                    side.wait_event(fork)
+                    return 0
+
+                def do_join():
+                    join.record(side)
+                    main.wait_event(join)
+                    return 0
+
+                ss = _stream(side)
+                keep = keep + (side, fork, join)
+            shared_calls = [
                 ("shared1", L.moe_grouped_gemm_wq, (_ptr(x), _ptr(b["sh_off"]), T, 1, self.d,
                                                     2 * self.shared_inter, _ptr(shw[0]),
                                                     None, 2, 0, 2, None, _ptr(b["sh_h"]), ob,
-                                                    wsp, wsn, st)),
+                                                    wsp, wsn, ss)),
                 ("shared2", L.moe_grouped_gemm_wq, (_ptr(b["sh_h"]), _ptr(b["sh_off"]), T, 1,
                                                     self.shared_inter, self.d,
                                                     _ptr(shw[1]), None, 2, 0, 0, None,
-                                                    _ptr(b["sh_y"]), ob, wsp, wsn, st)),
+                                                    _ptr(b["sh_y"]), ob, wsp, wsn, ss)),
             ]
+            if overlap:
+                calls = [("fork", do_fork, ())] + shared_calls + calls + [("join", do_join, ())]
+            else:
+                calls += shared_calls
             addend = b["sh_y"]
         calls.append(("combine", L.moe_unpermute_combine,
                       (_ptr(b["y"]), _ptr(b["inv"]), None if gate_in_gemm else _ptr(b["w"]),

@@ -172,21 +172,25 @@ def test_plan_outlives_its_layer(name, T):
     np.testing.assert_array_equal(got, want)
 
 
-@pytest.mark.parametrize("name,T,n_check", [("mt_encoder", 3840, 64), ("qwen15_moe", 544, 64),
-                                            ("dsv2_lite", 288, 64), ("phi35_moe", 8192, 256)])
-def test_layer_replays_from_a_graph(name, T, n_check):
+@pytest.mark.parametrize("name,T,n_check,overlap", [("mt_encoder", 3840, 64, False),
+                                                    ("qwen15_moe", 544, 64, False),
+                                                    ("dsv2_lite", 288, 64, False),
+                                                    ("dsv2_lite", 288, 64, True),
+                                                    ("phi35_moe", 8192, 256, False)])
+def test_layer_replays_from_a_graph(name, T, n_check, overlap):
     """The step the bench times: the layer plan captured once in a HIP graph and replayed with
-    eager work in between.  Every replay gives the eager output bit for bit, and sampled tokens
-    of the replayed output match the fp64 oracle."""
+    eager work in between (with overlap, the shared experts on a forked stream inside the
+    graph).  Every replay gives the eager output bit for bit, and sampled tokens of the
+    replayed output match the fp64 oracle."""
     import torch
 
     inp, layer = _layer(name, T, None, 0)
     x, L = dev(inp.x), dev(inp.logits)
     ws = layer.workspace(T)
-    case(f"layer graph {name} T={T}")
+    case(f"layer graph {name} T={T} overlap={overlap}")
     want = host(layer.forward(x, L, ws=ws)).copy()
     s = torch.cuda.Stream()
-    plan = layer.plan(ws, x, L, stream=s)
+    plan = layer.plan(ws, x, L, stream=s, overlap_shared=overlap)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         plan.run()
