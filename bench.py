@@ -93,6 +93,9 @@ def parse():
                     help="skip the per-configuration block (graph step and dominant-kernel "
                          "roofline of the other layer shapes) of the default line")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--no-shared-overlap", action="store_true",
+                    help="capture the shared experts in series with the routed launches "
+                         "(default: on a forked stream inside the graph)")
     ap.add_argument("--no-graph", action="store_true",
                     help="report the eager launches (one ctypes call per kernel) as the value "
                          "instead of the same steps replayed from captured HIP graphs")
@@ -376,7 +379,7 @@ def measure_layer(args, q, torch, np, synth, cfg, T, wtype, active_n, steps, war
         # the eager output of the same weights before they are timed
         gs = torch.cuda.Stream()
         gplans = [layer.plan(ws, x, logits, weights=c, stream=gs, active=active,
-                             overlap_shared=True) for c in copies]
+                             overlap_shared=not args.no_shared_overlap) for c in copies]
         graphs = []
         ref_out = None
         for gp in gplans:
